@@ -1,0 +1,113 @@
+"""CPU oracle for causal GQA attention (float64, plain C + OpenMP).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's CPU
+baseline may import this package; the product path (the HIP library and its
+Python binding) never does. The oracle and the HIP path share no code.
+
+The arithmetic lives in ``oracle.c``; this module compiles it with gcc when the
+shared library is missing and marshals float64 numpy arrays through ctypes.
+Scale: the caller's float (normally the float32 value of 1/sqrt(d)), widened to
+float64 exactly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+# Plain float64 semantics: no fast-math, no FMA contraction.
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(src: str = _SRC, out: str = _LIB) -> str:
+    """Compile the oracle with gcc into ``out`` (always recompiles)."""
+    tmp = out + ".tmp"
+    subprocess.run(["gcc", *CFLAGS, src, "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def load(path: str = _LIB):
+    """Load a compiled oracle library (building the default one if absent)."""
+    global _lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if path == _LIB and not os.path.exists(path):
+        build()
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i = ctypes.c_int
+    lib.oracle_attn_fwd.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_attn_fwd.restype = None
+    lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_attn_bwd.restype = None
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _f64(x) -> np.ndarray:
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            x = x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _dims(q, k):
+    B, Hq, N, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (B, N, d) != (Bk, Nk, dk) or Hkv < 1 or Hq % Hkv:
+        raise ValueError(f"bad shapes q{q.shape} k{k.shape}")
+    return B, Hq, Hkv, N, d
+
+
+def attn_fwd(q, k, v, causal: int = 1, scale: float | None = None, lib=None
+             ) -> Tuple[np.ndarray, np.ndarray]:
+    """Return (o [B,Hq,N,d], lse [B,Hq,N]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((B, Hq, N, d))
+    lse = np.zeros((B, Hq, N))
+    (lib or load()).oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                    B, Hq, Hkv, N, d, int(causal), float(scale))
+    return o, lse
+
+
+def attn_bwd(q, k, v, dout, causal: int = 1, scale: float | None = None, lib=None
+             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Return (dq [B,Hq,N,d], dk [B,Hkv,N,d], dv [B,Hkv,N,d]) in float64."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    dq = np.zeros((B, Hq, N, d))
+    dk = np.zeros((B, Hkv, N, d))
+    dv = np.zeros((B, Hkv, N, d))
+    (lib or load()).oracle_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(dout),
+                                    _ptr(dq), _ptr(dk), _ptr(dv),
+                                    B, Hq, Hkv, N, d, int(causal), float(scale))
+    return dq, dk, dv
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle will use (before capping by work units)."""
+    return int((lib or load()).oracle_threads())
