@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Throughput of causal GQA attention forward + backward on one MI355X.
+
+A step is one pass of the whole path on one batch of synthetic input:
+attn_fwd (O, LSE), then the backward's two phases, attn_bwd_preprocess
+(D = rowsum(dO o O), clearing) and attn_bwd_main (dQ, dK, dV) -- together
+exactly attn_bwd -- all on torch's current stream, inputs resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa]
+
+Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
+N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
+The roofline object describes the dominant kernel (the backward main loop):
+its algorithmic flops per launch divided by its mean duration, measured with
+HIP events recorded on the launch stream around each launch in the timed
+region. cpu_baseline times the float64 oracle on this host on the same
+workload (fwd + bwd).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import tiled_causal_attention_amd as tca  # noqa: E402
+import workloads  # noqa: E402
+
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X published dense bf16/fp16 matrix peak
+PEAK_HBM_GBS = 8000.0            # MI355X published HBM3E bandwidth
+METRIC = "causal attn fwd+bwd TFLOP/s + % bf16 MFMA peak, B8 Hq12/Hkv4 N1024 d64"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.CONFIGS))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-check", action="store_true")
+    return p.parse_args()
+
+
+def cpu_baseline(s: workloads.Shape, inputs):
+    """The float64 oracle, as it stands, on this host's cores."""
+    import oracle
+    q, k, v, do = inputs
+    units = s.B * s.Hkv
+    # bounded sample: whole (b, kv-head) units, as many as keep it to ~10-30 s of CPU work
+    work_per_unit = s.flops_fwd() * 3.5 / units        # fwd + bwd flops of one unit
+    max_units = max(1, int(30e9 * 8 / work_per_unit))  # ~1 GFLOP/s/thread, 8 threads' worth
+    nb = max(1, min(s.B, max_units // s.Hkv)) if max_units >= s.Hkv else 1
+    nh = s.Hkv if max_units >= s.Hkv else max(1, min(s.Hkv, max_units))
+    g = s.group
+    qs, dos = q[:nb, :nh * g], do[:nb, :nh * g]
+    ks, vs = k[:nb, :nh], v[:nb, :nh]
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qs, ks, vs, s.causal, s.scale)
+    t1 = time.perf_counter()
+    oracle.attn_bwd(qs, ks, vs, dos, s.causal, s.scale)
+    t2 = time.perf_counter()
+    frac = (nb * nh) / units
+    flops = (s.flops_fwd() + s.flops_bwd()) * frac
+    return {
+        "value": flops / (t2 - t0) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": min(oracle.threads(), nb * nh),
+        "kind": "oracle",
+        "sample": f"{nb} of {s.B} batch rows x {nh} of {s.Hkv} KV heads (all {g} query heads each) "
+                  f"= {frac:.3f} of the workload; fwd {t1 - t0:.2f} s + bwd {t2 - t1:.2f} s, float64",
+    }
+
+
+def sampled_check(s, inputs, out):
+    """Largest error on sampled outputs of one (b, kv-head) unit against the oracle."""
+    import numpy as np
+    import oracle
+    q, k, v, do = inputs
+    o, lse, dq, dk, dv = (t.cpu().double().numpy() for t in out)
+    b, hkv = s.B - 1, s.Hkv - 1
+    rows = [(g, i) for g in range(s.group) for i in (0, s.N // 3, s.N // 2, s.N - 1)]
+    keys = [0, s.N // 4, s.N - 1]
+    ref = oracle.attn_sampled(q, k, v, do, b, hkv, rows, keys, s.causal, s.scale)
+    hq = [hkv * s.group + g for g, _ in rows]
+    ii = [i for _, i in rows]
+    err = {
+        "o": np.abs(o[b, hq, ii] - ref["o"]).max(),
+        "lse": np.abs(lse[b, hq, ii] - ref["lse"]).max(),
+        "dq": np.abs(dq[b, hq, ii] - ref["dq"]).max(),
+        "dk": np.abs(dk[b, hkv, keys] - ref["dk"]).max(),
+        "dv": np.abs(dv[b, hkv, keys] - ref["dv"]).max(),
+    }
+    return {f"max_abs_{kk}": float(vv) for kk, vv in err.items()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this attention path runs on a single MI355X "
+              "(sharding over batch and KV-head groups needs no communication and is not "
+              "built here). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    tca.lib()  # fail loudly if the HIP library is missing
+
+    s = workloads.CONFIGS[args.workload]
+    inputs = workloads.make_inputs(s)
+    q, k, v, do = (t.cuda() for t in inputs)
+    dev = q.device
+    o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((s.B, s.Hq, s.N), dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    ws = tca.bwd_workspace(q, k)
+    causal, scale = bool(s.causal), s.scale
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        tca.attn_fwd(q, k, v, causal, scale, out=(o, lse))
+        if ev is not None:
+            ev[1].record()
+        tca.attn_bwd_preprocess(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+        if ev is not None:
+            ev[2].record()
+        tca.attn_bwd_main(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_pre = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_main = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+
+    flops_fwd, flops_bwd = s.flops_fwd(), s.flops_bwd()
+    tflops = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
+    kernels = {"attn_fwd": t_fwd, "bwd_preprocess": t_pre, "bwd_main": t_main}
+    dom = max(kernels, key=kernels.get)
+    dom_flops = {"attn_fwd": flops_fwd, "bwd_main": flops_bwd, "bwd_preprocess": 0.0}[dom]
+    if dom == "bwd_preprocess":
+        nbytes = s.B * s.Hq * s.N * s.d * (4 + 2) + s.B * s.Hq * s.N * 4
+        achieved = nbytes / (t_pre * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
+    else:
+        achieved = dom_flops / (kernels[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": None,
+                "kernel": dom}
+
+    result = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if s.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{s.name}: causal GQA attention fwd+bwd, B={s.B} Hq={s.Hq} "
+                               f"Hkv={s.Hkv} N={s.N} d={s.d} {s.dtype} in, fp32 out",
+                   "global_batch": s.B, "seq_len": s.N, "parallelism": "single-gpu"},
+        "pct_peak": 100.0 * tflops / PEAK_MFMA_BF16_TFLOPS,
+        "fwd_tflops": flops_fwd / (t_fwd * 1e-3) / 1e12,
+        "bwd_tflops": flops_bwd / ((t_pre + t_main) * 1e-3) / 1e12,
+        "kernel_ms": kernels,
+        "roofline": roof,
+    }
+    if not args.no_check:
+        result["check"] = sampled_check(s, inputs, (o, lse, dq, dk, dv))
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(s, inputs)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,151 @@
+/*
+ * tca.h -- causal, GQA-capable tiled attention (forward and backward) for
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The operation is the tiled FlashAttention of the NanoEuler blog page
+ * (section "Tiled FlashAttention": one block per query tile, a loop over K/V
+ * tiles staged in on-chip memory, a Q*K^T tile product, an online softmax
+ * update and an output accumulation), extended as follows:
+ *   - causal masking (the model is a decoder-only transformer, section
+ *     "Architecture Deep Dive"): query i attends to keys j <= i;
+ *   - grouped-query attention (config "num_heads": 12, "num_kv_heads": 4 in
+ *     section "Build and Run"; "GQA" in the FAQ): query head hq reads KV head
+ *     hq / (Hq / Hkv), so consecutive query heads share one KV head;
+ *   - the log-sum-exp of every query row is saved for the backward;
+ *   - a hand-derived backward (the pages hand-write every backward pass,
+ *     section "Hand-written Backpropagation"): D = rowsum(dO o O), P
+ *     recomputed from the saved log-sum-exp, dS = P o (dP - D), and dQ, dK, dV.
+ *
+ * Definitions (for every batch b, query head hq, query row i):
+ *   s_ij   = scale * <q_i, k_j>                 j visible: j <= i if causal, else all j
+ *   lse_i  = log(sum_j exp(s_ij))               natural logarithm
+ *   o_i    = sum_j exp(s_ij - lse_i) * v_j
+ *   dv_j   = sum over hq in the group, i     of P_ij * dO_i
+ *   dq_i   = scale * sum_j P_ij (dP_ij - D_i) k_j,   dP_ij = <dO_i, v_j>, D_i = <dO_i, o_i>
+ *   dk_j   = scale * sum over hq in the group, i of P_ij (dP_ij - D_i) q_i
+ *
+ * Layout: every tensor is contiguous row-major. q, o, dO, dq: [B, Hq, N, d];
+ * k, v, dk, dv: [B, Hkv, N, d]; lse: [B, Hq, N]. The head dimension d is the
+ * fastest-moving index.
+ *
+ * Precision: inputs q, k, v, dO are float32 (ATTN_F32) or bfloat16 (ATTN_BF16).
+ * Outputs o, lse, dq, dk, dv are always float32. With ATTN_F32 every step is
+ * computed in float32. With ATTN_BF16 and d in {64, 128}, Q*K^T and dO*V^T run
+ * as bf16 matrix-core products with float32 accumulation; the products whose
+ * operand is a computed probability or score gradient (P*V, P^T*dO, dS^T*Q,
+ * dS*K) run as fp16 matrix-core products, the bf16 partner converted to fp16
+ * (exact for |x| >= 2^-14; inputs must satisfy |x| < 65504); all accumulation
+ * is float32. bf16 inputs with d in {16, 32} are computed in float32.
+ *
+ * Memory ownership: the caller owns every buffer. All tensor pointers are
+ * device memory (hipMalloc or equivalent), 16-byte aligned, and must stay
+ * alive until the work enqueued on `stream` completes. The library allocates
+ * no memory and keeps no state between calls; calls are thread-safe.
+ *
+ * Asynchrony: every entry point validates its arguments, enqueues kernels on
+ * `stream` (a hipStream_t; NULL means the default stream) and returns. Results
+ * are valid after the caller synchronises with the stream.
+ *
+ * Errors: on any non-OK status nothing has been enqueued and no output has
+ * been written, except ATTN_EHIP, which reports a HIP launch error after
+ * enqueueing began. No exception crosses this interface and nothing is
+ * printed. Inputs and outputs must not alias.
+ *
+ * Supported shapes: B >= 0, N >= 0 (B*N == 0 is a no-op that returns ATTN_OK
+ * and ignores every pointer), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
+ * d in {16, 32, 64, 128}, N*d < 2^31, B*Hq*N < 2^31, causal in {0, 1},
+ * scale finite.
+ */
+#ifndef TCA_H
+#define TCA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,   /* float32 inputs  */
+    ATTN_BF16 = 1   /* bfloat16 inputs */
+} attn_dtype;
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_EINVAL = 1,        /* invalid argument: null or misaligned pointer, bad size, bad flag */
+    ATTN_EUNSUPPORTED = 2,  /* valid but not supported (head dimension) */
+    ATTN_EHIP = 3           /* the HIP runtime reported an error while enqueueing */
+} attn_status;
+
+/* Version of this interface; bumped on any incompatible change. */
+int attn_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_str(attn_status s);
+
+/* Workspace bytes attn_fwd needs for these sizes (currently 0 for every
+ * shape; a NULL workspace is accepted when this returns 0). */
+size_t attn_fwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d);
+
+/* Forward: o and lse from q, k, v.
+ *   q [B,Hq,N,d], k and v [B,Hkv,N,d] in `dtype`;
+ *   o [B,Hq,N,d] float32 and lse [B,Hq,N] float32 are fully overwritten.
+ * This is the tile loop of the "Tiled FlashAttention" section: per query tile,
+ * K/V tiles in on-chip memory, Q*K^T, online softmax, output accumulation; the
+ * causal variant visits only the K/V tiles at or below the diagonal. */
+attn_status attn_fwd(attn_dtype dtype,
+                     const void* q, const void* k, const void* v,
+                     float* o, float* lse,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     void* stream);
+
+/* Workspace bytes attn_bwd (and its two phases) need: the float32 row
+ * statistic D = rowsum(dO o O), B*Hq*N floats, rounded up to 256 bytes. */
+size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d);
+
+/* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dO.
+ *   q, k, v, dO in `dtype`; o, lse exactly as written by attn_fwd with the same
+ *   q, k, v, sizes, causal flag and scale; dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]
+ *   float32, fully overwritten. `workspace` holds at least
+ *   attn_bwd_workspace_bytes(...) bytes of device memory; its contents on entry
+ *   do not matter. dk and dv are bitwise reproducible for a fixed shape; dq is
+ *   accumulated with float32 atomics when dtype is ATTN_BF16 and d is 64 or
+ *   128, so its last bits may vary between runs.
+ * Equivalent to attn_bwd_preprocess followed by attn_bwd_main on `stream`. */
+attn_status attn_bwd(attn_dtype dtype,
+                     const void* q, const void* k, const void* v,
+                     const float* o, const float* lse, const void* dO,
+                     float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes,
+                     int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                     void* stream);
+
+/* First phase of attn_bwd: writes D = rowsum(dO o O) (float32, B*Hq*N) into
+ * `workspace` and clears whatever attn_bwd_main accumulates into atomically
+ * (dq, and dk/dv when Hq > Hkv) for the same dtype and d. dq, dk and dv may be
+ * written. Arguments as for attn_bwd. */
+attn_status attn_bwd_preprocess(attn_dtype dtype,
+                                const void* q, const void* k, const void* v,
+                                const float* o, const float* lse, const void* dO,
+                                float* dq, float* dk, float* dv,
+                                void* workspace, size_t workspace_bytes,
+                                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                void* stream);
+
+/* Second phase of attn_bwd: the K/V-tile-parallel main loop. Requires that
+ * attn_bwd_preprocess with the same arguments was enqueued before it on the
+ * same stream (or completed). Arguments as for attn_bwd. */
+attn_status attn_bwd_main(attn_dtype dtype,
+                          const void* q, const void* k, const void* v,
+                          const float* o, const float* lse, const void* dO,
+                          float* dq, float* dk, float* dv,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCA_H */

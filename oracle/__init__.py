@@ -49,6 +49,10 @@ def load(path: str = _LIB):
     lib.oracle_attn_fwd.restype = None
     lib.oracle_attn_bwd.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
     lib.oracle_attn_bwd.restype = None
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.oracle_attn_sampled.argtypes = [dp, dp, dp, dp, i, i, i, i, ctypes.c_double,
+                                        i, ip, ip, dp, dp, dp, i, ip, dp, dp]
+    lib.oracle_attn_sampled.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     if path == _LIB:
@@ -106,6 +110,37 @@ def attn_bwd(q, k, v, dout, causal: int = 1, scale: float | None = None, lib=Non
                                     _ptr(dq), _ptr(dk), _ptr(dv),
                                     B, Hq, Hkv, N, d, int(causal), float(scale))
     return dq, dk, dv
+
+
+def attn_sampled(q, k, v, dout, b: int, hkv: int, rows, keys, causal: int = 1,
+                 scale: float | None = None, lib=None):
+    """Sampled outputs of the (b, hkv) unit, for shapes too large for the full oracle.
+
+    rows: list of (g, i) with g the query head's index inside the group
+    (query head hq = hkv * group + g) and i the query row; keys: list of key rows.
+    Returns dict with o [R,d], lse [R], dq [R,d], dk [K,d], dv [K,d] (float64).
+    Only the unit's slices are widened to float64.
+    """
+    Hq, Hkv = q.shape[1], k.shape[1]
+    G = Hq // Hkv
+    qs = _f64(q[b, hkv * G:(hkv + 1) * G])
+    dos = _f64(dout[b, hkv * G:(hkv + 1) * G])
+    ks, vs = _f64(k[b, hkv]), _f64(v[b, hkv])
+    N, d = ks.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    rg = np.ascontiguousarray([g for g, _ in rows], dtype=np.int32)
+    ri = np.ascontiguousarray([i for _, i in rows], dtype=np.int32)
+    kj = np.ascontiguousarray(list(keys), dtype=np.int32)
+    R, K = len(rg), len(kj)
+    out = dict(o=np.zeros((R, d)), lse=np.zeros(R), dq=np.zeros((R, d)),
+               dk=np.zeros((K, d)), dv=np.zeros((K, d)))
+    ip = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int))
+    (lib or load()).oracle_attn_sampled(
+        _ptr(qs), _ptr(ks), _ptr(vs), _ptr(dos), G, N, d, int(causal), float(scale),
+        R, ip(rg), ip(ri), _ptr(out["o"]), _ptr(out["lse"]), _ptr(out["dq"]),
+        K, ip(kj), _ptr(out["dk"]), _ptr(out["dv"]))
+    return out
 
 
 def threads(lib=None) -> int:

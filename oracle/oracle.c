@@ -162,3 +162,99 @@ void oracle_attn_bwd(const double* q, const double* k, const double* v, const do
         free(dp);
     }
 }
+
+/* Sampled outputs of one (b, kv-head) unit, for shapes where the full oracle
+ * is too slow. Same definitions as above; the unit's G = Hq/Hkv query heads
+ * are passed as q, dout [G, N, d] and its KV head as k, v [N, d].
+ *   For each listed query row (row_g[r], row_i[r]): o_rows[r, :], lse_rows[r],
+ *   dq_rows[r, :].
+ *   For each listed key row keys[t]: dk_rows[t, :], dv_rows[t, :] (summed over
+ *   the G query heads). These need LSE_i and D_i of every query row, which a
+ *   first pass computes (OpenMP over rows; each row is independent). */
+void oracle_attn_sampled(const double* q, const double* k, const double* v, const double* dout,
+                         int G, int N, int d, int causal, double scale,
+                         int n_rows, const int* row_g, const int* row_i,
+                         double* o_rows, double* lse_rows, double* dq_rows,
+                         int n_keys, const int* keys, double* dk_rows, double* dv_rows) {
+    /* query rows: O, LSE, dQ */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int r = 0; r < n_rows; ++r) {
+        const int g = row_g[r], i = row_i[r];
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+        double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+        const double* qi = q + ((size_t)g * N + i) * d;
+        const double* doi = dout + ((size_t)g * N + i) * d;
+        double L = row_scores(qi, k, N, d, causal, i, scale, s);
+        lse_rows[r] = L;
+        double* oi = o_rows + (size_t)r * d;
+        double* dqi = dq_rows + (size_t)r * d;
+        for (int c = 0; c < d; ++c) { oi[c] = 0.0; dqi[c] = 0.0; }
+        double D = 0.0;
+        for (int j = 0; j < N; ++j) {
+            if (!visible(causal, i, j)) continue;
+            s[j] = exp(s[j] - L);
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += doi[c] * v[(size_t)j * d + c];
+            dp[j] = acc;
+            D += s[j] * dp[j];
+            for (int c = 0; c < d; ++c) oi[c] += s[j] * v[(size_t)j * d + c];
+        }
+        for (int j = 0; j < N; ++j) {
+            if (!visible(causal, i, j)) continue;
+            const double ds = s[j] * (dp[j] - D);
+            for (int c = 0; c < d; ++c) dqi[c] += scale * ds * k[(size_t)j * d + c];
+        }
+        free(s);
+        free(dp);
+    }
+    if (n_keys <= 0) return;
+    /* row statistics LSE_i and D_i for every query row of the unit */
+    double* lse_all = (double*)malloc(sizeof(double) * (size_t)G * N);
+    double* d_all = (double*)malloc(sizeof(double) * (size_t)G * N);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (long gi = 0; gi < (long)G * N; ++gi) {
+        const int g = (int)(gi / N), i = (int)(gi % N);
+        double* s = (double*)malloc(sizeof(double) * (size_t)N);
+        const double* qi = q + ((size_t)g * N + i) * d;
+        const double* doi = dout + ((size_t)g * N + i) * d;
+        double L = row_scores(qi, k, N, d, causal, i, scale, s);
+        double D = 0.0;
+        for (int j = 0; j < N; ++j) {
+            if (!visible(causal, i, j)) continue;
+            double acc = 0.0;
+            for (int c = 0; c < d; ++c) acc += doi[c] * v[(size_t)j * d + c];
+            D += exp(s[j] - L) * acc;
+        }
+        lse_all[gi] = L;
+        d_all[gi] = D;
+        free(s);
+    }
+    /* key rows: dK_j, dV_j over every query head of the group and every row */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int t = 0; t < n_keys; ++t) {
+        const int j = keys[t];
+        double* dkj = dk_rows + (size_t)t * d;
+        double* dvj = dv_rows + (size_t)t * d;
+        for (int c = 0; c < d; ++c) { dkj[c] = 0.0; dvj[c] = 0.0; }
+        for (int g = 0; g < G; ++g) {
+            for (int i = 0; i < N; ++i) {
+                if (!visible(causal, i, j)) continue;
+                const double* qi = q + ((size_t)g * N + i) * d;
+                const double* doi = dout + ((size_t)g * N + i) * d;
+                double dot = 0.0, acc = 0.0;
+                for (int c = 0; c < d; ++c) {
+                    dot += qi[c] * k[(size_t)j * d + c];
+                    acc += doi[c] * v[(size_t)j * d + c];
+                }
+                const double p = exp(scale * dot - lse_all[(size_t)g * N + i]);
+                const double ds = p * (acc - d_all[(size_t)g * N + i]);
+                for (int c = 0; c < d; ++c) {
+                    dvj[c] += p * doi[c];
+                    dkj[c] += scale * ds * qi[c];
+                }
+            }
+        }
+    }
+    free(lse_all);
+    free(d_all);
+}

@@ -1,0 +1,171 @@
+"""C-ABI tests that need no GPU: the library loads, exports every symbol the
+header declares, and rejects every invalid argument before touching the GPU.
+
+Validation happens on the host before any HIP call, so these calls use host
+addresses (or made-up aligned addresses) and never launch anything.
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import tiled_causal_attention_amd as tca
+from tiled_causal_attention_amd import build as tca_build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tca.h")
+
+F32, BF16 = tca.ATTN_F32, tca.ATTN_BF16
+OK, EINVAL, EUNSUP = tca.ATTN_OK, tca.ATTN_EINVAL, tca.ATTN_EUNSUPPORTED
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(tca.LIB_PATH):
+        tca_build.build()
+    return tca.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+                     "attn_bwd_preprocess", "attn_bwd_main", "attn_fwd_workspace_bytes",
+                     "attn_abi_version"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_exports_are_c_symbols():
+    out = os.popen(f"nm -D --defined-only {tca.LIB_PATH}").read()
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_version_and_status_strings(L):
+    assert L.attn_abi_version() == 1
+    for s in (OK, EINVAL, EUNSUP, tca.ATTN_EHIP):
+        assert L.attn_status_str(s)
+    assert b"unknown" in L.attn_status_str(99)
+
+
+def test_workspace_sizes(L):
+    assert L.attn_fwd_workspace_bytes(BF16, 8, 12, 4, 1024, 64) == 0
+    n = L.attn_bwd_workspace_bytes(BF16, 8, 12, 4, 1024, 64)
+    assert n >= 8 * 12 * 1024 * 4 and n % 256 == 0
+    assert L.attn_bwd_workspace_bytes(F32, 1, 2, 1, 3, 16) == 256
+
+
+# A made-up, 16-byte-aligned address: never dereferenced because every call
+# below fails validation (or is a no-op) before any HIP call.
+FAKE = 0x10000
+
+
+def fwd(L, dtype=BF16, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125,
+        q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=None, wsb=0):
+    return L.attn_fwd(dtype, q, k, v, o, lse, ws, wsb, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+def bwd(L, name="attn_bwd", dtype=BF16, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125,
+        ptrs=None, ws=FAKE, wsb=1 << 20):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+    p.update(ptrs or {})
+    return getattr(L, name)(dtype, p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"],
+                            p["dk"], p["dv"], ws, wsb, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=7), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(N=-5), EINVAL),
+    (dict(Hq=0), EINVAL),
+    (dict(Hkv=0), EINVAL),
+    (dict(Hq=12, Hkv=5), EINVAL),
+    (dict(Hq=2, Hkv=4), EINVAL),
+    (dict(causal=2), EINVAL),
+    (dict(causal=-1), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(scale=float("inf")), EINVAL),
+    (dict(N=1 << 25, d=64), EINVAL),           # N*d overflows int32
+    (dict(B=1 << 20, Hq=4096, Hkv=4096, N=1024, d=16), EINVAL),   # B*Hq*N overflows
+    (dict(d=48), EUNSUP),
+    (dict(d=256), EUNSUP),
+    (dict(d=8), EUNSUP),
+    (dict(q=None), EINVAL),
+    (dict(k=None), EINVAL),
+    (dict(v=None), EINVAL),
+    (dict(o=None), EINVAL),
+    (dict(lse=None), EINVAL),
+    (dict(q=FAKE + 8), EINVAL),              # not 16-byte aligned
+    (dict(o=FAKE + 4), EINVAL),
+    (dict(lse=FAKE + 2), EINVAL),
+])
+def test_fwd_rejects(L, kw, want):
+    assert fwd(L, **kw) == want
+
+
+@pytest.mark.parametrize("name", ["attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"])
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=3), EINVAL),
+    (dict(Hq=6, Hkv=4), EINVAL),
+    (dict(causal=5), EINVAL),
+    (dict(d=96), EUNSUP),
+    (dict(ws=None), EINVAL),
+    (dict(ws=FAKE + 8), EINVAL),
+    (dict(wsb=100), EINVAL),                  # smaller than attn_bwd_workspace_bytes
+    (dict(ptrs=dict(dO=None)), EINVAL),
+    (dict(ptrs=dict(dq=None)), EINVAL),
+    (dict(ptrs=dict(dk=FAKE + 4)), EINVAL),
+    (dict(ptrs=dict(dv=None)), EINVAL),
+    (dict(ptrs=dict(o=None)), EINVAL),
+    (dict(ptrs=dict(lse=FAKE + 12)), EINVAL),
+])
+def test_bwd_rejects(L, name, kw, want):
+    assert bwd(L, name, **kw) == want
+
+
+def test_empty_inputs_are_noops(L):
+    # B*N == 0: OK without touching (or needing) any pointer
+    assert fwd(L, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+    assert fwd(L, N=0, q=None, k=None, v=None, o=None, lse=None) == OK
+    nul = dict(q=None, k=None, v=None, o=None, lse=None, dO=None, dq=None, dk=None, dv=None)
+    for name in ("attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"):
+        assert bwd(L, name, B=0, ptrs=nul, ws=None, wsb=0) == OK
+        assert bwd(L, name, N=0, ptrs=nul, ws=None, wsb=0) == OK
+    # but an empty call with an invalid flag is still rejected
+    assert fwd(L, B=0, causal=3) == EINVAL
+
+
+def test_outputs_untouched_on_error(L):
+    # host buffers passed as pointers: validation fails, so nothing is written
+    o = np.full(4 * 64 * 64, 7.0, dtype=np.float32)
+    lse = np.full(4 * 64, 7.0, dtype=np.float32)
+    st = fwd(L, B=1, Hq=4, Hkv=3, N=64, d=64, o=o.ctypes.data, lse=lse.ctypes.data)
+    assert st == EINVAL
+    assert (o == 7.0).all() and (lse == 7.0).all()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 8, 16)
+    with pytest.raises(ValueError):
+        tca.attn_fwd(q, q[:, :1].contiguous(), q[:, :1].contiguous())
+
+
+def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tca, "_lib", None)
+    monkeypatch.setattr(tca, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        tca.lib()

@@ -94,6 +94,7 @@ def _pin_failures(lib=None, shapes=SHAPES, atol=1e-10):
             for nm, a, b in (("dQ", dq, tq), ("dK", dk, tk), ("dV", dv, tv)):
                 if not np.allclose(a, b, atol=atol, rtol=0):
                     fails.append(f"{nm} vs autograd {B,Hq,Hkv,N,d,causal}: {np.nanmax(np.abs(a - b))}")
+    fails += _sampled_failures(lib, atol)
     for fname in sorted(os.listdir(GOLDEN)):
         if not fname.endswith(".json"):
             continue
@@ -105,6 +106,48 @@ def _pin_failures(lib=None, shapes=SHAPES, atol=1e-10):
             if not np.allclose(a, arr[nm], atol=1e-12, rtol=0):
                 fails.append(f"golden {fname} {nm}: got {a.ravel()} want {arr[nm].ravel()}")
     return fails
+
+
+def _sampled_failures(lib=None, atol=1e-10):
+    """The sampled-output entry against torch autograd on small shapes."""
+    fails = []
+    for (B, Hq, Hkv, N, d) in [(2, 6, 2, 37, 8), (1, 4, 1, 20, 16)]:
+        G = Hq // Hkv
+        for causal in (1, 0):
+            q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=N + 100 * causal)
+            scale = 1.0 / math.sqrt(d)
+            ro = _torch_fwd(q, k, v, causal, scale).numpy()
+            rl = _torch_lse(q, k, causal, scale).numpy()
+            tq, tk, tv = (t.numpy() for t in _torch_bwd(q, k, v, do, causal, scale))
+            b, hkv = B - 1, Hkv - 1
+            rows = [(g, i) for g in range(G) for i in (0, 1, N // 2, N - 1)]
+            keys = [0, 1, N // 3, N - 2, N - 1]
+            got = oracle.attn_sampled(q, k, v, do, b, hkv, rows, keys, causal, scale, lib=lib)
+            for r, (g, i) in enumerate(rows):
+                hq = hkv * G + g
+                for nm, a, want in (("o", got["o"][r], ro[b, hq, i]), ("lse", got["lse"][r], rl[b, hq, i]),
+                                    ("dq", got["dq"][r], tq[b, hq, i])):
+                    if not np.allclose(a, want, atol=atol, rtol=0):
+                        fails.append(f"sampled {nm} row {(g, i)} of {B,Hq,Hkv,N,d,causal}")
+            for t, j in enumerate(keys):
+                for nm, a, want in (("dk", got["dk"][t], tk[b, hkv, j]), ("dv", got["dv"][t], tv[b, hkv, j])):
+                    if not np.allclose(a, want, atol=atol, rtol=0):
+                        fails.append(f"sampled {nm} key {j} of {B,Hq,Hkv,N,d,causal}")
+    return fails
+
+
+def test_sampled_entry_matches_full_oracle():
+    B, Hq, Hkv, N, d = 2, 6, 3, 45, 8
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=77, std=2.0)
+    o, lse = oracle.attn_fwd(q, k, v, 1)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, 1)
+    rows = [(g, i) for g in range(2) for i in range(N)]
+    got = oracle.attn_sampled(q, k, v, do, 1, 2, rows, list(range(N)), 1)
+    assert np.allclose(got["o"].reshape(2, N, d), o[1, 4:6], atol=1e-13)
+    assert np.allclose(got["lse"].reshape(2, N), lse[1, 4:6], atol=1e-13)
+    assert np.allclose(got["dq"].reshape(2, N, d), dq[1, 4:6], atol=1e-13)
+    assert np.allclose(got["dk"], dk[1, 2], atol=1e-13)
+    assert np.allclose(got["dv"], dv[1, 2], atol=1e-13)
 
 
 def test_library_and_golden_pins():
@@ -280,6 +323,9 @@ MUTANTS = [
     ("dK uses dO instead of Q", "dkh[(size_t)j * d + c] += scale * ds * qi[c];",
      "dkh[(size_t)j * d + c] += scale * ds * doi[c];"),
     ("dV uses P without dO", "dvh[(size_t)j * d + c] += p * doi[c];", "dvh[(size_t)j * d + c] += p * qi[c];"),
+    ("sampled: dropped scale in dK", "dkj[c] += scale * ds * qi[c];", "dkj[c] += ds * qi[c];"),
+    ("sampled: D without P", "D += exp(s[j] - L) * acc;", "D += acc;"),
+    ("sampled: O row uses K", "oi[c] += s[j] * v[(size_t)j * d + c];", "oi[c] += s[j] * k[(size_t)j * d + c];"),
     ("transposed V index", "acc += doi[c] * vh[(size_t)j * d + c];", "acc += doi[c] * vh[(size_t)c * d + j % d];"),
 ]
 

@@ -1,0 +1,229 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Tolerances (per output tensor: O, LSE, dQ, dK, dV), applied to the oracle run
+on the same rounded inputs:
+  * float32 inputs: max |x - ref| <= 1e-4;
+  * bfloat16 inputs: max |x - ref| <= 2e-2 and ||x - ref||_2 / ||ref||_2 <= 1e-2.
+dq on the matrix-core path is accumulated with float32 atomics, so only its
+tolerance is pinned, not its bits.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_causal_attention_amd as tca
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": dict(max_abs=1e-4, rel_rms=None), "bf16": dict(max_abs=2e-2, rel_rms=1e-2)}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tca.lib()   # fail loudly if the HIP library is missing
+    yield
+
+
+def _dev(*ts):
+    return [t.cuda() for t in ts]
+
+
+def run_gpu(q, k, v, do, causal, scale, poison=False):
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    B, Hq, N, d = q.shape
+    out_f = out_b = None
+    if poison:
+        nan = float("nan")
+        out_f = (torch.full((B, Hq, N, d), nan, device="cuda"), torch.full((B, Hq, N), nan, device="cuda"))
+        out_b = (torch.full(q.shape, nan, device="cuda"), torch.full(k.shape, nan, device="cuda"),
+                 torch.full(v.shape, nan, device="cuda"))
+    o, lse = tca.attn_fwd(qd, kd, vd, causal=causal, scale=scale, out=out_f)
+    dq, dk, dv = tca.attn_bwd(qd, kd, vd, o, lse, dod, causal=causal, scale=scale, out=out_b)
+    torch.cuda.synchronize()
+    return {n: t.cpu().double().numpy() for n, t in
+            dict(o=o, lse=lse, dq=dq, dk=dk, dv=dv).items()}
+
+
+def errs(got, ref):
+    diff = got - ref
+    max_abs = float(np.max(np.abs(diff))) if diff.size else 0.0
+    den = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(diff)) / den if den > 0 else float(np.linalg.norm(diff))
+    return max_abs, rel
+
+
+def check(name, got, ref, dtype, ctx=""):
+    assert np.isfinite(got).all(), f"{ctx} {name}: non-finite values"
+    max_abs, rel = errs(got, ref)
+    t = TOL[dtype]
+    assert max_abs <= t["max_abs"], f"{ctx} {name}: max abs {max_abs:.3e} > {t['max_abs']}"
+    if t["rel_rms"] is not None:
+        assert rel <= t["rel_rms"], f"{ctx} {name}: rel rms {rel:.3e} > {t['rel_rms']}"
+    return max_abs, rel
+
+
+def full_parity(s: workloads.Shape, seed=None, causal=None, poison=False):
+    causal = s.causal if causal is None else causal
+    q, k, v, do = workloads.make_inputs(s, seed)
+    g = run_gpu(q, k, v, do, causal, s.scale, poison=poison)
+    ro, rl = oracle.attn_fwd(q, k, v, causal, s.scale)
+    rq, rk, rv = oracle.attn_bwd(q, k, v, do, causal, s.scale)
+    ctx = f"{s.name} {s.B,s.Hq,s.Hkv,s.N,s.d} {s.dtype} causal={causal}"
+    res = {}
+    for name, ref in (("o", ro), ("lse", rl), ("dq", rq), ("dk", rk), ("dv", rv)):
+        res[name] = check(name, g[name], ref, s.dtype, ctx)
+    return res
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "gpt2_mha", "gpt2_gqa", "long_gqa"])
+def test_named_config_full(name):
+    s = workloads.CONFIGS[name]
+    print(f"[parity] {name}", flush=True)
+    full_parity(s)
+
+
+def test_headline_second_seed():
+    s = workloads.CONFIGS["gpt2_gqa"]
+    full_parity(s, seed=s.seed + 100)
+
+
+def test_wide_d128_sampled():
+    """Full-size wide-head stress case; the oracle computes sampled rows and keys."""
+    s = workloads.CONFIGS["wide_d128"]
+    print("[parity] wide_d128 sampled", flush=True)
+    q, k, v, do = workloads.make_inputs(s)
+    g = run_gpu(q, k, v, do, 1, s.scale)
+    N, G = s.N, s.group
+    for name in g:
+        assert np.isfinite(g[name]).all(), name
+    rows_i = [0, 1, 2, 63, 64, 127, 128, 1000, 4095, 4096, 6001, N - 2, N - 1]
+    keys = [0, 1, 63, 64, 127, 128, 2047, 4096, 8000, N - 65, N - 2, N - 1]
+    for (b, hkv) in [(0, 0), (s.B - 1, s.Hkv - 1)]:
+        rows = [(gg, i) for gg in range(G) for i in rows_i]
+        ref = oracle.attn_sampled(q, k, v, do, b, hkv, rows, keys, 1, s.scale)
+        hq = [hkv * G + gg for gg, _ in rows]
+        ii = [i for _, i in rows]
+        ctx = f"wide_d128 unit {(b, hkv)}"
+        check("o", g["o"][b, hq, ii], ref["o"], "bf16", ctx)
+        check("lse", g["lse"][b, hq, ii], ref["lse"], "bf16", ctx)
+        check("dq", g["dq"][b, hq, ii], ref["dq"], "bf16", ctx)
+        check("dk", g["dk"][b, hkv, keys], ref["dk"], "bf16", ctx)
+        check("dv", g["dv"][b, hkv, keys], ref["dv"], "bf16", ctx)
+    # property at full size: sum_j dV_j = sum over the group and rows of dO_i,
+    # up to the fp16 rounding of P (<= 2^-11 of each row's unit mass) -> bound 2^-10 sum|dO|
+    dof = do.double().numpy().reshape(s.B, s.Hkv, G, N, s.d)
+    lhs = g["dv"].sum(axis=2)
+    rhs = dof.sum(axis=(2, 3))
+    bound = 2.0 ** -10 * np.abs(dof).sum(axis=(2, 3))
+    assert (np.abs(lhs - rhs) <= bound + 1e-3).all()
+
+
+SMALL = [
+    # B, Hq, Hkv, N, d, dtype
+    (1, 2, 1, 1, 64, "bf16"),
+    (1, 2, 1, 17, 64, "bf16"),
+    (2, 3, 1, 63, 64, "bf16"),
+    (1, 4, 2, 65, 64, "bf16"),
+    (2, 4, 4, 129, 64, "bf16"),
+    (1, 6, 1, 200, 64, "bf16"),
+    (1, 12, 4, 300, 64, "bf16"),
+    (1, 4, 1, 1, 128, "bf16"),
+    (1, 2, 1, 33, 128, "bf16"),
+    (2, 4, 2, 161, 128, "bf16"),
+    (1, 2, 2, 257, 128, "bf16"),
+    (1, 2, 1, 50, 16, "bf16"),
+    (2, 6, 3, 77, 32, "bf16"),
+    (1, 2, 1, 1, 16, "f32"),
+    (2, 4, 2, 37, 16, "f32"),
+    (1, 3, 1, 100, 32, "f32"),
+    (1, 4, 2, 129, 64, "f32"),
+    (1, 2, 1, 70, 128, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,dtype", SMALL)
+@pytest.mark.parametrize("causal", [1, 0])
+def test_small_shapes(B, Hq, Hkv, N, d, dtype, causal):
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype=dtype, seed=N * 31 + d + causal, causal=causal)
+    full_parity(s, poison=True)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_stress_peaked_softmax_small(d):
+    # the wide-head stress distribution (Q, K ~ N(0, 3^2)) at a size the full oracle covers
+    s = workloads.make_shape(2, 8, 2, 512, d, dtype="bf16", seed=5, qk_std=3.0)
+    full_parity(s)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 16), ("f32", 64)])
+def test_query_row_zero_returns_v0(dtype, d):
+    s = workloads.make_shape(2, 6, 2, 150, d, dtype=dtype, seed=3)
+    q, k, v, do = workloads.make_inputs(s)
+    g = run_gpu(q, k, v, do, 1, s.scale)
+    v0 = v.double().numpy()[:, :, 0].repeat(3, axis=1)
+    # P = 1 exactly for row 0; fp16 staging of V is exact above 2^-14 in magnitude
+    assert np.abs(g["o"][:, :, 0] - v0).max() <= 1e-6
+    k0 = k.double().numpy()[:, :, 0].repeat(3, axis=1)
+    lse0 = s.scale * (q.double().numpy()[:, :, 0] * k0).sum(-1)
+    assert np.abs(g["lse"][:, :, 0] - lse0).max() <= 1e-4
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("bf16", 128), ("f32", 32)])
+def test_v_ones(dtype, d):
+    s = workloads.make_shape(1, 4, 2, 333, d, dtype=dtype, seed=4, qk_std=2.0)
+    q, k, _, do = workloads.make_inputs(s)
+    v = torch.ones_like(k)
+    g = run_gpu(q, k, v, do, 1, s.scale)
+    # fp16 P: sum of rounded weights differs from the fp32 row sum by <= 2^-11
+    assert np.abs(g["o"] - 1.0).max() <= 2.0 ** -10
+    scale_dq = np.abs(do.double().numpy()).max() * np.abs(k.double().numpy()).max() * s.scale
+    assert np.abs(g["dq"]).max() <= 2e-3 * scale_dq
+    assert np.abs(g["dk"]).max() <= 2e-3 * scale_dq * 3
+
+
+@pytest.mark.parametrize("name", ["gpt2_mha", "gpt2_gqa"])
+def test_determinism(name):
+    s = workloads.CONFIGS[name]
+    q, k, v, do = _dev(*workloads.make_inputs(s))
+    outs = []
+    for _ in range(3):
+        o, lse = tca.attn_fwd(q, k, v, causal=True, scale=s.scale)
+        dq, dk, dv = tca.attn_bwd(q, k, v, o, lse, do, causal=True, scale=s.scale)
+        torch.cuda.synchronize()
+        outs.append([t.clone() for t in (o, lse, dq, dk, dv)])
+    for rep in outs[1:]:
+        assert torch.equal(rep[0], outs[0][0]) and torch.equal(rep[1], outs[0][1])
+        if s.Hq == s.Hkv:   # no atomics on dK/dV
+            assert torch.equal(rep[3], outs[0][3]) and torch.equal(rep[4], outs[0][4])
+        for a, b in zip(rep[2:], outs[0][2:]):
+            assert (a - b).abs().max().item() <= 1e-5
+
+
+def test_side_stream_matches_default_stream():
+    s = workloads.make_shape(2, 12, 4, 700, 64, dtype="bf16", seed=12)
+    q, k, v, do = _dev(*workloads.make_inputs(s))
+    o1, l1 = tca.attn_fwd(q, k, v)
+    torch.cuda.synchronize()
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        o2, l2 = tca.attn_fwd(q, k, v)
+    st.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_empty_inputs_on_gpu():
+    q = torch.empty(0, 4, 16, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(0, 2, 16, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = tca.attn_fwd(q, k, k)
+    assert o.shape == (0, 4, 16, 64) and lse.shape == (0, 4, 16)
+    q = torch.empty(2, 4, 0, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.empty(2, 2, 0, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = tca.attn_fwd(q, k, k)
+    dq, dk, dv = tca.attn_bwd(q, k, k, o, lse, q)
+    assert dq.shape == q.shape and dk.shape == k.shape

@@ -1,0 +1,162 @@
+"""Python binding for libtca.so: causal GQA tiled attention on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/tca.h. PyTorch provides device
+memory and the current stream. There is no CPU fallback: if the library is
+not built, every call raises.
+
+    o, lse = attn_fwd(q, k, v, causal=True)             # q [B,Hq,N,d], k/v [B,Hkv,N,d]
+    dq, dk, dv = attn_bwd(q, k, v, o, lse, dO, causal=True)
+
+Inputs are float32 or bfloat16 CUDA tensors, contiguous; outputs are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtca.so")
+
+ATTN_F32, ATTN_BF16 = 0, 1
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from the C ABI."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libtca.so with argument types declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                           "(python tiled_causal_attention_amd/build.py)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_abi_version.argtypes, L.attn_abi_version.restype = [], i
+    L.attn_status_str.argtypes, L.attn_status_str.restype = [i], ctypes.c_char_p
+    L.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_fwd_workspace_bytes.restype = sz
+    L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_fwd.argtypes = [i, vp, vp, vp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.restype = i
+    bwd_args = [i, vp, vp, vp, fp, fp, vp, fp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    for name in ("attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"):
+        getattr(L, name).argtypes = bwd_args
+        getattr(L, name).restype = i
+    _lib = L
+    return L
+
+
+def status_str(status: int) -> str:
+    return lib().attn_status_str(int(status)).decode()
+
+
+def _check(status: int):
+    if status != ATTN_OK:
+        raise AttnError(status, status_str(status))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported input dtype {t.dtype}; use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dims(q: torch.Tensor, k: torch.Tensor):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    return B, Hq, k.shape[1], N, d
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+             scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
+             ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (o float32 [B,Hq,N,d], lse float32 [B,Hq,N])."""
+    B, Hq, Hkv, N, d = _dims(q, k)
+    scale = default_scale(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    L = lib()
+    ws_bytes = L.attn_fwd_workspace_bytes(dt, B, Hq, Hkv, N, d)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check(L.attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
+                      B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
+    return o, lse
+
+
+def bwd_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
+    B, Hq, Hkv, N, d = _dims(q, k)
+    n = lib().attn_bwd_workspace_bytes(_dtype_code(q), B, Hq, Hkv, N, d)
+    return torch.empty(max(int(n), 1), dtype=torch.uint8, device=q.device)
+
+
+def _bwd_call(name, q, k, v, o, lse, dO, dq, dk, dv, ws, causal, scale):
+    B, Hq, Hkv, N, d = _dims(q, k)
+    scale = default_scale(d) if scale is None else float(scale)
+    _check(getattr(lib(), name)(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
+
+
+def attn_bwd(q, k, v, o, lse, dO, causal: bool = True, scale: Optional[float] = None,
+             out=None, workspace: Optional[torch.Tensor] = None):
+    """Backward: returns (dq float32 [B,Hq,N,d], dk, dv float32 [B,Hkv,N,d])."""
+    if out is None:
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    else:
+        dq, dk, dv = out
+    ws = bwd_workspace(q, k) if workspace is None else workspace
+    _bwd_call("attn_bwd", q, k, v, o, lse, dO, dq, dk, dv, ws, causal, scale)
+    return dq, dk, dv
+
+
+def attn_bwd_preprocess(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
+    """First backward phase (row statistic D and clearing), into preallocated buffers."""
+    _bwd_call("attn_bwd_preprocess", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
+
+
+def attn_bwd_main(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
+    """Second backward phase (the K/V-tile-parallel main loop)."""
+    _bwd_call("attn_bwd_main", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)

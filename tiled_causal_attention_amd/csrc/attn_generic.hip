@@ -1,0 +1,339 @@
+// attn_generic.hip -- float32-arithmetic attention kernels for any supported
+// head dimension and input type, plus the backward preprocess shared by every
+// path.
+//
+// These kernels follow the tile loop of the NanoEuler "Tiled FlashAttention"
+// section literally: one block per query tile, K/V tiles staged in LDS
+// between barriers, and an online softmax per query row. One lane owns one
+// query row (forward, dQ) or one key row (dK/dV), so every reduction is
+// in-lane and the results are deterministic. They serve float32 inputs, where
+// the accuracy target is float32, and bf16 inputs with small head dimensions.
+#include "tca_internal.h"
+
+namespace tca {
+
+constexpr int kGenRows = 64;   // rows (queries or keys) per block = one wave
+constexpr int kGenTile = 32;   // K/V (or Q/dO) rows staged per LDS tile
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kGenRows)
+fwd_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                   float* __restrict__ o, float* __restrict__ lse,
+                   int Hq, int Hkv, int N, int causal, float scale) {
+    __shared__ float Ks[kGenTile][D];
+    __shared__ float Vs[kGenTile][D];
+    const int bh = blockIdx.y;
+    const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
+    const int i = blockIdx.x * kGenRows + threadIdx.x;
+    const T* qh = q + (size_t)bh * N * D;
+    const T* kh = k + ((size_t)b * Hkv + hkv) * N * D;
+    const T* vh = v + ((size_t)b * Hkv + hkv) * N * D;
+
+    float qr[D], acc[D];
+    float m = -INFINITY, l = 0.f;
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        qr[c] = (i < N) ? load_as_f32(qh + (size_t)i * D + c) : 0.f;
+        acc[c] = 0.f;
+    }
+    const int last_row = min(N, (int)(blockIdx.x + 1) * kGenRows) - 1;
+    const int kend = causal ? last_row + 1 : N;
+    for (int k0 = 0; k0 < kend; k0 += kGenTile) {
+        for (int x = threadIdx.x; x < kGenTile * D; x += kGenRows) {
+            const int r = x / D, c = x % D;
+            const bool ok = k0 + r < N;
+            Ks[r][c] = ok ? load_as_f32(kh + (size_t)(k0 + r) * D + c) : 0.f;
+            Vs[r][c] = ok ? load_as_f32(vh + (size_t)(k0 + r) * D + c) : 0.f;
+        }
+        __syncthreads();
+        if (i < N) {
+            for (int jj = 0; jj < kGenTile; ++jj) {
+                const int j = k0 + jj;
+                if (j >= N || (causal && j > i)) break;
+                float dot = 0.f;
+#pragma unroll
+                for (int c = 0; c < D; ++c) dot = fmaf(qr[c], Ks[jj][c], dot);
+                const float s = scale * dot;
+                if (s > m) {
+                    const float alpha = expf(m - s);
+                    l *= alpha;
+#pragma unroll
+                    for (int c = 0; c < D; ++c) acc[c] *= alpha;
+                    m = s;
+                }
+                const float p = expf(s - m);
+                l += p;
+#pragma unroll
+                for (int c = 0; c < D; ++c) acc[c] = fmaf(p, Vs[jj][c], acc[c]);
+            }
+        }
+        __syncthreads();
+    }
+    if (i < N) {
+        const float inv = 1.f / l;
+        float* oi = o + ((size_t)bh * N + i) * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) oi[c] = acc[c] * inv;
+        lse[(size_t)bh * N + i] = m + logf(l);
+    }
+}
+
+// dK, dV for one KV head: one lane per key, looping over every query head of
+// the group and every visible query. No atomics: each key row is owned by one lane.
+template <typename T, int D>
+__global__ void __launch_bounds__(kGenRows)
+bwd_dkdv_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                        const float* __restrict__ lse, const T* __restrict__ dout,
+                        const float* __restrict__ delta,
+                        float* __restrict__ dk, float* __restrict__ dv,
+                        int Hq, int Hkv, int N, int causal, float scale) {
+    __shared__ float Qs[kGenTile][D];
+    __shared__ float dOs[kGenTile][D];
+    __shared__ float Ls[kGenTile], Ds[kGenTile];
+    const int bkv = blockIdx.y;
+    const int b = bkv / Hkv, hkv = bkv % Hkv, group = Hq / Hkv;
+    const int j = blockIdx.x * kGenRows + threadIdx.x;
+    const size_t kvoff = (size_t)bkv * N * D;
+
+    float kr[D], vr[D], dkr[D], dvr[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        kr[c] = (j < N) ? load_as_f32(k + kvoff + (size_t)j * D + c) : 0.f;
+        vr[c] = (j < N) ? load_as_f32(v + kvoff + (size_t)j * D + c) : 0.f;
+        dkr[c] = 0.f;
+        dvr[c] = 0.f;
+    }
+    const int first_key = blockIdx.x * kGenRows;
+    const int qstart = causal ? (first_key / kGenTile) * kGenTile : 0;
+    for (int g = 0; g < group; ++g) {
+        const int hq = hkv * group + g;
+        const size_t qrow0 = ((size_t)b * Hq + hq) * N;
+        for (int i0 = qstart; i0 < N; i0 += kGenTile) {
+            for (int x = threadIdx.x; x < kGenTile * D; x += kGenRows) {
+                const int r = x / D, c = x % D;
+                const bool ok = i0 + r < N;
+                Qs[r][c] = ok ? load_as_f32(q + (qrow0 + i0 + r) * D + c) : 0.f;
+                dOs[r][c] = ok ? load_as_f32(dout + (qrow0 + i0 + r) * D + c) : 0.f;
+            }
+            for (int r = threadIdx.x; r < kGenTile; r += kGenRows) {
+                const bool ok = i0 + r < N;
+                Ls[r] = ok ? lse[qrow0 + i0 + r] : 0.f;
+                Ds[r] = ok ? delta[qrow0 + i0 + r] : 0.f;
+            }
+            __syncthreads();
+            if (j < N) {
+                for (int ii = 0; ii < kGenTile; ++ii) {
+                    const int i = i0 + ii;
+                    if (i >= N) break;
+                    if (causal && j > i) continue;
+                    float s = 0.f, dp = 0.f;
+#pragma unroll
+                    for (int c = 0; c < D; ++c) {
+                        s = fmaf(Qs[ii][c], kr[c], s);
+                        dp = fmaf(dOs[ii][c], vr[c], dp);
+                    }
+                    const float p = expf(scale * s - Ls[ii]);
+                    const float ds = p * (dp - Ds[ii]);
+#pragma unroll
+                    for (int c = 0; c < D; ++c) {
+                        dvr[c] = fmaf(p, dOs[ii][c], dvr[c]);
+                        dkr[c] = fmaf(ds, Qs[ii][c], dkr[c]);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (j < N) {
+        float* dkj = dk + kvoff + (size_t)j * D;
+        float* dvj = dv + kvoff + (size_t)j * D;
+#pragma unroll
+        for (int c = 0; c < D; ++c) {
+            dkj[c] = scale * dkr[c];
+            dvj[c] = dvr[c];
+        }
+    }
+}
+
+// dQ: one lane per query row, looping over the visible keys.
+template <typename T, int D>
+__global__ void __launch_bounds__(kGenRows)
+bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                      const float* __restrict__ lse, const T* __restrict__ dout,
+                      const float* __restrict__ delta, float* __restrict__ dq,
+                      int Hq, int Hkv, int N, int causal, float scale) {
+    __shared__ float Ks[kGenTile][D];
+    __shared__ float Vs[kGenTile][D];
+    const int bh = blockIdx.y;
+    const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
+    const int i = blockIdx.x * kGenRows + threadIdx.x;
+    const size_t qrow = (size_t)bh * N + i;
+    const T* kh = k + ((size_t)b * Hkv + hkv) * N * D;
+    const T* vh = v + ((size_t)b * Hkv + hkv) * N * D;
+
+    float qr[D], dor[D], dqr[D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+        qr[c] = (i < N) ? load_as_f32(q + qrow * D + c) : 0.f;
+        dor[c] = (i < N) ? load_as_f32(dout + qrow * D + c) : 0.f;
+        dqr[c] = 0.f;
+    }
+    const float L = (i < N) ? lse[qrow] : 0.f;
+    const float Di = (i < N) ? delta[qrow] : 0.f;
+    const int last_row = min(N, (int)(blockIdx.x + 1) * kGenRows) - 1;
+    const int kend = causal ? last_row + 1 : N;
+    for (int k0 = 0; k0 < kend; k0 += kGenTile) {
+        for (int x = threadIdx.x; x < kGenTile * D; x += kGenRows) {
+            const int r = x / D, c = x % D;
+            const bool ok = k0 + r < N;
+            Ks[r][c] = ok ? load_as_f32(kh + (size_t)(k0 + r) * D + c) : 0.f;
+            Vs[r][c] = ok ? load_as_f32(vh + (size_t)(k0 + r) * D + c) : 0.f;
+        }
+        __syncthreads();
+        if (i < N) {
+            for (int jj = 0; jj < kGenTile; ++jj) {
+                const int j = k0 + jj;
+                if (j >= N || (causal && j > i)) break;
+                float s = 0.f, dp = 0.f;
+#pragma unroll
+                for (int c = 0; c < D; ++c) {
+                    s = fmaf(qr[c], Ks[jj][c], s);
+                    dp = fmaf(dor[c], Vs[jj][c], dp);
+                }
+                const float p = expf(scale * s - L);
+                const float ds = p * (dp - Di);
+#pragma unroll
+                for (int c = 0; c < D; ++c) dqr[c] = fmaf(ds, Ks[jj][c], dqr[c]);
+            }
+        }
+        __syncthreads();
+    }
+    if (i < N) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) dq[qrow * D + c] = scale * dqr[c];
+    }
+}
+
+// Backward preprocess: delta_i = sum_c dO_ic * O_ic for every row, and
+// optional clearing of the buffers the matrix-core backward accumulates into.
+// D/4 lanes cooperate on one row (4 elements each); rows are grid-strided.
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+bwd_preprocess_kernel(const float* __restrict__ o, const T* __restrict__ dout,
+                      float* __restrict__ delta, long rows,
+                      float* __restrict__ zero0, long n0,
+                      float* __restrict__ zero1, float* __restrict__ zero2, long n12) {
+    constexpr int LPR = D / 4;                // lanes per row
+    constexpr int RPB = 256 / LPR;            // rows per block pass
+    const int sub = threadIdx.x % LPR;
+    const long stride_rows = (long)gridDim.x * RPB;
+    // every lane of a row group holds the same `row`, so groups leave the loop together
+    for (long row = (long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows; row += stride_rows) {
+        float acc = 0.f;
+        {
+            const float4 ov = *reinterpret_cast<const float4*>(o + row * D + 4 * sub);
+            float d0, d1, d2, d3;
+            if constexpr (sizeof(T) == 2) {
+                const uint2 w = *reinterpret_cast<const uint2*>(dout + row * D + 4 * sub);
+                d0 = bf16_lo(w.x); d1 = bf16_hi(w.x); d2 = bf16_lo(w.y); d3 = bf16_hi(w.y);
+            } else {
+                const float4 w = *reinterpret_cast<const float4*>(dout + row * D + 4 * sub);
+                d0 = w.x; d1 = w.y; d2 = w.z; d3 = w.w;
+            }
+            acc = d0 * ov.x;
+            acc = fmaf(d1, ov.y, acc);
+            acc = fmaf(d2, ov.z, acc);
+            acc = fmaf(d3, ov.w, acc);
+        }
+#pragma unroll
+        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (sub == 0) delta[row] = acc;
+    }
+    // clearing: float4 grid-stride fills (sizes are multiples of 4 since d is)
+    const long tid = (long)blockIdx.x * 256 + threadIdx.x;
+    const long nthr = (long)gridDim.x * 256;
+    const float4 z = {0.f, 0.f, 0.f, 0.f};
+    if (zero0)
+        for (long x = tid; x < n0 / 4; x += nthr) reinterpret_cast<float4*>(zero0)[x] = z;
+    if (zero1)
+        for (long x = tid; x < n12 / 4; x += nthr) {
+            reinterpret_cast<float4*>(zero1)[x] = z;
+            reinterpret_cast<float4*>(zero2)[x] = z;
+        }
+}
+
+// ---------------------------------------------------------------- launchers
+template <typename T, int D>
+static hipError_t launch_fwd_generic_t(const AttnArgs& a, hipStream_t st) {
+    dim3 grid((a.N + kGenRows - 1) / kGenRows, a.B * a.Hq);
+    hipLaunchKernelGGL((fwd_generic_kernel<T, D>), grid, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.o, a.lse,
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_bwd_generic_t(const AttnArgs& a, hipStream_t st) {
+    dim3 gkv((a.N + kGenRows - 1) / kGenRows, a.B * a.Hkv);
+    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D>), gkv, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
+                       (const T*)a.dout, (const float*)a.workspace, a.dk, a.dv,
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dim3 gq((a.N + kGenRows - 1) / kGenRows, a.B * a.Hq);
+    hipLaunchKernelGGL((bwd_dq_generic_kernel<T, D>), gq, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
+                       (const T*)a.dout, (const float*)a.workspace, a.dq,
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_preprocess_t(const AttnArgs& a, bool clear_dq, bool clear_dkdv, hipStream_t st) {
+    const long rows = (long)a.B * a.Hq * a.N;
+    constexpr int RPB = 256 / (D / 4);
+    long blocks = (rows + RPB - 1) / RPB;
+    if (blocks > 4096) blocks = 4096;
+    if (blocks < 1) blocks = 1;
+    const long nq = rows * D;
+    const long nkv = (long)a.B * a.Hkv * a.N * D;
+    hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const float*)a.o, (const T*)a.dout, (float*)a.workspace, rows,
+                       clear_dq ? a.dq : nullptr, nq,
+                       clear_dkdv ? a.dk : nullptr, clear_dkdv ? a.dv : nullptr, nkv);
+    return hipGetLastError();
+}
+
+#define TCA_DISPATCH_D(D_, FN, ...)                                   \
+    switch (D_) {                                                     \
+        case 16: return FN<16>(__VA_ARGS__);                          \
+        case 32: return FN<32>(__VA_ARGS__);                          \
+        case 64: return FN<64>(__VA_ARGS__);                          \
+        case 128: return FN<128>(__VA_ARGS__);                        \
+        default: return hipErrorInvalidValue;                         \
+    }
+
+template <int D> static hipError_t fwd_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<float, D>(a, s); }
+template <int D> static hipError_t fwd_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<bf16_t, D>(a, s); }
+template <int D> static hipError_t bwd_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_t<float, D>(a, s); }
+template <int D> static hipError_t bwd_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_t<bf16_t, D>(a, s); }
+template <int D> static hipError_t pre_f32(const AttnArgs& a, bool cq, bool ckv, hipStream_t s) { return launch_preprocess_t<float, D>(a, cq, ckv, s); }
+template <int D> static hipError_t pre_bf16(const AttnArgs& a, bool cq, bool ckv, hipStream_t s) { return launch_preprocess_t<bf16_t, D>(a, cq, ckv, s); }
+
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st) {
+    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, fwd_gen_f32, a, st) }
+    TCA_DISPATCH_D(a.d, fwd_gen_bf16, a, st)
+}
+
+hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t st) {
+    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, bwd_gen_f32, a, st) }
+    TCA_DISPATCH_D(a.d, bwd_gen_bf16, a, st)
+}
+
+hipError_t launch_bwd_preprocess(const AttnArgs& a, bool clear_dq, bool clear_dkdv, hipStream_t st) {
+    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, pre_f32, a, clear_dq, clear_dkdv, st) }
+    TCA_DISPATCH_D(a.d, pre_bf16, a, clear_dq, clear_dkdv, st)
+}
+
+}  // namespace tca

@@ -1,0 +1,179 @@
+// tca_api.hip -- the extern "C" entry points declared in include/tca.h:
+// argument validation (host only, before any HIP call) and dispatch to the
+// matrix-core or float32-arithmetic kernels.
+#include <math.h>
+#include <stdint.h>
+
+#include "tca_internal.h"
+
+using tca::AttnArgs;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+// Shape, flag and scalar checks shared by every entry point.
+attn_status check_sizes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+    if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_EINVAL;
+    if (Hq % Hkv != 0) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!isfinite(scale)) return ATTN_EINVAL;
+    if ((int64_t)N * d >= ((int64_t)1 << 31)) return ATTN_EINVAL;
+    if ((int64_t)B * Hq * N >= ((int64_t)1 << 31)) return ATTN_EINVAL;
+    if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+    return ATTN_OK;
+}
+
+attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
+    for (const void* p : ptrs)
+        if (p == nullptr || !aligned16(p)) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+size_t bwd_ws_bytes(int B, int Hq, int N) {
+    const size_t bytes = (size_t)B * Hq * N * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+attn_status check_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
+                      const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                      void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                      float scale, bool* noop) {
+    attn_status s = check_sizes(dtype, B, Hq, Hkv, N, d, causal, scale);
+    if (s != ATTN_OK) return s;
+    *noop = ((int64_t)B * N == 0);
+    if (*noop) return ATTN_OK;
+    s = check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, ws});
+    if (s != ATTN_OK) return s;
+    if (ws_bytes < bwd_ws_bytes(B, Hq, N)) return ATTN_EINVAL;
+    return ATTN_OK;
+}
+
+AttnArgs make_args(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
+                   const float* lse, const void* dO, float* dq, float* dk, float* dv, void* ws,
+                   size_t ws_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+    AttnArgs a;
+    a.dtype = dtype;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = const_cast<float*>(o);
+    a.lse = const_cast<float*>(lse);
+    a.dout = dO;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.workspace = ws;
+    a.workspace_bytes = ws_bytes;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.N = N;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    return a;
+}
+
+attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
+
+attn_status run_preprocess(const AttnArgs& a, hipStream_t st) {
+    const bool mfma = tca::mfma_path(a);
+    return from_hip(tca::launch_bwd_preprocess(a, mfma, mfma && tca::bwd_mfma_atomic_dkdv(a), st));
+}
+
+attn_status run_main(const AttnArgs& a, hipStream_t st) {
+    return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma(a, st) : tca::launch_bwd_generic(a, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_abi_version(void) { return kAbiVersion; }
+
+const char* attn_status_str(attn_status s) {
+    switch (s) {
+        case ATTN_OK: return "ATTN_OK";
+        case ATTN_EINVAL: return "ATTN_EINVAL: invalid argument";
+        case ATTN_EUNSUPPORTED: return "ATTN_EUNSUPPORTED: unsupported head dimension";
+        case ATTN_EHIP: return "ATTN_EHIP: HIP runtime error while enqueueing";
+        default: return "unknown attn_status";
+    }
+}
+
+size_t attn_fwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d) {
+    (void)dtype; (void)B; (void)Hq; (void)Hkv; (void)N; (void)d;
+    return 0;
+}
+
+attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, float* o,
+                     float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                     int N, int d, int causal, float scale, void* stream) {
+    attn_status s = check_sizes(dtype, B, Hq, Hkv, N, d, causal, scale);
+    if (s != ATTN_OK) return s;
+    if ((int64_t)B * N == 0) return ATTN_OK;
+    s = check_ptrs({q, k, v, o, lse});
+    if (s != ATTN_OK) return s;
+    if (workspace_bytes < attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, N, d)) return ATTN_EINVAL;
+    const AttnArgs a = make_args(dtype, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr,
+                                 workspace, workspace_bytes, B, Hq, Hkv, N, d, causal, scale);
+    hipStream_t st = (hipStream_t)stream;
+    return from_hip(tca::mfma_path(a) ? tca::launch_fwd_mfma(a, st) : tca::launch_fwd_generic(a, st));
+}
+
+size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d) {
+    (void)dtype; (void)Hkv; (void)d;
+    if (B < 0 || Hq < 0 || N < 0) return 0;
+    return bwd_ws_bytes(B, Hq, N);
+}
+
+attn_status attn_bwd_preprocess(attn_dtype dtype, const void* q, const void* k, const void* v,
+                                const float* o, const float* lse, const void* dO, float* dq,
+                                float* dk, float* dv, void* workspace, size_t workspace_bytes,
+                                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                                void* stream) {
+    bool noop = false;
+    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+                              Hq, Hkv, N, d, causal, scale, &noop);
+    if (s != ATTN_OK || noop) return s;
+    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+                                 B, Hq, Hkv, N, d, causal, scale);
+    return run_preprocess(a, (hipStream_t)stream);
+}
+
+attn_status attn_bwd_main(attn_dtype dtype, const void* q, const void* k, const void* v,
+                          const float* o, const float* lse, const void* dO, float* dq, float* dk,
+                          float* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                          int N, int d, int causal, float scale, void* stream) {
+    bool noop = false;
+    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+                              Hq, Hkv, N, d, causal, scale, &noop);
+    if (s != ATTN_OK || noop) return s;
+    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+                                 B, Hq, Hkv, N, d, causal, scale);
+    return run_main(a, (hipStream_t)stream);
+}
+
+attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
+                     const float* lse, const void* dO, float* dq, float* dk, float* dv,
+                     void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                     int causal, float scale, void* stream) {
+    bool noop = false;
+    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+                              Hq, Hkv, N, d, causal, scale, &noop);
+    if (s != ATTN_OK || noop) return s;
+    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+                                 B, Hq, Hkv, N, d, causal, scale);
+    hipStream_t st = (hipStream_t)stream;
+    s = run_preprocess(a, st);
+    if (s != ATTN_OK) return s;
+    return run_main(a, st);
+}
+
+}  // extern "C"
