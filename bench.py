@@ -2,17 +2,19 @@
 """Throughput of causal GQA attention forward + backward on one MI355X.
 
 A step is one pass of the whole path on one batch of synthetic input:
-attn_fwd (O, LSE), then the backward's two phases, attn_bwd_preprocess
-(D = rowsum(dO o O), clearing) and attn_bwd_main (dQ, dK, dV) -- together
-exactly attn_bwd -- all on torch's current stream, inputs resident in HBM.
+attn_fwd (O, LSE), then the backward's two phases, attn_bwd_dq (D =
+rowsum(dO o O), dQ) and attn_bwd_dkdv (dK, dV) -- together exactly attn_bwd --
+all on torch's current stream, inputs resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa]
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
 N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
-The roofline object describes the dominant kernel (the backward main loop):
-its algorithmic flops per launch divided by its mean duration, measured with
-HIP events recorded on the launch stream around each launch in the timed
+The roofline object describes the dominant kernel (the longest of the
+three): the contraction flops that kernel performs per launch -- per visible
+(query, key) pair 4d for the forward, 6d for the dQ pass (S, dP, dQ) and 8d
+for the dK/dV pass (S, dP, dV, dK) -- divided by its mean duration, measured
+with HIP events recorded on the launch stream around each launch in the timed
 region. cpu_baseline times the float64 oracle on this host on the same
 workload (fwd + bwd).
 """
@@ -33,7 +35,6 @@ import tiled_causal_attention_amd as tca  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X published dense bf16/fp16 matrix peak
-PEAK_HBM_GBS = 8000.0            # MI355X published HBM3E bandwidth
 METRIC = "causal attn fwd+bwd TFLOP/s + % bf16 MFMA peak, B8 Hq12/Hkv4 N1024 d64"
 
 
@@ -130,10 +131,10 @@ def main():
         tca.attn_fwd(q, k, v, causal, scale, out=(o, lse))
         if ev is not None:
             ev[1].record()
-        tca.attn_bwd_preprocess(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+        tca.attn_bwd_dq(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
         if ev is not None:
             ev[2].record()
-        tca.attn_bwd_main(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+        tca.attn_bwd_dkdv(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
         if ev is not None:
             ev[3].record()
 
@@ -149,24 +150,18 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     t_fwd = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    t_pre = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
-    t_main = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    t_dq = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_kv = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
 
     flops_fwd, flops_bwd = s.flops_fwd(), s.flops_bwd()
     tflops = (flops_fwd + flops_bwd) / (ms_per_step * 1e-3) / 1e12
-    kernels = {"attn_fwd": t_fwd, "bwd_preprocess": t_pre, "bwd_main": t_main}
+    kernels = {"attn_fwd": t_fwd, "attn_bwd_dq": t_dq, "attn_bwd_dkdv": t_kv}
+    kernel_flops = {"attn_fwd": flops_fwd, "attn_bwd_dq": 1.5 * flops_fwd, "attn_bwd_dkdv": 2.0 * flops_fwd}
     dom = max(kernels, key=kernels.get)
-    dom_flops = {"attn_fwd": flops_fwd, "bwd_main": flops_bwd, "bwd_preprocess": 0.0}[dom]
-    if dom == "bwd_preprocess":
-        nbytes = s.B * s.Hq * s.N * s.d * (4 + 2) + s.B * s.Hq * s.N * 4
-        achieved = nbytes / (t_pre * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
-    else:
-        achieved = dom_flops / (kernels[dom] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": None,
-                "kernel": dom}
+    achieved = kernel_flops[dom] / (kernels[dom] * 1e-3) / 1e12
+    roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": None, "kernel": dom,
+            "flops_per_launch": kernel_flops[dom]}
 
     result = {
         "metric": METRIC,
@@ -186,7 +181,7 @@ def main():
                    "global_batch": s.B, "seq_len": s.N, "parallelism": "single-gpu"},
         "pct_peak": 100.0 * tflops / PEAK_MFMA_BF16_TFLOPS,
         "fwd_tflops": flops_fwd / (t_fwd * 1e-3) / 1e12,
-        "bwd_tflops": flops_bwd / ((t_pre + t_main) * 1e-3) / 1e12,
+        "bwd_tflops": flops_bwd / ((t_dq + t_kv) * 1e-3) / 1e12,
         "kernel_ms": kernels,
         "roofline": roof,
     }

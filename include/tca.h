@@ -109,10 +109,9 @@ size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N,
  *   q, k, v, sizes, causal flag and scale; dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]
  *   float32, fully overwritten. `workspace` holds at least
  *   attn_bwd_workspace_bytes(...) bytes of device memory; its contents on entry
- *   do not matter. dk and dv are bitwise reproducible for a fixed shape; dq is
- *   accumulated with float32 atomics when dtype is ATTN_BF16 and d is 64 or
- *   128, so its last bits may vary between runs.
- * Equivalent to attn_bwd_preprocess followed by attn_bwd_main on `stream`. */
+ *   do not matter. Every output element is written exactly once (no atomics),
+ *   so dq, dk and dv are bitwise reproducible for fixed inputs.
+ * Equivalent to attn_bwd_dq followed by attn_bwd_dkdv on `stream`. */
 attn_status attn_bwd(attn_dtype dtype,
                      const void* q, const void* k, const void* v,
                      const float* o, const float* lse, const void* dO,
@@ -121,22 +120,22 @@ attn_status attn_bwd(attn_dtype dtype,
                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      void* stream);
 
-/* First phase of attn_bwd: writes D = rowsum(dO o O) (float32, B*Hq*N) into
- * `workspace` and clears whatever attn_bwd_main accumulates into atomically
- * (dq, and dk/dv when Hq > Hkv) for the same dtype and d. dq, dk and dv may be
- * written. Arguments as for attn_bwd. */
-attn_status attn_bwd_preprocess(attn_dtype dtype,
-                                const void* q, const void* k, const void* v,
-                                const float* o, const float* lse, const void* dO,
-                                float* dq, float* dk, float* dv,
-                                void* workspace, size_t workspace_bytes,
-                                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                                void* stream);
+/* First phase of attn_bwd, query-tile parallel: writes D = rowsum(dO o O)
+ * (float32, B*Hq*N) into `workspace`, then dq (recomputing P and dP for each
+ * visible K/V tile). dk and dv are not touched. Arguments as for attn_bwd. */
+attn_status attn_bwd_dq(attn_dtype dtype,
+                        const void* q, const void* k, const void* v,
+                        const float* o, const float* lse, const void* dO,
+                        float* dq, float* dk, float* dv,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                        void* stream);
 
-/* Second phase of attn_bwd: the K/V-tile-parallel main loop. Requires that
- * attn_bwd_preprocess with the same arguments was enqueued before it on the
- * same stream (or completed). Arguments as for attn_bwd. */
-attn_status attn_bwd_main(attn_dtype dtype,
+/* Second phase of attn_bwd, K/V-tile parallel: dk and dv, reading D from
+ * `workspace`. Requires attn_bwd_dq with the same arguments to have been
+ * enqueued before it on the same stream (or completed). dq is not touched.
+ * Arguments as for attn_bwd. */
+attn_status attn_bwd_dkdv(attn_dtype dtype,
                           const void* q, const void* k, const void* v,
                           const float* o, const float* lse, const void* dO,
                           float* dq, float* dk, float* dv,

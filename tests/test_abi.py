@@ -38,7 +38,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
-                     "attn_bwd_preprocess", "attn_bwd_main", "attn_fwd_workspace_bytes",
+                     "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_workspace_bytes",
                      "attn_abi_version"):
         assert required in names
 
@@ -116,7 +116,7 @@ def test_fwd_rejects(L, kw, want):
     assert fwd(L, **kw) == want
 
 
-@pytest.mark.parametrize("name", ["attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"])
+@pytest.mark.parametrize("name", ["attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"])
 @pytest.mark.parametrize("kw,want", [
     (dict(dtype=3), EINVAL),
     (dict(Hq=6, Hkv=4), EINVAL),
@@ -141,7 +141,7 @@ def test_empty_inputs_are_noops(L):
     assert fwd(L, B=0, q=None, k=None, v=None, o=None, lse=None) == OK
     assert fwd(L, N=0, q=None, k=None, v=None, o=None, lse=None) == OK
     nul = dict(q=None, k=None, v=None, o=None, lse=None, dO=None, dq=None, dk=None, dv=None)
-    for name in ("attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"):
+    for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         assert bwd(L, name, B=0, ptrs=nul, ws=None, wsb=0) == OK
         assert bwd(L, name, N=0, ptrs=nul, ws=None, wsb=0) == OK
     # but an empty call with an invalid flag is still rejected

@@ -55,7 +55,7 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd.argtypes = [i, vp, vp, vp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
     L.attn_fwd.restype = i
     bwd_args = [i, vp, vp, vp, fp, fp, vp, fp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
-    for name in ("attn_bwd", "attn_bwd_preprocess", "attn_bwd_main"):
+    for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         getattr(L, name).argtypes = bwd_args
         getattr(L, name).restype = i
     _lib = L
@@ -152,11 +152,11 @@ def attn_bwd(q, k, v, o, lse, dO, causal: bool = True, scale: Optional[float] = 
     return dq, dk, dv
 
 
-def attn_bwd_preprocess(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
-    """First backward phase (row statistic D and clearing), into preallocated buffers."""
-    _bwd_call("attn_bwd_preprocess", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
+def attn_bwd_dq(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
+    """First backward phase (D = rowsum(dO o O) into the workspace, then dq)."""
+    _bwd_call("attn_bwd_dq", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
 
 
-def attn_bwd_main(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
-    """Second backward phase (the K/V-tile-parallel main loop)."""
-    _bwd_call("attn_bwd_main", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
+def attn_bwd_dkdv(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
+    """Second backward phase (dk, dv; reads D from the workspace)."""
+    _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)

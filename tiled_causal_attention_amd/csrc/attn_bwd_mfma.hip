@@ -1,307 +1,483 @@
 // attn_bwd_mfma.hip -- causal GQA attention backward on gfx950 matrix cores.
 //
-// K/V-tile parallel: a workgroup owns BC = 128 keys of one (batch, query head)
-// and keeps their dK, dV accumulators in registers while it walks the query
-// tiles at or below the diagonal. For every query tile (BR rows):
+// The backward the pages hand-derive (P recomputed from the saved
+// log-sum-exp, D = rowsum(dO o O), dS = P o (dP - D), then dQ, dK, dV) runs as
+// two kernels with no atomics, so every output is written exactly once and is
+// bitwise reproducible:
 //
-//   S    = Q K^T           bf16 product, fp32 accumulate     (P recomputed:)
-//   P    = exp2(S*scale*log2e - LSE*log2e)   from the forward's saved LSE
-//   dP   = dO V^T          bf16 product
-//   dS   = P o (dP - D)    D = rowsum(dO o O) from the preprocess kernel
-//   dV  += P^T dO          fp16 product (P rounded to fp16)
-//   dK  += dS^T Q          fp16 product (dS rounded to fp16)
-//   dQ  += dS K * scale    fp16 product, added to global dq with fp32 atomics
+//   1. bwd_dq_kernel, query-tile parallel (the shape of the forward): for its
+//      query rows it computes D from O and dO, writes D to the workspace, then
+//      walks the visible K/V tiles: S^T = K Q^T, P, dP^T = V dO^T, dS, and
+//      dQ^T += K^T dS^T; dQ is stored once at the end.
+//   2. bwd_dkdv_kernel, K/V-tile parallel: a workgroup owns 64 keys of one
+//      (batch, KV head), walks every query head of its GQA group and every
+//      query tile at or below the diagonal, and accumulates dV += P^T dO and
+//      dK += dS^T Q in registers (reading D from the workspace).
 //
-// Layout choices (see tca_device.h for the operand layouts):
-//  * S and dP are computed with queries as rows and keys as columns, so each
-//    lane owns one key; P and dS are then already in the A-operand layout of
-//    the two products that contract over queries (dV, dK).
-//  * Q and dO tiles are staged twice: as bf16 rows (A operands of S and dP,
-//    read at row perm32(m) so accumulator e holds query 16(e/8) + 8h + e%8)
-//    and transposed as fp16 ([d][query], B operands of dV and dK).
-//  * dQ contracts over keys, so dS goes through LDS ([query][key], fp16) and
-//    the four waves split the BR x d dQ tile into 32x32 blocks; K^T (fp16) is
-//    staged once per workgroup for it.
-//  * When several query heads share a KV head, each head's workgroup adds its
-//    dK, dV into fp32 outputs cleared by the preprocess (atomics); with one
-//    query head per KV head they are stored directly.
-//  * Grid order: K/V tile 0 (the longest causal walk) first.
+// Float32 atomics were measured at ~0.6 G adds/ms on this part (an L2 limit):
+// accumulating dQ (or dK/dV across the query heads of a group) through them
+// costs more than recomputing S and dP in a second kernel, which is why dQ has
+// its own pass.
+//
+// Precision: S and dP are bf16 (dQ pass: dP) or fp16 (dK/dV pass, dQ pass S)
+// products of the bf16 inputs -- identical values, since bf16 -> fp16 is
+// exact for |x| >= 2^-14 -- with fp32 accumulation. P and dS, computed values,
+// are rounded to fp16 (not bf16) for the products that consume them; their
+// partner operands are converted to fp16 in registers or when staged to LDS.
 #include "tca_internal.h"
 
 namespace tca {
 
-namespace bwd {
-constexpr int NW = 4;
-constexpr int BC = 32 * NW;   // keys per workgroup
-constexpr int PAD = 8;        // 16-bit elements of row padding (16 bytes)
-template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int BR = 64; };
-template <> struct Cfg<128> { static constexpr int BR = 32; };
-}  // namespace bwd
+namespace bwdq {
+constexpr int NW = 4;            // waves per workgroup
+constexpr int BQ = 32 * NW;      // query rows per workgroup
+constexpr int BC = 64;           // keys per K/V tile
+constexpr int PAD = 8;
+}  // namespace bwdq
 
-template <int D, bool ATOMIC_KV>
+// Global -> registers: K and V rows k0 .. k0 + BC - 1 (clamped to N - 1).
+template <int D, int KCH>
+__device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], const bf16_t* kh,
+                                            const bf16_t* vh, int k0, int N, int tid) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+        const int cid = tid + 256 * u;
+        const int key = min(k0 + cid / CPR, N - 1);
+        const size_t off = (size_t)key * D + (cid % CPR) * 8;
+        kreg[u] = *reinterpret_cast<const u32x4*>(kh + off);
+        vreg[u] = *reinterpret_cast<const u32x4*>(vh + off);
+    }
+}
+
+// Registers -> LDS: K converted to fp16 rows, V kept as bf16 rows.
+template <int D, int KCH>
+__device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH],
+                                             _Float16 (*Ks)[D + bwdq::PAD], bf16_t (*Vs)[D + bwdq::PAD],
+                                             int tid) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int u = 0; u < KCH; ++u) {
+        const int cid = tid + 256 * u;
+        const int row = cid / CPR, col = (cid % CPR) * 8;
+        *reinterpret_cast<u32x4*>(&Ks[row][col]) = bf16x8_to_f16x8(kreg[u]);
+        *reinterpret_cast<u32x4*>(&Vs[row][col]) = vreg[u];
+    }
+}
+
+template <int D>
 __global__ void __launch_bounds__(256, (D == 64) ? 2 : 1)
-bwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                const bf16_t* __restrict__ v, const float* __restrict__ lse,
-                const bf16_t* __restrict__ dout, const float* __restrict__ delta,
-                float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
-                int BH, int Hq, int Hkv, int N, int causal, float scale) {
-    using namespace bwd;
-    constexpr int BR = Cfg<D>::BR;
-    constexpr int DC = D / 16, DB = D / 32, QB = BR / 32;
-    __shared__ __attribute__((aligned(16))) bf16_t Qs[BR][D + PAD];
-    __shared__ __attribute__((aligned(16))) bf16_t dOs[BR][D + PAD];
-    __shared__ __attribute__((aligned(16))) _Float16 Qt[D][BR + PAD];
-    __shared__ __attribute__((aligned(16))) _Float16 dOt[D][BR + PAD];
-    __shared__ __attribute__((aligned(16))) float Ls[BR];
-    __shared__ __attribute__((aligned(16))) float Dl[BR];
-    __shared__ __attribute__((aligned(16))) _Float16 dSs[BR][BC + PAD];
-    __shared__ __attribute__((aligned(16))) _Float16 Kt[D][BC + PAD];
+bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+              const float* __restrict__ o, const float* __restrict__ lse,
+              const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ dq,
+              int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
+    using namespace bwdq;
+    constexpr int DC = D / 16, DB = D / 32, NB = BC / 32, LD = D + PAD;
+    constexpr int CPR = D / 8, KCH = BC * CPR / 256;
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BC][LD];
+    __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BC][LD];
 
-    const int wg = blockIdx.x;
-    const int kt = wg / BH;           // K/V tile: tile 0 has the longest causal walk
-    const int bh = wg % BH;
-    const int b = bh / Hq, hq = bh % Hq, hkv = hq / (Hq / Hkv);
+    const int group = Hq / Hkv;
+    const TileMap tm = map_workgroup(blockIdx.x, nqt, units, Hkv, group);
+    const int hq = tm.hkv * group + tm.g;
+    const size_t bh = (size_t)tm.b * Hq + hq;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, r = lane & 31;
-    const int kbase = kt * BC;
-    const int kw = kbase + 32 * w + r;   // this lane's key
-    const size_t kvoff = ((size_t)b * Hkv + hkv) * N * D;
-    const bf16_t* kh = k + kvoff;
-    const bf16_t* vh = v + kvoff;
-    const bf16_t* qh = q + (size_t)bh * N * D;
-    const bf16_t* doh = dout + (size_t)bh * N * D;
-    const float* lseh = lse + (size_t)bh * N;
-    const float* delh = delta + (size_t)bh * N;
-    float* dqh = dq + (size_t)bh * N * D;
+    const int q0w = tm.qt * BQ + 32 * w;
+    const int qi = q0w + r;
+    const int qc = min(qi, N - 1);
+    const bool qok = qi < N;
+    const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
+    const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = scale * kLog2e;
 
-    // K and V rows of this lane's key as B operands (lane holds row kw, dims 16c + 8h .. +7)
-    bf16x8 kb[DC], vb[DC];
-#pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        if (kw < N) {
-            kb[c] = *reinterpret_cast<const bf16x8*>(kh + (size_t)kw * D + 16 * c + 8 * h);
-            vb[c] = *reinterpret_cast<const bf16x8*>(vh + (size_t)kw * D + 16 * c + 8 * h);
-        } else {
-            kb[c] = bf16x8{};
-            vb[c] = bf16x8{};
-        }
-    }
-    // K^T (fp16) for the dQ product: items of 4 keys x 4 dims
+    // Q (fp16) and dO (bf16) rows of this lane's query as B operands, and D_i
+    f16x8 qb[DC];
+    bf16x8 db[DC];
+    float Di;
     {
-        constexpr int IT = (BC / 4) * (D / 4);
+        const bf16_t* qrow = q + (bh * N + qc) * D + 8 * h;
+        const bf16_t* drow = dout + (bh * N + qc) * D + 8 * h;
+        const float* orow = o + (bh * N + qc) * D + 8 * h;
+        float part = 0.f;
 #pragma unroll
-        for (int u = 0; u < IT / 256; ++u) {
-            const int it = tid + 256 * u;
-            const int dq4 = it % (D / 4), kq4 = it / (D / 4);
-            uint2 rows[4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int key = kbase + 4 * kq4 + rr;
-                rows[rr] = (key < N) ? *reinterpret_cast<const uint2*>(kh + (size_t)key * D + 4 * dq4)
-                                     : uint2{0u, 0u};
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float f[4];
-#pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const uint32_t wv = (e < 2) ? rows[rr].x : rows[rr].y;
-                    f[rr] = (e & 1) ? bf16_hi(wv) : bf16_lo(wv);
-                }
-                *reinterpret_cast<uint2*>(&Kt[4 * dq4 + e][4 * kq4]) = uint2{pack_f16(f[0], f[1]), pack_f16(f[2], f[3])};
-            }
+        for (int c = 0; c < DC; ++c) {
+            const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+            const u32x4 dv = *reinterpret_cast<const u32x4*>(drow + 16 * c);
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
+            const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
+            qb[c] = qok ? __builtin_bit_cast(f16x8, bf16x8_to_f16x8(qv)) : f16x8{};
+            db[c] = qok ? __builtin_bit_cast(bf16x8, dv) : bf16x8{};
+            part = fmaf(bf16_lo(dv.x), o0[0], part);
+            part = fmaf(bf16_hi(dv.x), o0[1], part);
+            part = fmaf(bf16_lo(dv.y), o0[2], part);
+            part = fmaf(bf16_hi(dv.y), o0[3], part);
+            part = fmaf(bf16_lo(dv.z), o1[0], part);
+            part = fmaf(bf16_hi(dv.z), o1[1], part);
+            part = fmaf(bf16_lo(dv.w), o1[2], part);
+            part = fmaf(bf16_hi(dv.w), o1[3], part);
         }
+        Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
+        if (qok && h == 0) delta[bh * N + qi] = Di;
     }
+    const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
 
-    f32x16 dka[DB], dva[DB];
+    u32x4 kreg[KCH], vreg[KCH];
+    f32x16 dqa[DB];
 #pragma unroll
-    for (int x = 0; x < DB; ++x) {
-        dka[x] = f32x16{};
-        dva[x] = f32x16{};
-    }
+    for (int x = 0; x < DB; ++x) dqa[x] = f32x16{};
 
-    const int nqt = (N + BR - 1) / BR;
-    const int qt0 = causal ? kbase / BR : 0;
-    for (int qt = qt0; qt < nqt; ++qt) {
-        const int qbase = qt * BR;
-        __syncthreads();   // the previous step is done reading LDS
-        // ---- stage Q and dO: bf16 rows and fp16 transposed, items of 4 rows x 4 dims
-        {
-            constexpr int IT = (BR / 4) * (D / 4);
+    const int last_q = min(N, (tm.qt + 1) * BQ) - 1;
+    const int kend = causal ? last_q + 1 : N;
+    const int ntile = (kend + BC - 1) / BC;
+    const int krow_a = perm32(r);
+
+    bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, 0, N, tid);
+    bwd_store_kv<D, KCH>(kreg, vreg, Ks[0], Vs[0], tid);
+    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, BC, N, tid);
+    __syncthreads();
+
+    for (int j = 0; j < ntile; ++j) {
+        const int buf = j & 1, k0 = j * BC;
+        if (!causal || k0 <= q0w + 31) {
+            // ---- S^T = K Q^T and dP^T = V dO^T (rows: keys, permuted; columns: queries)
+            f32x16 s[NB], dp[NB];
 #pragma unroll
-            for (int u = 0; u < (IT + 255) / 256; ++u) {
-                const int it = tid + 256 * u;
-                if (IT % 256 == 0 || it < IT) {
-                    const int dq4 = it % (D / 4), rq4 = it / (D / 4);
-                    uint2 qr[4], dr[4];
+            for (int nb = 0; nb < NB; ++nb) {
+                s[nb] = f32x16{};
+                dp[nb] = f32x16{};
+            }
 #pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) {
-                        const int row = qbase + 4 * rq4 + rr;
-                        if (row < N) {
-                            qr[rr] = *reinterpret_cast<const uint2*>(qh + (size_t)row * D + 4 * dq4);
-                            dr[rr] = *reinterpret_cast<const uint2*>(doh + (size_t)row * D + 4 * dq4);
-                        } else {
-                            qr[rr] = uint2{0u, 0u};
-                            dr[rr] = uint2{0u, 0u};
-                        }
-                        *reinterpret_cast<uint2*>(&Qs[4 * rq4 + rr][4 * dq4]) = qr[rr];
-                        *reinterpret_cast<uint2*>(&dOs[4 * rq4 + rr][4 * dq4]) = dr[rr];
+            for (int c = 0; c < DC; ++c)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * nb + krow_a][16 * c + 8 * h]);
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[buf][32 * nb + krow_a][16 * c + 8 * h]);
+                    s[nb] = mfma_f16(ak, qb[c], s[nb]);
+                    dp[nb] = mfma_bf16(av, db[c], dp[nb]);
+                }
+            // ---- P, dS (accumulator e of block nb: key k0 + 32nb + 16(e/8) + 8h + e%8)
+            const bool need_mask = (k0 + BC > N) || (causal && k0 + BC - 1 > q0w);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float p = fast_exp2(fmaf(s[nb][e], sl2, -Li));
+                    if (need_mask) {
+                        const int key = k0 + 32 * nb + 16 * (e >> 3) + 8 * h + (e & 7);
+                        if (key >= N || (causal && key > qi)) p = 0.f;
                     }
+                    s[nb][e] = p * (dp[nb][e] - Di);   // dS
+                }
+            // ---- dQ^T += K^T dS^T  (A: K tile read transposed; B: dS from registers)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float fq[4], fd[4];
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                        for (int rr = 0; rr < 4; ++rr) {
-                            const uint32_t wq = (e < 2) ? qr[rr].x : qr[rr].y;
-                            const uint32_t wd = (e < 2) ? dr[rr].x : dr[rr].y;
-                            fq[rr] = (e & 1) ? bf16_hi(wq) : bf16_lo(wq);
-                            fd[rr] = (e & 1) ? bf16_hi(wd) : bf16_lo(wd);
-                        }
-                        *reinterpret_cast<uint2*>(&Qt[4 * dq4 + e][4 * rq4]) =
-                            uint2{pack_f16(fq[0], fq[1]), pack_f16(fq[2], fq[3])};
-                        *reinterpret_cast<uint2*>(&dOt[4 * dq4 + e][4 * rq4]) =
-                            uint2{pack_f16(fd[0], fd[1]), pack_f16(fd[2], fd[3])};
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const f16x8 dsb = to_f16x8(s[nb][8 * c2 + 0], s[nb][8 * c2 + 1], s[nb][8 * c2 + 2],
+                                               s[nb][8 * c2 + 3], s[nb][8 * c2 + 4], s[nb][8 * c2 + 5],
+                                               s[nb][8 * c2 + 6], s[nb][8 * c2 + 7]);
+#pragma unroll
+                    for (int x = 0; x < DB; ++x) {
+                        const f16x8 a = lds_tr_operand(&Ks[buf][0][0], LD, 32 * nb + 16 * c2, 32 * x, h, r);
+                        dqa[x] = mfma_f16(a, dsb, dqa[x]);
                     }
                 }
-            }
-            if (tid < BR) {
-                const int row = qbase + tid;
-                Ls[tid] = (row < N) ? lseh[row] * kLog2e : 0.f;
-                Dl[tid] = (row < N) ? delh[row] : 0.f;
-            }
+        }
+        if (j + 1 < ntile) {
+            bwd_store_kv<D, KCH>(kreg, vreg, Ks[buf ^ 1], Vs[buf ^ 1], tid);
+            if (j + 2 < ntile) bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, (j + 2) * BC, N, tid);
         }
         __syncthreads();
+    }
 
-        // ---- S = Q K^T and dP = dO V^T (rows: queries, permuted; columns: this wave's keys)
-        f32x16 s[QB], dp[QB];
+    // ---- store dQ: accumulator e of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of query qi
+    if (qok) {
+        float* row = dq + (bh * N + qi) * D;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-            s[qb] = f32x16{};
-            dp[qb] = f32x16{};
-        }
+        for (int x = 0; x < DB; ++x)
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const bf16x8 aq = *reinterpret_cast<const bf16x8*>(&Qs[32 * qb + perm32(r)][16 * c + 8 * h]);
-                const bf16x8 ad = *reinterpret_cast<const bf16x8*>(&dOs[32 * qb + perm32(r)][16 * c + 8 * h]);
-                s[qb] = mfma_bf16(aq, kb[c], s[qb]);
-                dp[qb] = mfma_bf16(ad, vb[c], dp[qb]);
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const f32x4 val = {dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
+                                   dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
+                *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
             }
+    }
+}
 
-        // ---- P and dS (accumulator e of block qb: query qbase + 32qb + 16(e/8) + 8h + e%8)
-        const int kw0 = kbase + 32 * w;
-        const bool need_mask = (qbase + BR > N) || (kw0 + 32 > N) || (causal && qbase < kw0 + 31);
+// ---------------------------------------------------------------------------
+// dK / dV: K/V-tile parallel.
+//
+// A workgroup owns the K/V tiles j and T-1-j (64 keys each) of one (batch, KV
+// head) when causal -- tile j sees T-j query tiles and tile T-1-j sees j+1, so
+// every workgroup does the same amount of work -- or one tile otherwise. Its
+// waves are NKH = 2 key halves x NQW query sub-blocks: wave (kh, qw) handles
+// keys 32kh .. 32kh+31 of the tile and rows 32qw .. 32qw+31 of each staged
+// query tile (BQ = 32 NQW rows), accumulating partial dK, dV for its keys in
+// registers. At the end of a K/V tile the NQW partials of each key half are
+// summed in LDS in a fixed order (deterministic) and written out.
+//
+//   S  = Q K^T, dP = dO V^T  (rows: queries, permuted; columns: keys -> one key
+//                             per lane, so P and dS are A operands in place)
+//   dV += P^T dO, dK += dS^T Q (B operands: dO, Q tiles read transposed)
+namespace bwdkv {
+constexpr int BC = 64;
+constexpr int PAD = 8;
+template <int D> struct Cfg;
+template <> struct Cfg<64> { static constexpr int NQW = 4; };   // 8 waves, 128-row query tiles
+template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles
+}  // namespace bwdkv
+
+template <int D>
+__global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, 1)
+bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                const float* __restrict__ lse, const bf16_t* __restrict__ dout,
+                const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+                int Hq, int Hkv, int N, int causal, float scale, int ntiles, int wg_per_unit) {
+    using namespace bwdkv;
+    constexpr int NQW = Cfg<D>::NQW;
+    constexpr int NT = 64 * 2 * NQW;          // threads
+    constexpr int BQ = 32 * NQW;              // query rows per staged tile
+    constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
+    constexpr int CPR = D / 8;
+    constexpr int QCH = BQ * CPR / NT;        // 16-byte chunks per thread per tensor per tile
+    __shared__ __attribute__((aligned(16))) _Float16 Qs[2][BQ][LD];
+    __shared__ __attribute__((aligned(16))) _Float16 dOs[2][BQ][LD];
+    __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
+    __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+    __shared__ __attribute__((aligned(16))) float red[2][BC][D];   // dK, dV partial sums
+
+    const int group = Hq / Hkv;
+    const int unit = blockIdx.x / wg_per_unit;
+    const int slot = blockIdx.x % wg_per_unit;
+    const int b = unit / Hkv, hkv = unit % Hkv;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, r = lane & 31;
+    const int kh_ = w & 1, qw = w >> 1;       // key half, query sub-block
+    const size_t kvoff = ((size_t)b * Hkv + hkv) * N * D;
+    const float sl2 = scale * kLog2e;
+    const int nqt = (N + BQ - 1) / BQ;
+
+    // K/V tiles of this workgroup: causal -> {slot, ntiles-1-slot} (one if they coincide)
+    const int tile_a = slot;
+    const int tile_b = (causal && ntiles - 1 - slot != slot) ? ntiles - 1 - slot : -1;
+
+    // items: (tile index t in {0,1}, head g, query tile i); for each tile, the
+    // query tiles at or below the diagonal, for every head of the group
+    auto first_qt = [&](int tile) { return causal ? (tile * BC) / BQ : 0; };
+    const int na = group * (nqt - first_qt(tile_a));
+    const int nbitems = (tile_b >= 0) ? group * (nqt - first_qt(tile_b)) : 0;
+    const int nitems = na + nbitems;
+
+    u32x4 qreg[QCH], dreg[QCH];
+    float lreg = 0.f, dlreg = 0.f;
+    // decode item -> (tile, head, query tile)
+    auto item = [&](int it, int& tile, int& g, int& qt) {
+        const int t = (it < na) ? 0 : 1;
+        const int rel = t ? it - na : it;
+        tile = t ? tile_b : tile_a;
+        const int f = first_qt(tile), per = nqt - f;
+        g = rel / per;
+        qt = f + rel % per;
+    };
+    auto load_item = [&](int it) {
+        int tile, g, qt;
+        item(it, tile, g, qt);
+        const size_t bh = (size_t)b * Hq + hkv * group + g;
+        const bf16_t* qh = q + bh * N * D;
+        const bf16_t* dh = dout + bh * N * D;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int u = 0; u < QCH; ++u) {
+            const int cid = tid + NT * u;
+            const int row = min(qt * BQ + cid / CPR, N - 1);
+            const size_t off = (size_t)row * D + (cid % CPR) * 8;
+            qreg[u] = *reinterpret_cast<const u32x4*>(qh + off);
+            dreg[u] = *reinterpret_cast<const u32x4*>(dh + off);
+        }
+        if (tid < BQ) {
+            const int row = qt * BQ + tid;
+            const int rc = min(row, N - 1);
+            lreg = lse[bh * N + rc] * kLog2e;
+            dlreg = delta[bh * N + rc];
+        }
+    };
+    auto store_item = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < QCH; ++u) {
+            const int cid = tid + NT * u;
+            const int row = cid / CPR, col = (cid % CPR) * 8;
+            *reinterpret_cast<u32x4*>(&Qs[buf][row][col]) = bf16x8_to_f16x8(qreg[u]);
+            *reinterpret_cast<u32x4*>(&dOs[buf][row][col]) = bf16x8_to_f16x8(dreg[u]);
+        }
+        if (tid < BQ) {
+            Ls[buf][tid] = lreg;
+            Ds[buf][tid] = dlreg;
+        }
+    };
+
+    f16x8 kb[DC], vb[DC];
+    f32x16 dka[DB], dva[DB];
+    int cur_tile = -1;
+
+    if (nitems > 0) {
+        load_item(0);
+        store_item(0);
+        if (nitems > 1) load_item(1);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < nitems; ++it) {
+        const int buf = it & 1;
+        int tile, g, qt;
+        item(it, tile, g, qt);
+        const int kw0 = tile * BC + 32 * kh_;   // first key of this wave
+        const int kw = kw0 + r;                 // this lane's key
+        if (tile != cur_tile) {
+            // new K/V tile: this lane's K, V rows as fp16 B operands; clear partials
+            cur_tile = tile;
+            const bf16_t* krow = k + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
+            const bf16_t* vrow = v + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                kb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(krow + 16 * c)));
+                vb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(vrow + 16 * c)));
+            }
+#pragma unroll
+            for (int x = 0; x < DB; ++x) {
+                dka[x] = f32x16{};
+                dva[x] = f32x16{};
+            }
+        }
+        const int q0 = qt * BQ + 32 * qw;        // first query row of this wave's block
+        const bool live = !causal || q0 + 31 >= kw0;
+        if (live) {
+            // ---- S = Q K^T, dP = dO V^T (accumulator e: query q0 + 16(e/8) + 8h + e%8, key kw)
+            f32x16 s = f32x16{}, dp = f32x16{};
+            const int arow = 32 * qw + perm32(r);
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const f16x8 aq = *reinterpret_cast<const f16x8*>(&Qs[buf][arow][16 * c + 8 * h]);
+                const f16x8 ad = *reinterpret_cast<const f16x8*>(&dOs[buf][arow][16 * c + 8 * h]);
+                s = mfma_f16(aq, kb[c], s);
+                dp = mfma_f16(ad, vb[c], dp);
+            }
+            const bool need_mask = (q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31);
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const int qq = 32 * qb + 16 * c2 + 8 * h;   // first tile row of this 8-group
-                const float4 l0 = *reinterpret_cast<const float4*>(&Ls[qq]);
-                const float4 l1 = *reinterpret_cast<const float4*>(&Ls[qq + 4]);
-                const float4 d0 = *reinterpret_cast<const float4*>(&Dl[qq]);
-                const float4 d1 = *reinterpret_cast<const float4*>(&Dl[qq + 4]);
-                const float lv[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                const float dl[8] = {d0.x, d0.y, d0.z, d0.w, d1.x, d1.y, d1.z, d1.w};
+                const int qq = 32 * qw + 16 * c2 + 8 * h;   // tile row of accumulator 8c2
+                const f32x4 l0 = *reinterpret_cast<const f32x4*>(&Ls[buf][qq]);
+                const f32x4 l1 = *reinterpret_cast<const f32x4*>(&Ls[buf][qq + 4]);
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(&Ds[buf][qq]);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(&Ds[buf][qq + 4]);
+                const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+                const float dl[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int e = 8 * c2 + t;
-                    float p = fast_exp2(fmaf(s[qb][e], sl2, -lv[t]));
+                    float p = fast_exp2(fmaf(s[e], sl2, -lv[t]));
                     if (need_mask) {
-                        const int qrow = qbase + qq + t;
+                        const int qrow = qt * BQ + qq + t;
                         if (qrow >= N || kw >= N || (causal && kw > qrow)) p = 0.f;
                     }
-                    s[qb][e] = p;
-                    dp[qb][e] = p * (dp[qb][e] - dl[t]);
+                    s[e] = p;
+                    dp[e] = p * (dp[e] - dl[t]);
                 }
             }
-
-        // ---- dV += P^T dO and dK += dS^T Q  (A: this lane's key row; B: transposed tiles)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+            // ---- dV += P^T dO, dK += dS^T Q (B: dO, Q tiles read transposed, rows = queries)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
-                const int e0 = 8 * c2;
-                const f16x8 pa = to_f16x8(s[qb][e0 + 0], s[qb][e0 + 1], s[qb][e0 + 2], s[qb][e0 + 3],
-                                          s[qb][e0 + 4], s[qb][e0 + 5], s[qb][e0 + 6], s[qb][e0 + 7]);
-                const f16x8 da = to_f16x8(dp[qb][e0 + 0], dp[qb][e0 + 1], dp[qb][e0 + 2], dp[qb][e0 + 3],
-                                          dp[qb][e0 + 4], dp[qb][e0 + 5], dp[qb][e0 + 6], dp[qb][e0 + 7]);
-                const int qq = 32 * qb + 16 * c2 + 8 * h;
+                const f16x8 pa = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                          s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+                const f16x8 da = to_f16x8(dp[8 * c2 + 0], dp[8 * c2 + 1], dp[8 * c2 + 2], dp[8 * c2 + 3],
+                                          dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
 #pragma unroll
                 for (int x = 0; x < DB; ++x) {
-                    const f16x8 bo = *reinterpret_cast<const f16x8*>(&dOt[32 * x + r][qq]);
-                    const f16x8 bq = *reinterpret_cast<const f16x8*>(&Qt[32 * x + r][qq]);
+                    const f16x8 bo = lds_tr_operand(&dOs[buf][0][0], LD, 32 * qw + 16 * c2, 32 * x, h, r);
+                    const f16x8 bq = lds_tr_operand(&Qs[buf][0][0], LD, 32 * qw + 16 * c2, 32 * x, h, r);
                     dva[x] = mfma_f16(pa, bo, dva[x]);
                     dka[x] = mfma_f16(da, bq, dka[x]);
                 }
-                // dS to LDS as [query][key] for the dQ product
-#pragma unroll
-                for (int t = 0; t < 8; ++t) dSs[qq + t][32 * w + r] = da[t];
-            }
-        __syncthreads();
-
-        // ---- dQ (BR x D) += dS (BR x BC) * K (BC x D), 32x32 blocks split over the waves
-#pragma unroll
-        for (int blk = w; blk < QB * DB; blk += NW) {
-            const int qb = blk / DB, x = blk % DB;
-            f32x16 acc = f32x16{};
-#pragma unroll
-            for (int kc = 0; kc < BC / 16; ++kc) {
-                const f16x8 a = *reinterpret_cast<const f16x8*>(&dSs[32 * qb + r][16 * kc + 8 * h]);
-                const f16x8 bk = *reinterpret_cast<const f16x8*>(&Kt[32 * x + r][16 * kc + 8 * h]);
-                acc = mfma_f16(a, bk, acc);
-            }
-            // accumulator e: query 32qb + 8(e/4) + 4h + e%4, dim 32x + r
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int qrow = qbase + 32 * qb + 8 * (e >> 2) + 4 * h + (e & 3);
-                if (qrow < N) unsafeAtomicAdd(dqh + (size_t)qrow * D + 32 * x + r, scale * acc[e]);
             }
         }
-    }
-
-    // ---- epilogue: accumulator e of dim block x holds key kbase + 32w + 8(e/4) + 4h + e%4, dim 32x + r
+        if (it + 1 < nitems) {
+            store_item(buf ^ 1);
+            if (it + 2 < nitems) load_item(it + 2);
+        }
+        // ---- end of a K/V tile: fixed-order reduction of the query sub-block partials
+        int ntile_next = -1;
+        if (it + 1 < nitems) {
+            int g2, qt2;
+            item(it + 1, ntile_next, g2, qt2);
+        }
+        if (ntile_next != tile) {
+            // accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r
+#pragma unroll 1
+            for (int step = 0; step < NQW; ++step) {
+                if (qw == step) {
 #pragma unroll
-    for (int x = 0; x < DB; ++x)
+                    for (int x = 0; x < DB; ++x)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int key = kbase + 32 * w + 8 * (e >> 2) + 4 * h + (e & 3);
-            if (key < N) {
-                const size_t off = kvoff + (size_t)key * D + 32 * x + r;
-                if (ATOMIC_KV) {
-                    unsafeAtomicAdd(dk + off, scale * dka[x][e]);
-                    unsafeAtomicAdd(dv + off, dva[x][e]);
-                } else {
-                    dk[off] = scale * dka[x][e];
-                    dv[off] = dva[x][e];
+                        for (int e = 0; e < 16; ++e) {
+                            const int key = 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
+                            float* pk = &red[0][key][32 * x + r];
+                            float* pv = &red[1][key][32 * x + r];
+                            if (step == 0) {
+                                *pk = dka[x][e];
+                                *pv = dva[x][e];
+                            } else {
+                                *pk += dka[x][e];
+                                *pv += dva[x][e];
+                            }
+                        }
+                }
+                __syncthreads();
+            }
+            // write the tile's dK (scaled) and dV rows
+            const int key0 = tile * BC;
+            constexpr int F4 = BC * D / 4;   // float4 per tensor
+#pragma unroll
+            for (int u = 0; u < F4 / NT; ++u) {
+                const int idx = tid + NT * u;
+                const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
+                if (key0 + row < N) {
+                    const f32x4 kv = *reinterpret_cast<const f32x4*>(&red[0][row][col]);
+                    const f32x4 vv = *reinterpret_cast<const f32x4*>(&red[1][row][col]);
+                    const size_t off = kvoff + (size_t)(key0 + row) * D + col;
+                    *reinterpret_cast<f32x4*>(dk + off) = kv * scale;
+                    *reinterpret_cast<f32x4*>(dv + off) = vv;
                 }
             }
         }
+        __syncthreads();
+    }
 }
 
-bool bwd_mfma_atomic_dkdv(const AttnArgs& a) { return a.Hq != a.Hkv; }
-
 template <int D>
-static hipError_t launch_bwd_mfma_d(const AttnArgs& a, hipStream_t st) {
-    const int BH = a.B * a.Hq;
-    const int nkt = (a.N + bwd::BC - 1) / bwd::BC;
-    const dim3 grid((unsigned)(nkt * BH));
-    if (bwd_mfma_atomic_dkdv(a))
-        hipLaunchKernelGGL((bwd_mfma_kernel<D, true>), grid, dim3(256), 0, st, (const bf16_t*)a.q,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.lse,
-                           (const bf16_t*)a.dout, (const float*)a.workspace, a.dq, a.dk, a.dv, BH,
-                           a.Hq, a.Hkv, a.N, a.causal, a.scale);
-    else
-        hipLaunchKernelGGL((bwd_mfma_kernel<D, false>), grid, dim3(256), 0, st, (const bf16_t*)a.q,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.lse,
-                           (const bf16_t*)a.dout, (const float*)a.workspace, a.dq, a.dk, a.dv, BH,
-                           a.Hq, a.Hkv, a.N, a.causal, a.scale);
+static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
+    const int nqt = (a.N + bwdq::BQ - 1) / bwdq::BQ;
+    const int units = a.B * a.Hkv;
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0, st,
+                       (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.o,
+                       (const float*)a.lse, (const bf16_t*)a.dout, (float*)a.workspace, a.dq, a.Hq,
+                       a.Hkv, a.N, a.causal, a.scale, nqt, units);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t st) {
-    return (a.d == 64) ? launch_bwd_mfma_d<64>(a, st) : launch_bwd_mfma_d<128>(a, st);
+template <int D>
+static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
+    const int ntiles = (a.N + bwdkv::BC - 1) / bwdkv::BC;
+    const int per_unit = a.causal ? (ntiles + 1) / 2 : ntiles;
+    const int threads = 64 * 2 * bwdkv::Cfg<D>::NQW;
+    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
+                       (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.lse,
+                       (const bf16_t*)a.dout, (const float*)a.workspace, a.dk, a.dv, a.Hq, a.Hkv, a.N,
+                       a.causal, a.scale, ntiles, per_unit);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st) {
+    return (a.d == 64) ? launch_bwd_dq_d<64>(a, st) : launch_bwd_dq_d<128>(a, st);
+}
+hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st) {
+    return (a.d == 64) ? launch_bwd_dkdv_d<64>(a, st) : launch_bwd_dkdv_d<128>(a, st);
 }
 
 }  // namespace tca

@@ -1,6 +1,5 @@
 // attn_generic.hip -- float32-arithmetic attention kernels for any supported
-// head dimension and input type, plus the backward preprocess shared by every
-// path.
+// head dimension and input type.
 //
 // These kernels follow the tile loop of the NanoEuler "Tiled FlashAttention"
 // section literally: one block per query tile, K/V tiles staged in LDS
@@ -155,12 +154,13 @@ bwd_dkdv_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
     }
 }
 
-// dQ: one lane per query row, looping over the visible keys.
+// dQ: one lane per query row, looping over the visible keys. The lane first
+// forms D_i = <dO_i, O_i> and publishes it (the dK/dV kernel reads it).
 template <typename T, int D>
 __global__ void __launch_bounds__(kGenRows)
 bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                      const float* __restrict__ lse, const T* __restrict__ dout,
-                      const float* __restrict__ delta, float* __restrict__ dq,
+                      const float* __restrict__ o, const float* __restrict__ lse,
+                      const T* __restrict__ dout, float* __restrict__ delta, float* __restrict__ dq,
                       int Hq, int Hkv, int N, int causal, float scale) {
     __shared__ float Ks[kGenTile][D];
     __shared__ float Vs[kGenTile][D];
@@ -179,7 +179,12 @@ bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
         dqr[c] = 0.f;
     }
     const float L = (i < N) ? lse[qrow] : 0.f;
-    const float Di = (i < N) ? delta[qrow] : 0.f;
+    float Di = 0.f;
+    if (i < N) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) Di = fmaf(dor[c], o[qrow * D + c], Di);
+        delta[qrow] = Di;
+    }
     const int last_row = min(N, (int)(blockIdx.x + 1) * kGenRows) - 1;
     const int kend = causal ? last_row + 1 : N;
     for (int k0 = 0; k0 < kend; k0 += kGenTile) {
@@ -214,54 +219,6 @@ bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     }
 }
 
-// Backward preprocess: delta_i = sum_c dO_ic * O_ic for every row, and
-// optional clearing of the buffers the matrix-core backward accumulates into.
-// D/4 lanes cooperate on one row (4 elements each); rows are grid-strided.
-template <typename T, int D>
-__global__ void __launch_bounds__(256)
-bwd_preprocess_kernel(const float* __restrict__ o, const T* __restrict__ dout,
-                      float* __restrict__ delta, long rows,
-                      float* __restrict__ zero0, long n0,
-                      float* __restrict__ zero1, float* __restrict__ zero2, long n12) {
-    constexpr int LPR = D / 4;                // lanes per row
-    constexpr int RPB = 256 / LPR;            // rows per block pass
-    const int sub = threadIdx.x % LPR;
-    const long stride_rows = (long)gridDim.x * RPB;
-    // every lane of a row group holds the same `row`, so groups leave the loop together
-    for (long row = (long)blockIdx.x * RPB + threadIdx.x / LPR; row < rows; row += stride_rows) {
-        float acc = 0.f;
-        {
-            const float4 ov = *reinterpret_cast<const float4*>(o + row * D + 4 * sub);
-            float d0, d1, d2, d3;
-            if constexpr (sizeof(T) == 2) {
-                const uint2 w = *reinterpret_cast<const uint2*>(dout + row * D + 4 * sub);
-                d0 = bf16_lo(w.x); d1 = bf16_hi(w.x); d2 = bf16_lo(w.y); d3 = bf16_hi(w.y);
-            } else {
-                const float4 w = *reinterpret_cast<const float4*>(dout + row * D + 4 * sub);
-                d0 = w.x; d1 = w.y; d2 = w.z; d3 = w.w;
-            }
-            acc = d0 * ov.x;
-            acc = fmaf(d1, ov.y, acc);
-            acc = fmaf(d2, ov.z, acc);
-            acc = fmaf(d3, ov.w, acc);
-        }
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (sub == 0) delta[row] = acc;
-    }
-    // clearing: float4 grid-stride fills (sizes are multiples of 4 since d is)
-    const long tid = (long)blockIdx.x * 256 + threadIdx.x;
-    const long nthr = (long)gridDim.x * 256;
-    const float4 z = {0.f, 0.f, 0.f, 0.f};
-    if (zero0)
-        for (long x = tid; x < n0 / 4; x += nthr) reinterpret_cast<float4*>(zero0)[x] = z;
-    if (zero1)
-        for (long x = tid; x < n12 / 4; x += nthr) {
-            reinterpret_cast<float4*>(zero1)[x] = z;
-            reinterpret_cast<float4*>(zero2)[x] = z;
-        }
-}
-
 // ---------------------------------------------------------------- launchers
 template <typename T, int D>
 static hipError_t launch_fwd_generic_t(const AttnArgs& a, hipStream_t st) {
@@ -273,35 +230,22 @@ static hipError_t launch_fwd_generic_t(const AttnArgs& a, hipStream_t st) {
 }
 
 template <typename T, int D>
-static hipError_t launch_bwd_generic_t(const AttnArgs& a, hipStream_t st) {
-    dim3 gkv((a.N + kGenRows - 1) / kGenRows, a.B * a.Hkv);
-    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D>), gkv, dim3(kGenRows), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
-                       (const T*)a.dout, (const float*)a.workspace, a.dk, a.dv,
-                       a.Hq, a.Hkv, a.N, a.causal, a.scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+static hipError_t launch_bwd_generic_dq_t(const AttnArgs& a, hipStream_t st) {
     dim3 gq((a.N + kGenRows - 1) / kGenRows, a.B * a.Hq);
     hipLaunchKernelGGL((bwd_dq_generic_kernel<T, D>), gq, dim3(kGenRows), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
-                       (const T*)a.dout, (const float*)a.workspace, a.dq,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.o,
+                       (const float*)a.lse, (const T*)a.dout, (float*)a.workspace, a.dq,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_preprocess_t(const AttnArgs& a, bool clear_dq, bool clear_dkdv, hipStream_t st) {
-    const long rows = (long)a.B * a.Hq * a.N;
-    constexpr int RPB = 256 / (D / 4);
-    long blocks = (rows + RPB - 1) / RPB;
-    if (blocks > 4096) blocks = 4096;
-    if (blocks < 1) blocks = 1;
-    const long nq = rows * D;
-    const long nkv = (long)a.B * a.Hkv * a.N * D;
-    hipLaunchKernelGGL((bwd_preprocess_kernel<T, D>), dim3((unsigned)blocks), dim3(256), 0, st,
-                       (const float*)a.o, (const T*)a.dout, (float*)a.workspace, rows,
-                       clear_dq ? a.dq : nullptr, nq,
-                       clear_dkdv ? a.dk : nullptr, clear_dkdv ? a.dv : nullptr, nkv);
+static hipError_t launch_bwd_generic_dkdv_t(const AttnArgs& a, hipStream_t st) {
+    dim3 gkv((a.N + kGenRows - 1) / kGenRows, a.B * a.Hkv);
+    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D>), gkv, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
+                       (const T*)a.dout, (const float*)a.workspace, a.dk, a.dv,
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale);
     return hipGetLastError();
 }
 
@@ -316,24 +260,24 @@ static hipError_t launch_preprocess_t(const AttnArgs& a, bool clear_dq, bool cle
 
 template <int D> static hipError_t fwd_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<float, D>(a, s); }
 template <int D> static hipError_t fwd_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<bf16_t, D>(a, s); }
-template <int D> static hipError_t bwd_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_t<float, D>(a, s); }
-template <int D> static hipError_t bwd_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_t<bf16_t, D>(a, s); }
-template <int D> static hipError_t pre_f32(const AttnArgs& a, bool cq, bool ckv, hipStream_t s) { return launch_preprocess_t<float, D>(a, cq, ckv, s); }
-template <int D> static hipError_t pre_bf16(const AttnArgs& a, bool cq, bool ckv, hipStream_t s) { return launch_preprocess_t<bf16_t, D>(a, cq, ckv, s); }
+template <int D> static hipError_t dq_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dq_t<float, D>(a, s); }
+template <int D> static hipError_t dq_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dq_t<bf16_t, D>(a, s); }
+template <int D> static hipError_t kv_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dkdv_t<float, D>(a, s); }
+template <int D> static hipError_t kv_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dkdv_t<bf16_t, D>(a, s); }
 
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st) {
     if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, fwd_gen_f32, a, st) }
     TCA_DISPATCH_D(a.d, fwd_gen_bf16, a, st)
 }
 
-hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t st) {
-    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, bwd_gen_f32, a, st) }
-    TCA_DISPATCH_D(a.d, bwd_gen_bf16, a, st)
+hipError_t launch_bwd_generic_dq(const AttnArgs& a, hipStream_t st) {
+    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, dq_gen_f32, a, st) }
+    TCA_DISPATCH_D(a.d, dq_gen_bf16, a, st)
 }
 
-hipError_t launch_bwd_preprocess(const AttnArgs& a, bool clear_dq, bool clear_dkdv, hipStream_t st) {
-    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, pre_f32, a, clear_dq, clear_dkdv, st) }
-    TCA_DISPATCH_D(a.d, pre_bf16, a, clear_dq, clear_dkdv, st)
+hipError_t launch_bwd_generic_dkdv(const AttnArgs& a, hipStream_t st) {
+    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, kv_gen_f32, a, st) }
+    TCA_DISPATCH_D(a.d, kv_gen_bf16, a, st)
 }
 
 }  // namespace tca

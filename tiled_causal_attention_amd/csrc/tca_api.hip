@@ -82,13 +82,12 @@ AttnArgs make_args(attn_dtype dtype, const void* q, const void* k, const void* v
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
-attn_status run_preprocess(const AttnArgs& a, hipStream_t st) {
-    const bool mfma = tca::mfma_path(a);
-    return from_hip(tca::launch_bwd_preprocess(a, mfma, mfma && tca::bwd_mfma_atomic_dkdv(a), st));
+attn_status run_dq(const AttnArgs& a, hipStream_t st) {
+    return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma_dq(a, st) : tca::launch_bwd_generic_dq(a, st));
 }
 
-attn_status run_main(const AttnArgs& a, hipStream_t st) {
-    return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma(a, st) : tca::launch_bwd_generic(a, st));
+attn_status run_dkdv(const AttnArgs& a, hipStream_t st) {
+    return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma_dkdv(a, st) : tca::launch_bwd_generic_dkdv(a, st));
 }
 
 }  // namespace
@@ -133,7 +132,7 @@ size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N,
     return bwd_ws_bytes(B, Hq, N);
 }
 
-attn_status attn_bwd_preprocess(attn_dtype dtype, const void* q, const void* k, const void* v,
+attn_status attn_bwd_dq(attn_dtype dtype, const void* q, const void* k, const void* v,
                                 const float* o, const float* lse, const void* dO, float* dq,
                                 float* dk, float* dv, void* workspace, size_t workspace_bytes,
                                 int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -144,10 +143,10 @@ attn_status attn_bwd_preprocess(attn_dtype dtype, const void* q, const void* k, 
     if (s != ATTN_OK || noop) return s;
     const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
-    return run_preprocess(a, (hipStream_t)stream);
+    return run_dq(a, (hipStream_t)stream);
 }
 
-attn_status attn_bwd_main(attn_dtype dtype, const void* q, const void* k, const void* v,
+attn_status attn_bwd_dkdv(attn_dtype dtype, const void* q, const void* k, const void* v,
                           const float* o, const float* lse, const void* dO, float* dq, float* dk,
                           float* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                           int N, int d, int causal, float scale, void* stream) {
@@ -157,7 +156,7 @@ attn_status attn_bwd_main(attn_dtype dtype, const void* q, const void* k, const 
     if (s != ATTN_OK || noop) return s;
     const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
-    return run_main(a, (hipStream_t)stream);
+    return run_dkdv(a, (hipStream_t)stream);
 }
 
 attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
@@ -171,9 +170,9 @@ attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void*
     const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
     hipStream_t st = (hipStream_t)stream;
-    s = run_preprocess(a, st);
+    s = run_dq(a, st);
     if (s != ATTN_OK) return s;
-    return run_main(a, st);
+    return run_dkdv(a, st);
 }
 
 }  // extern "C"

@@ -20,7 +20,10 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // one 16-byte chunk
 typedef uint16_t bf16_t;   // raw bfloat16 bits in memory
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -53,6 +56,53 @@ __device__ __forceinline__ f16x8 to_f16x8(float a0, float a1, float a2, float a3
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Eight bfloat16 (one 16-byte chunk) -> eight fp16, round to nearest even
+// (exact for |x| in [2^-14, 65504]).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+    u32x4 r;
+    r.x = pack_f16(bf16_lo(w.x), bf16_hi(w.x));
+    r.y = pack_f16(bf16_lo(w.y), bf16_hi(w.y));
+    r.z = pack_f16(bf16_lo(w.z), bf16_hi(w.z));
+    r.w = pack_f16(bf16_lo(w.w), bf16_hi(w.w));
+    return r;
+}
+
+// Sum of a packed fp16 pair added to acc in fp32 (v_dot2c_f32_f16 with (1, 1)).
+__device__ __forceinline__ float add_f16_pair(uint32_t pair, float acc) {
+    const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
+}
+
+// Matrix-core operand that contracts over the ROWS of a row-major 16-bit LDS
+// tile, read with the transposing LDS load (ds_read_b64_tr_b16): lane (h, r)
+// receives tile[row0 + 8h + t][col0 + r], t = 0..7 -- the A operand of a
+// product whose m index is the tile column, or the B operand whose n index is.
+// The transposing load hands lane i of each 16-lane group element (i mod 4) of
+// the 8-byte chunks addressed by lanes 4k + i/4 (k = 0..3) of that group; the
+// addresses below put row row0 + 8h + (r%16)/4 (+4 for the second load),
+// columns col0 + 16(r/16) + 4(r%4) .. +3 behind each lane.
+__device__ __forceinline__ f16x8 lds_tr_operand(const _Float16* tile, int stride, int row0, int col0,
+                                                int h, int r) {
+    const _Float16* p = tile + (row0 + 8 * h + ((r & 15) >> 2)) * stride + col0 + 16 * (r >> 4) + 4 * (r & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 4 * stride));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// Reductions across the two half-waves with v_permlane32_swap: swapping a
+// register with itself leaves, in every lane, the pair {own value, value of
+// lane l ^ 32}, so max/sum over the pair combine the two halves.
+__device__ __forceinline__ float max_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Value held by lane (lane ^ 32): the other half of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -62,6 +112,36 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32,
 // e of lane (h, r) holds source row 16(e/8) + 8h + (e%8).
 __device__ __forceinline__ int perm32(int m) {
     return (m & ~0xC) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// Workgroup id -> (query tile, batch, KV head, head within the group) for the
+// query-tile-parallel kernels. Longest (last) query tiles come first. When the
+// number of (batch, KV head) units is a multiple of 8, all workgroups of a unit
+// share w mod 8, i.e. land on one XCD (workgroups are dealt to the 8 XCDs
+// round-robin), so the unit's K/V tiles stay in that XCD's L2.
+struct TileMap {
+    int qt, b, hkv, g;
+};
+__device__ __forceinline__ TileMap map_workgroup(int w, int nqt, int units, int Hkv, int group) {
+    TileMap m;
+    int t, u;
+    if ((units & 7) == 0) {
+        const int x = w & 7, i = w >> 3, upx = units >> 3;
+        m.g = i % group;
+        const int rest = i / group;
+        u = (rest % upx) * 8 + x;
+        t = rest / upx;
+    } else {
+        const int per = units * group;
+        t = w / per;
+        const int rem = w % per;
+        u = rem / group;
+        m.g = rem % group;
+    }
+    m.qt = nqt - 1 - t;
+    m.b = u / Hkv;
+    m.hkv = u % Hkv;
+    return m;
 }
 
 template <typename T>

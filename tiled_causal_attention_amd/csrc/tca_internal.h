@@ -27,18 +27,17 @@ struct AttnArgs {
     float scale;
 };
 
-// float32-arithmetic path (any supported d, either dtype)
+// float32-arithmetic path (any supported d, either dtype). The backward's
+// first phase writes D = rowsum(dO o O) into the workspace and dq; the second
+// reads D and writes dk, dv.
 hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st);
-hipError_t launch_bwd_generic(const AttnArgs& a, hipStream_t st);
-// backward preprocess shared by both paths: delta into the workspace, and
-// clearing of dq (clear_dq) and dk/dv (clear_dkdv)
-hipError_t launch_bwd_preprocess(const AttnArgs& a, bool clear_dq, bool clear_dkdv, hipStream_t st);
+hipError_t launch_bwd_generic_dq(const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd_generic_dkdv(const AttnArgs& a, hipStream_t st);
 
-// matrix-core path: bf16 inputs, d in {64, 128}
+// matrix-core path: bf16 inputs, d in {64, 128}; same two backward phases
 bool mfma_path(const AttnArgs& a);
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st);
-hipError_t launch_bwd_mfma(const AttnArgs& a, hipStream_t st);
-// which outputs the matrix-core backward accumulates atomically
-bool bwd_mfma_atomic_dkdv(const AttnArgs& a);
+hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st);
+hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st);
 
 }  // namespace tca
