@@ -28,9 +28,12 @@
 
 namespace tca {
 
+// dQ pass layout: a workgroup covers 64 query rows with 4 waves, 2 row blocks
+// of 32 rows x 2 key halves (wave (rb, kh) takes keys 32kh .. 32kh+31 of each
+// K/V tile); the two key halves' partial dQ are summed through LDS at the end.
 namespace bwdq {
 constexpr int NW = 4;            // waves per workgroup
-constexpr int BQ = 32 * NW;      // query rows per workgroup
+constexpr int BQ = 64;           // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile
 constexpr int PAD = 8;
 }  // namespace bwdq
@@ -66,13 +69,13 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, (D == 64) ? 2 : 1)
+__global__ void __launch_bounds__(256, (D == 64) ? 3 : 1)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
               const float* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ dq,
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
-    constexpr int DC = D / 16, DB = D / 32, NB = BC / 32, LD = D + PAD;
+    constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
     constexpr int CPR = D / 8, KCH = BC * CPR / 256;
     __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BC][LD];
     __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BC][LD];
@@ -81,8 +84,10 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const TileMap tm = map_workgroup(blockIdx.x, nqt, units, Hkv, group);
     const int hq = tm.hkv * group + tm.g;
     const size_t bh = (size_t)tm.b * Hq + hq;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, r = lane & 31;
-    const int q0w = tm.qt * BQ + 32 * w;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
+    const int rb = w >> 1, khalf = w & 1;   // row block, key half
+    const int q0w = tm.qt * BQ + 32 * rb;
     const int qi = q0w + r;
     const int qc = min(qi, N - 1);
     const bool qok = qi < N;
@@ -117,7 +122,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             part = fmaf(bf16_hi(dv.w), o1[3], part);
         }
         Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
-        if (qok && h == 0) delta[bh * N + qi] = Di;
+        if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = Di;
     }
     const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
 
@@ -138,50 +143,40 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
-        if (!causal || k0 <= q0w + 31) {
-            // ---- S^T = K Q^T and dP^T = V dO^T (rows: keys, permuted; columns: queries)
-            f32x16 s[NB], dp[NB];
+        const int kw0 = k0 + 32 * khalf;   // first key of this wave's half
+        if (!causal || kw0 <= q0w + 31) {
+            // ---- S^T = K Q^T and dP^T = V dO^T (rows: the wave's keys, permuted; columns: queries)
+            f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                s[nb] = f32x16{};
-                dp[nb] = f32x16{};
+            for (int c = 0; c < DC; ++c) {
+                const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[buf][32 * khalf + krow_a][16 * c + 8 * h]);
+                s = mfma_f16(ak, qb[c], s);
+                dp = mfma_bf16(av, db[c], dp);
             }
+            // ---- P, dS (accumulator e: key kw0 + 16(e/8) + 8h + e%8)
+            const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > q0w);
 #pragma unroll
-            for (int c = 0; c < DC; ++c)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * nb + krow_a][16 * c + 8 * h]);
-                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[buf][32 * nb + krow_a][16 * c + 8 * h]);
-                    s[nb] = mfma_f16(ak, qb[c], s[nb]);
-                    dp[nb] = mfma_bf16(av, db[c], dp[nb]);
+            for (int e = 0; e < 16; ++e) {
+                float p = fast_exp2(fmaf(s[e], sl2, -Li));
+                if (need_mask) {   // wave-uniform; the select itself is branch-free
+                    const int key = kw0 + 16 * (e >> 3) + 8 * h + (e & 7);
+                    const bool keep = (key < N) & (!causal | (key <= qi));
+                    p = keep ? p : 0.f;
                 }
-            // ---- P, dS (accumulator e of block nb: key k0 + 32nb + 16(e/8) + 8h + e%8)
-            const bool need_mask = (k0 + BC > N) || (causal && k0 + BC - 1 > q0w);
+                s[e] = p * (dp[e] - Di);   // dS
+            }
+            // ---- dQ^T += K^T dS^T  (A: the wave's K rows read transposed; B: dS from registers)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int c2 = 0; c2 < 2; ++c2) {
+                const f16x8 dsb = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                           s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float p = fast_exp2(fmaf(s[nb][e], sl2, -Li));
-                    if (need_mask) {
-                        const int key = k0 + 32 * nb + 16 * (e >> 3) + 8 * h + (e & 7);
-                        if (key >= N || (causal && key > qi)) p = 0.f;
-                    }
-                    s[nb][e] = p * (dp[nb][e] - Di);   // dS
+                for (int x = 0; x < DB; ++x) {
+                    const f16x8 a = lds_tr_operand(&Ks[buf][0][0], LD, 32 * khalf + 16 * c2, 32 * x, h, r);
+                    dqa[x] = mfma_f16(a, dsb, dqa[x]);
                 }
-            // ---- dQ^T += K^T dS^T  (A: K tile read transposed; B: dS from registers)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    const f16x8 dsb = to_f16x8(s[nb][8 * c2 + 0], s[nb][8 * c2 + 1], s[nb][8 * c2 + 2],
-                                               s[nb][8 * c2 + 3], s[nb][8 * c2 + 4], s[nb][8 * c2 + 5],
-                                               s[nb][8 * c2 + 6], s[nb][8 * c2 + 7]);
-#pragma unroll
-                    for (int x = 0; x < DB; ++x) {
-                        const f16x8 a = lds_tr_operand(&Ks[buf][0][0], LD, 32 * nb + 16 * c2, 32 * x, h, r);
-                        dqa[x] = mfma_f16(a, dsb, dqa[x]);
-                    }
-                }
+            }
         }
         if (j + 1 < ntile) {
             bwd_store_kv<D, KCH>(kreg, vreg, Ks[buf ^ 1], Vs[buf ^ 1], tid);
@@ -190,15 +185,28 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         __syncthreads();
     }
 
-    // ---- store dQ: accumulator e of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of query qi
-    if (qok) {
+    // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
+    // after the last barrier) and store. Accumulator e of dim block x holds dim
+    // 32x + 8(e/4) + 4h + e%4 of query qi.
+    float* xo = reinterpret_cast<float*>(&Ks[0][0][0]) + rb * (32 * D);   // [32 rows][D]
+    if (khalf == 1) {
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h) =
+                    f32x4{dqa[x][4 * a4 + 0], dqa[x][4 * a4 + 1], dqa[x][4 * a4 + 2], dqa[x][4 * a4 + 3]};
+    }
+    __syncthreads();
+    if (khalf == 0 && qok) {
         float* row = dq + (bh * N + qi) * D;
 #pragma unroll
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const f32x4 val = {dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
-                                   dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h);
+                const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
+                                   (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
                 *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
             }
     }
@@ -244,13 +252,27 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
     __shared__ __attribute__((aligned(16))) _Float16 dOs[2][BQ][LD];
     __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
     __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
-    __shared__ __attribute__((aligned(16))) float red[2][BC][D];   // dK, dV partial sums
+    __shared__ __attribute__((aligned(16))) float red[NQW / 2][2][BC][D];   // dK, dV partial sums
 
     const int group = Hq / Hkv;
-    const int unit = blockIdx.x / wg_per_unit;
-    const int slot = blockIdx.x % wg_per_unit;
+    // all workgroups of one (batch, KV head) unit on one XCD (w mod 8), so the
+    // unit's Q/dO stream is fetched into that XCD's L2 once
+    int unit, slot;
+    {
+        const int w8 = blockIdx.x;
+        const int units = gridDim.x / wg_per_unit;
+        if ((units & 7) == 0) {
+            const int i = w8 >> 3;
+            unit = (i / wg_per_unit) * 8 + (w8 & 7);
+            slot = i % wg_per_unit;
+        } else {
+            unit = w8 / wg_per_unit;
+            slot = w8 % wg_per_unit;
+        }
+    }
     const int b = unit / Hkv, hkv = unit % Hkv;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, r = lane & 31;
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
     const int kh_ = w & 1, qw = w >> 1;       // key half, query sub-block
     const size_t kvoff = ((size_t)b * Hkv + hkv) * N * D;
     const float sl2 = scale * kLog2e;
@@ -260,43 +282,47 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
     const int tile_a = slot;
     const int tile_b = (causal && ntiles - 1 - slot != slot) ? ntiles - 1 - slot : -1;
 
-    // items: (tile index t in {0,1}, head g, query tile i); for each tile, the
-    // query tiles at or below the diagonal, for every head of the group
-    auto first_qt = [&](int tile) { return causal ? (tile * BC) / BQ : 0; };
-    const int na = group * (nqt - first_qt(tile_a));
-    const int nbitems = (tile_b >= 0) ? group * (nqt - first_qt(tile_b)) : 0;
-    const int nitems = na + nbitems;
+    // items: for each of the workgroup's K/V tiles, every head g of the group
+    // and every query tile qt at or below the diagonal (qt from first_qt(tile)).
+    // Two cursors walk the sequence: `cur` (computed now) and `ld` (prefetched,
+    // two items ahead); advancing is a few scalar compares, no division.
+    struct Cursor {
+        int t, g, qt;   // t: 0 -> tile_a, 1 -> tile_b, 2 -> done
+    };
+    const int fa = causal ? (tile_a * BC) / BQ : 0;
+    const int fb = (tile_b >= 0 && causal) ? (tile_b * BC) / BQ : 0;
+    const int nitems = group * (nqt - fa) + ((tile_b >= 0) ? group * (nqt - fb) : 0);
+    auto advance = [&](Cursor& c) {
+        if (++c.qt < nqt) return;
+        if (++c.g < group) {
+            c.qt = c.t ? fb : fa;
+            return;
+        }
+        c.g = 0;
+        c.t += 1;
+        c.qt = fb;
+        if (c.t == 1 && tile_b < 0) c.t = 2;
+    };
+    auto tile_of = [&](const Cursor& c) { return c.t == 0 ? tile_a : tile_b; };
 
     u32x4 qreg[QCH], dreg[QCH];
     float lreg = 0.f, dlreg = 0.f;
-    // decode item -> (tile, head, query tile)
-    auto item = [&](int it, int& tile, int& g, int& qt) {
-        const int t = (it < na) ? 0 : 1;
-        const int rel = t ? it - na : it;
-        tile = t ? tile_b : tile_a;
-        const int f = first_qt(tile), per = nqt - f;
-        g = rel / per;
-        qt = f + rel % per;
-    };
-    auto load_item = [&](int it) {
-        int tile, g, qt;
-        item(it, tile, g, qt);
-        const size_t bh = (size_t)b * Hq + hkv * group + g;
+    auto load_item = [&](const Cursor& c) {
+        const size_t bh = (size_t)b * Hq + hkv * group + c.g;
         const bf16_t* qh = q + bh * N * D;
         const bf16_t* dh = dout + bh * N * D;
 #pragma unroll
         for (int u = 0; u < QCH; ++u) {
             const int cid = tid + NT * u;
-            const int row = min(qt * BQ + cid / CPR, N - 1);
+            const int row = min(c.qt * BQ + cid / CPR, N - 1);
             const size_t off = (size_t)row * D + (cid % CPR) * 8;
             qreg[u] = *reinterpret_cast<const u32x4*>(qh + off);
             dreg[u] = *reinterpret_cast<const u32x4*>(dh + off);
         }
         if (tid < BQ) {
-            const int row = qt * BQ + tid;
-            const int rc = min(row, N - 1);
-            lreg = lse[bh * N + rc] * kLog2e;
-            dlreg = delta[bh * N + rc];
+            const int rc = min(c.qt * BQ + tid, N - 1);
+            lreg = lse[bh * N + rc];       // scaled to log2 units when staged, so
+            dlreg = delta[bh * N + rc];    // the prefetch is not waited on here
         }
     };
     auto store_item = [&](int buf) {
@@ -308,7 +334,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
             *reinterpret_cast<u32x4*>(&dOs[buf][row][col]) = bf16x8_to_f16x8(dreg[u]);
         }
         if (tid < BQ) {
-            Ls[buf][tid] = lreg;
+            Ls[buf][tid] = lreg * kLog2e;
             Ds[buf][tid] = dlreg;
         }
     };
@@ -316,18 +342,22 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
     f16x8 kb[DC], vb[DC];
     f32x16 dka[DB], dva[DB];
     int cur_tile = -1;
+    Cursor cur = {0, 0, fa}, ld = cur;
 
     if (nitems > 0) {
-        load_item(0);
+        load_item(ld);
         store_item(0);
-        if (nitems > 1) load_item(1);
+        advance(ld);
+        if (nitems > 1) {
+            load_item(ld);
+            advance(ld);
+        }
     }
     __syncthreads();
 
     for (int it = 0; it < nitems; ++it) {
         const int buf = it & 1;
-        int tile, g, qt;
-        item(it, tile, g, qt);
+        const int tile = tile_of(cur), qt = cur.qt;
         const int kw0 = tile * BC + 32 * kh_;   // first key of this wave
         const int kw = kw0 + r;                 // this lane's key
         if (tile != cur_tile) {
@@ -348,6 +378,21 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
         }
         const int q0 = qt * BQ + 32 * qw;        // first query row of this wave's block
         const bool live = !causal || q0 + 31 >= kw0;
+        // Staging the next item (fp16 conversion + LDS stores) is VALU work;
+        // the two waves sharing a SIMD (w and w+4) run it at opposite ends of
+        // the iteration, so one wave's VALU phase meets the other's matrix
+        // phase instead of both doing the same thing in lock step.
+        auto stage = [&]() {
+            if (it + 1 < nitems) {
+                store_item(buf ^ 1);
+                if (it + 2 < nitems) {
+                    load_item(ld);
+                    advance(ld);
+                }
+            }
+        };
+        const bool stage_first = w >= 4;
+        if (stage_first) stage();
         if (live) {
             // ---- S = Q K^T, dP = dO V^T (accumulator e: query q0 + 16(e/8) + 8h + e%8, key kw)
             f32x16 s = f32x16{}, dp = f32x16{};
@@ -373,9 +418,10 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
                 for (int t = 0; t < 8; ++t) {
                     const int e = 8 * c2 + t;
                     float p = fast_exp2(fmaf(s[e], sl2, -lv[t]));
-                    if (need_mask) {
+                    if (need_mask) {   // wave-uniform; the select itself is branch-free
                         const int qrow = qt * BQ + qq + t;
-                        if (qrow >= N || kw >= N || (causal && kw > qrow)) p = 0.f;
+                        const bool keep = (qrow < N) & (kw < N) & (!causal | (kw <= qrow));
+                        p = keep ? p : 0.f;
                     }
                     s[e] = p;
                     dp[e] = p * (dp[e] - dl[t]);
@@ -397,53 +443,65 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
                 }
             }
         }
-        if (it + 1 < nitems) {
-            store_item(buf ^ 1);
-            if (it + 2 < nitems) load_item(it + 2);
-        }
+        if (!stage_first) stage();
+        advance(cur);
         // ---- end of a K/V tile: fixed-order reduction of the query sub-block partials
-        int ntile_next = -1;
-        if (it + 1 < nitems) {
-            int g2, qt2;
-            item(it + 1, ntile_next, g2, qt2);
-        }
-        if (ntile_next != tile) {
+        if (it + 1 == nitems || tile_of(cur) != tile) {
+            // Tree over the NQW query sub-blocks (fixed order -> deterministic):
+            // each round the upper half of the remaining sub-blocks writes its
+            // partials to LDS and the lower half adds them in registers; sub-block
+            // 0 ends with the full sums and stores dK (scaled) and dV rows.
             // accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r
 #pragma unroll 1
-            for (int step = 0; step < NQW; ++step) {
-                if (qw == step) {
+            for (int half = NQW / 2; half >= 1; half >>= 1) {
+                if (qw >= half && qw < 2 * half) {
+                    float* dst = &red[qw - half][0][0][0];
 #pragma unroll
                     for (int x = 0; x < DB; ++x)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
                             const int key = 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
-                            float* pk = &red[0][key][32 * x + r];
-                            float* pv = &red[1][key][32 * x + r];
-                            if (step == 0) {
-                                *pk = dka[x][e];
-                                *pv = dva[x][e];
-                            } else {
-                                *pk += dka[x][e];
-                                *pv += dva[x][e];
+                            dst[(0 * BC + key) * D + 32 * x + r] = dka[x][e];
+                            dst[(1 * BC + key) * D + 32 * x + r] = dva[x][e];
+                        }
+                }
+                __syncthreads();
+                if (qw < half) {
+                    const float* src = &red[qw][0][0][0];
+#pragma unroll
+                    for (int x = 0; x < DB; ++x)
+#pragma unroll
+                        for (int e0 = 0; e0 < 16; e0 += 8) {
+                            // 16 loads in flight, then 16 adds (bounded register use)
+                            float tk[8], tv[8];
+#pragma unroll
+                            for (int e = e0; e < e0 + 8; ++e) {
+                                const int key = 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
+                                tk[e - e0] = src[(0 * BC + key) * D + 32 * x + r];
+                                tv[e - e0] = src[(1 * BC + key) * D + 32 * x + r];
                             }
+#pragma unroll
+                            for (int e = e0; e < e0 + 8; ++e) {
+                                dka[x][e] += tk[e - e0];
+                                dva[x][e] += tv[e - e0];
+                            }
+                            __builtin_amdgcn_sched_barrier(0);
                         }
                 }
                 __syncthreads();
             }
-            // write the tile's dK (scaled) and dV rows
-            const int key0 = tile * BC;
-            constexpr int F4 = BC * D / 4;   // float4 per tensor
+            if (qw == 0) {
 #pragma unroll
-            for (int u = 0; u < F4 / NT; ++u) {
-                const int idx = tid + NT * u;
-                const int row = idx / (D / 4), col = (idx % (D / 4)) * 4;
-                if (key0 + row < N) {
-                    const f32x4 kv = *reinterpret_cast<const f32x4*>(&red[0][row][col]);
-                    const f32x4 vv = *reinterpret_cast<const f32x4*>(&red[1][row][col]);
-                    const size_t off = kvoff + (size_t)(key0 + row) * D + col;
-                    *reinterpret_cast<f32x4*>(dk + off) = kv * scale;
-                    *reinterpret_cast<f32x4*>(dv + off) = vv;
-                }
+                for (int x = 0; x < DB; ++x)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key < N) {
+                            const size_t off = kvoff + (size_t)key * D + 32 * x + r;
+                            dk[off] = dka[x][e] * scale;
+                            dv[off] = dva[x][e];
+                        }
+                    }
             }
         }
         __syncthreads();

@@ -4,10 +4,17 @@
 // workgroup per query tile; for each K/V tile: stage it on chip, Q*K^T, online
 // softmax, accumulate the output), re-shaped for CDNA4:
 //
-//  * A workgroup is 4 waves x 32 query rows (BR = 128). Each wave keeps its Q
-//    rows in registers as the B operand of S^T = K * Q^T, so the score
-//    accumulator holds one query per lane (lane = 32h + r -> query r): the row
-//    max and row sum are in-lane reductions plus one half-wave exchange.
+//  * A workgroup covers 64 query rows with 4 waves: 2 row blocks of 32 rows x
+//    2 key halves. Wave (rb, kh) takes keys 32kh .. 32kh+31 of every K/V tile
+//    for its 32 rows and runs its own online softmax over them; the two key
+//    halves of a row block are merged once, through LDS, at the end. Splitting
+//    the keys halves the serial work each wave does per tile, which is what
+//    bounds short-sequence shapes (the last query tile's walk over all K/V
+//    tiles), and doubles the waves available to hide latency.
+//  * Each wave keeps its Q rows in registers as the B operand of
+//    S^T = K * Q^T, so the score accumulator holds one query per lane
+//    (lane = 32h + r -> query r): the row max and row sum are in-lane
+//    reductions plus one half-wave exchange.
 //  * K/V tiles (BC = 64 keys) are double-buffered in LDS and prefetched one
 //    tile ahead into registers: the global loads for tile j+2 are issued while
 //    tile j is computed and land in LDS after it, so their latency is hidden
@@ -39,9 +46,9 @@
 namespace tca {
 
 namespace fwd {
-constexpr int NW = 4;            // waves per workgroup
-constexpr int BR = 32 * NW;      // query rows per workgroup
-constexpr int BC = 64;           // keys per K/V tile
+constexpr int NW = 4;            // waves per workgroup: 2 row blocks x 2 key halves
+constexpr int BR = 64;           // query rows per workgroup
+constexpr int BC = 64;           // keys per K/V tile (32 per key half)
 constexpr int PAD = 8;           // 16-bit elements of row padding (16 bytes)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 }  // namespace fwd
@@ -85,7 +92,6 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     using namespace fwd;
     constexpr int DC = D / 16;          // 16-deep chunks of the head dimension
     constexpr int DB = D / 32;          // 32-wide blocks of the head dimension
-    constexpr int NB = BC / 32;         // 32-key blocks per tile
     constexpr int LD = D + PAD;         // LDS row stride (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
     constexpr int KCH = BC * CPR / 256; // chunks per thread per tensor per tile
@@ -96,8 +102,10 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const TileMap tm = map_workgroup(blockIdx.x, nqt, units, Hkv, group);
     const int hq = tm.hkv * group + tm.g;
     const size_t bh = (size_t)tm.b * Hq + hq;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, h = lane >> 5, r = lane & 31;
-    const int q0w = tm.qt * BR + 32 * w;   // first query row of this wave
+    const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
+    const int rb = w >> 1, khalf = w & 1;  // row block, key half
+    const int q0w = tm.qt * BR + 32 * rb;  // first query row of this wave
     const int qi = q0w + r;                // this lane's query row
     const bf16_t* qh = q + bh * N * D;
     const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
@@ -135,35 +143,30 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
-        const bool active = !causal || k0 <= q0w + 31;
+        const int kw0 = k0 + 32 * khalf;        // first key of this wave's half
+        const bool active = !causal || kw0 <= q0w + 31;
         if (active) {
-            // ---- S^T = K * Q^T  (rows: keys, permuted; columns: this wave's queries)
-            f32x16 s[NB];
+            // ---- S^T = K * Q^T  (rows: this wave's 32 keys, permuted; columns: its queries)
+            f32x16 s = f32x16{};
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < DC; ++c)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][32 * nb + krow_a][16 * c + 8 * h]);
-                    s[nb] = mfma_bf16(a, qb[c], s[nb]);
-                }
+            for (int c = 0; c < DC; ++c) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
+                s = mfma_bf16(a, qb[c], s);
+            }
             // ---- mask: only tiles crossing the diagonal or the end of the sequence
-            if ((k0 + BC > N) || (causal && k0 + BC - 1 > q0w)) {
+            // (accumulator e holds key kw0 + 16(e/8) + 8h + e%8)
+            if ((kw0 + 32 > N) || (causal && kw0 + 31 > q0w)) {
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int key = k0 + 32 * nb + 16 * (e >> 3) + 8 * h + (e & 7);
-                        if (key >= N || (causal && key > qi)) s[nb][e] = -INFINITY;
-                    }
+                for (int e = 0; e < 16; ++e) {
+                    const int key = kw0 + 16 * (e >> 3) + 8 * h + (e & 7);
+                    const bool keep = (key < N) & (!causal | (key <= qi));
+                    s[e] = keep ? s[e] : -INFINITY;
+                }
             }
             // ---- online softmax with lazy rescaling (log2 domain)
-            float mx = s[0][0];
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[nb][e]);
+            const float mx = fmaxf(fmaxf(fmaxf(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5])),
+                                         fmaxf(max3f(s[6], s[7], s[8]), max3f(s[9], s[10], s[11]))),
+                                   max3f(s[12], s[13], fmaxf(s[14], s[15])));
             const float mt = max_halves(mx) * sl2;
             if (__any(mt > m_s + kTau)) {
                 const float m_new = fmaxf(m_s, mt);
@@ -176,27 +179,25 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 m_s = m_new;
             }
             const float mb = (m_s == -INFINITY) ? 0.f : m_s;
-            // ---- P (fp16) and O^T += V^T * P^T
+            // ---- P (fp16) and O^T += V^T * P^T over the wave's 32 keys
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
+            for (int c2 = 0; c2 < 2; ++c2) {
+                float p[8];
 #pragma unroll
-                for (int c2 = 0; c2 < 2; ++c2) {
-                    float p[8];
+                for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * c2 + t], sl2, -mb));
+                uint32_t pk[4];
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[nb][8 * c2 + t], sl2, -mb));
-                    uint32_t pk[4];
-#pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        pk[t] = pack_f16(p[2 * t], p[2 * t + 1]);
-                        l_run = add_f16_pair(pk[t], l_run);
-                    }
-                    const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-                    for (int x = 0; x < DB; ++x) {
-                        const f16x8 a = lds_tr_operand(&Vs[buf][0][0], LD, 32 * nb + 16 * c2, 32 * x, h, r);
-                        oacc[x] = mfma_f16(a, pb, oacc[x]);
-                    }
+                for (int t = 0; t < 4; ++t) {
+                    pk[t] = pack_f16(p[2 * t], p[2 * t + 1]);
+                    l_run = add_f16_pair(pk[t], l_run);
                 }
+                const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+                for (int x = 0; x < DB; ++x) {
+                    const f16x8 a = lds_tr_operand(&Vs[buf][0][0], LD, 32 * khalf + 16 * c2, 32 * x, h, r);
+                    oacc[x] = mfma_f16(a, pb, oacc[x]);
+                }
+            }
         }
         if (j + 1 < ntile) {
             store_kv_tile<D, KCH>(kreg, vreg, Ks[buf ^ 1], Vs[buf ^ 1], tid);
@@ -205,21 +206,44 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();
     }
 
-    // ---- epilogue: normalise, store O (fp32) and LSE (natural log)
-    // accumulator e of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of query qi
-    const float l_tot = sum_halves(l_run);
-    if (qi < N) {
-        const float inv = 1.f / l_tot;
+    // ---- epilogue: merge the two key halves of each row block through LDS
+    // (the K tile buffers are free after the loop's last barrier), normalise,
+    // store O (fp32) and LSE (natural log). Accumulator e of dim block x holds
+    // dim 32x + 8(e/4) + 4h + e%4 of query qi.
+    float l_tot = sum_halves(l_run);
+    float* xo = reinterpret_cast<float*>(&Ks[0][0][0]) + rb * (32 * D);   // [32 rows][D]
+    float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + 2 * 32 * D + rb * 64;   // m[32], l[32]
+    if (khalf == 1) {
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h) =
+                    f32x4{oacc[x][4 * a4 + 0], oacc[x][4 * a4 + 1], oacc[x][4 * a4 + 2], oacc[x][4 * a4 + 3]};
+        if (h == 0) {
+            xs[r] = m_s;
+            xs[32 + r] = l_tot;
+        }
+    }
+    __syncthreads();
+    if (khalf == 0 && qi < N) {
+        const float m1 = xs[r], l1 = xs[32 + r];
+        const float m = fmaxf(m_s, m1);               // finite: key half 0 always sees key 0
+        const float a0 = fast_exp2(m_s - m), a1 = fast_exp2(m1 - m);
+        const float l = l_tot * a0 + l1 * a1;
+        const float inv = 1.f / l;
+        const float c0 = a0 * inv, c1 = a1 * inv;
         float* orow = o + (bh * N + qi) * D;
 #pragma unroll
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const float4 val = {oacc[x][4 * a4 + 0] * inv, oacc[x][4 * a4 + 1] * inv,
-                                    oacc[x][4 * a4 + 2] * inv, oacc[x][4 * a4 + 3] * inv};
-                *reinterpret_cast<float4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h);
+                const f32x4 val = {oacc[x][4 * a4 + 0] * c0 + o1[0] * c1, oacc[x][4 * a4 + 1] * c0 + o1[1] * c1,
+                                   oacc[x][4 * a4 + 2] * c0 + o1[2] * c1, oacc[x][4 * a4 + 3] * c0 + o1[3] * c1};
+                *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
             }
-        if (h == 0) lse[bh * N + qi] = (m_s + __log2f(l_tot)) * kLn2;
+        if (h == 0) lse[bh * N + qi] = (m + __log2f(l)) * kLn2;
     }
 }
 

@@ -55,6 +55,7 @@ __device__ __forceinline__ f16x8 to_f16x8(float a0, float a1, float a2, float a3
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // Eight bfloat16 (one 16-byte chunk) -> eight fp16, round to nearest even
 // (exact for |x| in [2^-14, 65504]).
