@@ -53,34 +53,31 @@ constexpr int PAD = 8;           // 16-bit elements of row padding (16 bytes)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 }  // namespace fwd
 
-// Global -> registers: the K and V rows k0 .. k0 + BC - 1 (clamped to N - 1);
-// thread tid owns the 16-byte chunks tid + 256u, so a wave reads whole rows.
+// Global -> registers: the K and V chunks of one tile through buffer
+// resources over the head's N rows; voff is this thread's byte offset of chunk
+// 0 in the tile's first row. Thread tid owns chunks tid + 256u (a wave reads
+// whole rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
-__device__ __forceinline__ void load_kv_tile(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], const bf16_t* kh,
-                                             const bf16_t* vh, int k0, int N, int tid) {
-    constexpr int CPR = D / 8;
+__device__ __forceinline__ void load_kv_tile(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
+                                             __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        const int cid = tid + 256 * u;
-        const int key = min(k0 + cid / CPR, N - 1);
-        const size_t off = (size_t)key * D + (cid % CPR) * 8;
-        kreg[u] = *reinterpret_cast<const u32x4*>(kh + off);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vh + off);
+        kreg[u] = buf_load16(kr, voff + u * 256 * 16);
+        vreg[u] = buf_load16(vr, voff + u * 256 * 16);
     }
 }
 
-// Registers -> LDS: K as bf16 rows, V converted to fp16 rows.
+// Registers -> LDS: K as bf16 rows, V converted to fp16 rows. kdst/vdst point
+// at this thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8))); chunk u
+// sits 256u / (D/8) rows further down.
 template <int D, int KCH>
-__device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH],
-                                              bf16_t (*Ks)[D + fwd::PAD], _Float16 (*Vs)[D + fwd::PAD],
-                                              int tid) {
-    constexpr int CPR = D / 8;
+__device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH], bf16_t* kdst,
+                                              _Float16* vdst) {
+    constexpr int ROWS_PER_U = 256 / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        const int cid = tid + 256 * u;
-        const int row = cid / CPR, col = (cid % CPR) * 8;
-        *reinterpret_cast<u32x4*>(&Ks[row][col]) = kreg[u];
-        *reinterpret_cast<u32x4*>(&Vs[row][col]) = bf16x8_to_f16x8(vreg[u]);
+        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + fwd::PAD)) = kreg[u];
+        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + fwd::PAD)) = bf16x8_to_f16x8(vreg[u]);
     }
 }
 
@@ -108,8 +105,6 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int q0w = tm.qt * BR + 32 * rb;  // first query row of this wave
     const int qi = q0w + r;                // this lane's query row
     const bf16_t* qh = q + bh * N * D;
-    const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
-    const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = scale * kLog2e;      // scores in log2 units
 
     // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]
@@ -128,17 +123,32 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     f32x16 oacc[DB];
 #pragma unroll
     for (int x = 0; x < DB; ++x) oacc[x] = f32x16{};
-    float m_s = -INFINITY;   // running (possibly stale) max, log2 units
+    // Running (possibly stale) max in log2 units. It starts finite and far
+    // below any score, so the first tile's rescale factor is exactly 0 and no
+    // -inf - -inf can arise.
+    float m_s = -0x1p100f;
     float l_run = 0.f;       // sum of this lane's fp16 probabilities (other half added at the end)
 
     const int last_q = min(N, (tm.qt + 1) * BR) - 1;
     const int kend = causal ? last_q + 1 : N;   // keys needed by this workgroup
     const int ntile = (kend + BC - 1) / BC;
     const int krow_a = perm32(r);
+    // masking: accumulator e holds key kw0 + 8h + c_e with c_e = 16(e/8) + e%8;
+    // it is kept iff c_e <= lim_row - kw0 (key < N, and key <= qi if causal)
+    const int lim_row = (causal ? min(qi, N - 1) : N - 1) - 8 * h;
 
-    load_kv_tile<D, KCH>(kreg, vreg, kh, vh, 0, N, tid);
-    store_kv_tile<D, KCH>(kreg, vreg, Ks[0], Vs[0], tid);
-    if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, kh, vh, BC, N, tid);
+    const size_t kvoff = ((size_t)tm.b * Hkv + tm.hkv) * N * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff, (uint32_t)N * D * 2);
+    const uint32_t ld_off = (uint32_t)tid * 16;                     // byte offset of chunk 0 in a tile
+    const int st_row = tid / CPR, st_col = (tid % CPR) * 8;           // LDS slot of chunk 0
+    bf16_t* const kst0 = &Ks[0][st_row][st_col];
+    _Float16* const vst0 = &Vs[0][st_row][st_col];
+    constexpr int KBUF = BC * LD;                                     // elements per LDS buffer
+
+    load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off);
+    store_kv_tile<D, KCH>(kreg, vreg, kst0, vst0);
+    if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
 
     for (int j = 0; j < ntile; ++j) {
@@ -154,22 +164,16 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 s = mfma_bf16(a, qb[c], s);
             }
             // ---- mask: only tiles crossing the diagonal or the end of the sequence
-            // (accumulator e holds key kw0 + 16(e/8) + 8h + e%8)
             if ((kw0 + 32 > N) || (causal && kw0 + 31 > q0w)) {
+                const int lim = lim_row - kw0;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int key = kw0 + 16 * (e >> 3) + 8 * h + (e & 7);
-                    const bool keep = (key < N) & (!causal | (key <= qi));
-                    s[e] = keep ? s[e] : -INFINITY;
-                }
+                for (int e = 0; e < 16; ++e)
+                    s[e] = (16 * (e >> 3) + (e & 7) <= lim) ? s[e] : -INFINITY;
             }
             // ---- online softmax with lazy rescaling (log2 domain)
-            const float mx = fmaxf(fmaxf(fmaxf(max3f(s[0], s[1], s[2]), max3f(s[3], s[4], s[5])),
-                                         fmaxf(max3f(s[6], s[7], s[8]), max3f(s[9], s[10], s[11]))),
-                                   max3f(s[12], s[13], fmaxf(s[14], s[15])));
-            const float mt = max_halves(mx) * sl2;
+            const float mt = max_halves(max16(s)) * sl2;
             if (__any(mt > m_s + kTau)) {
-                const float m_new = fmaxf(m_s, mt);
+                const float m_new = vmax(m_s, mt);
                 const float alpha = fast_exp2(m_s - m_new);
                 l_run *= alpha;
 #pragma unroll
@@ -178,7 +182,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
                 m_s = m_new;
             }
-            const float mb = (m_s == -INFINITY) ? 0.f : m_s;
+            const float mb = m_s;
             // ---- P (fp16) and O^T += V^T * P^T over the wave's 32 keys
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
@@ -200,8 +204,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             }
         }
         if (j + 1 < ntile) {
-            store_kv_tile<D, KCH>(kreg, vreg, Ks[buf ^ 1], Vs[buf ^ 1], tid);
-            if (j + 2 < ntile) load_kv_tile<D, KCH>(kreg, vreg, kh, vh, (j + 2) * BC, N, tid);
+            store_kv_tile<D, KCH>(kreg, vreg, kst0 + (buf ^ 1) * KBUF, vst0 + (buf ^ 1) * KBUF);
+            if (j + 2 < ntile) load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off + (uint32_t)(j + 2) * (BC * D * 2));
         }
         __syncthreads();
     }
@@ -228,7 +232,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     __syncthreads();
     if (khalf == 0 && qi < N) {
         const float m1 = xs[r], l1 = xs[32 + r];
-        const float m = fmaxf(m_s, m1);               // finite: key half 0 always sees key 0
+        const float m = vmax(m_s, m1);                // key half 0 always sees key 0
         const float a0 = fast_exp2(m_s - m), a1 = fast_exp2(m1 - m);
         const float l = l_tot * a0 + l1 * a1;
         const float inv = 1.f / l;

@@ -57,6 +57,28 @@ __device__ __forceinline__ f16x8 to_f16x8(float a0, float a1, float a2, float a3
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
+// IEEE-754-2019 maximum (NaN-propagating). Unlike fmaxf it needs no operand
+// canonicalisation, so a chain of them maps onto v_maximum3_f32 directly.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(vmax(a, b), c); }
+
+// Maximum over the 16 accumulator values of a lane (8 v_maximum3_f32).
+__device__ __forceinline__ float max16(const f32x16& s) {
+    const float a = vmax3(s[0], s[1], s[2]), b = vmax3(s[3], s[4], s[5]), c = vmax3(s[6], s[7], s[8]);
+    const float d = vmax3(s[9], s[10], s[11]), e = vmax3(s[12], s[13], s[14]);
+    return vmax(vmax3(a, b, c), vmax3(d, e, s[15]));
+}
+
+// Buffer resource over `bytes` bytes at `base` (raw buffer, stride 0). Loads
+// through it at byte offsets >= bytes return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One 16-byte chunk at byte offset voff (per lane) through a buffer resource.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+}
+
 // Eight bfloat16 (one 16-byte chunk) -> eight fp16, round to nearest even
 // (exact for |x| in [2^-14, 65504]).
 __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
@@ -97,7 +119,7 @@ __device__ __forceinline__ f16x8 lds_tr_operand(const _Float16* tile, int stride
 // lane l ^ 32}, so max/sum over the pair combine the two halves.
 __device__ __forceinline__ float max_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_halves(float x) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
