@@ -53,7 +53,7 @@
  *
  * Supported shapes: B >= 0, N >= 0 (B*N == 0 is a no-op that returns ATTN_OK
  * and ignores every pointer), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
- * d in {16, 32, 64, 128}, N*d < 2^31, B*Hq*N < 2^31, causal in {0, 1},
+ * d in {16, 32, 64, 128}, (N+64)*d < 2^31, B*Hq*N < 2^31, causal in {0, 1},
  * scale finite.
  */
 #ifndef TCA_H

@@ -99,6 +99,7 @@ def bwd(L, name="attn_bwd", dtype=BF16, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, 
     (dict(scale=float("nan")), EINVAL),
     (dict(scale=float("inf")), EINVAL),
     (dict(N=1 << 25, d=64), EINVAL),           # N*d overflows int32
+    (dict(N=(1 << 25) - 64, d=64), EINVAL),    # the tail tile's rows would pass 2^31 elements
     (dict(B=1 << 20, Hq=4096, Hkv=4096, N=1024, d=16), EINVAL),   # B*Hq*N overflows
     (dict(d=48), EUNSUP),
     (dict(d=256), EUNSUP),

@@ -23,7 +23,7 @@ attn_status check_sizes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d, 
     if (Hq % Hkv != 0) return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
     if (!isfinite(scale)) return ATTN_EINVAL;
-    if ((int64_t)N * d >= ((int64_t)1 << 31)) return ATTN_EINVAL;
+    if ((int64_t)(N + 64) * d >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // row offsets of a head, tail tile included, fit 32-bit byte offsets
     if ((int64_t)B * Hq * N >= ((int64_t)1 << 31)) return ATTN_EINVAL;
     if (!supported_d(d)) return ATTN_EUNSUPPORTED;
     return ATTN_OK;
