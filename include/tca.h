@@ -30,12 +30,16 @@
  *
  * Precision: inputs q, k, v, dO are float32 (ATTN_F32) or bfloat16 (ATTN_BF16).
  * Outputs o, lse, dq, dk, dv are always float32. With ATTN_F32 every step is
- * computed in float32. With ATTN_BF16 and d in {64, 128}, Q*K^T and dO*V^T run
- * as bf16 matrix-core products with float32 accumulation; the products whose
- * operand is a computed probability or score gradient (P*V, P^T*dO, dS^T*Q,
- * dS*K) run as fp16 matrix-core products, the bf16 partner converted to fp16
- * (exact for |x| >= 2^-14; inputs must satisfy |x| < 65504); all accumulation
- * is float32. bf16 inputs with d in {16, 32} are computed in float32.
+ * computed in float32. With ATTN_BF16 and d in {64, 128} every product runs on
+ * the matrix cores with float32 accumulation. Products of two inputs take them
+ * as they are: in the forward Q*K^T is a bf16 product, in the backward dO*V^T
+ * (dQ phase) is bf16 and the recomputed Q*K^T (both phases) and dO*V^T (dK/dV
+ * phase) are fp16 products of the inputs converted to fp16, which is exact for
+ * |x| >= 2^-14 (inputs must satisfy |x| < 65504). The probabilities P and the
+ * score gradient dS are rounded to fp16 (11-bit significand) for the products
+ * that consume them (P*V, P^T*dO, dS*K, dS^T*Q), whose other operand is
+ * converted to fp16 likewise. bf16 inputs with d in {16, 32} are computed in
+ * float32.
  *
  * Memory ownership: the caller owns every buffer. All tensor pointers are
  * device memory (hipMalloc or equivalent), 16-byte aligned, and must stay
@@ -101,7 +105,10 @@ attn_status attn_fwd(attn_dtype dtype,
                      void* stream);
 
 /* Workspace bytes attn_bwd (and its two phases) need: the float32 row
- * statistic D = rowsum(dO o O), B*Hq*N floats, rounded up to 256 bytes. */
+ * statistic D = rowsum(dO o O) (B*Hq*N floats); for bf16 inputs with d in
+ * {64, 128} also lse in base-2 units (B*Hq*N floats) and fp16 copies of q and
+ * dO (B*Hq*N*d halves each), which the dQ phase writes and the dK/dV phase
+ * reads. Each part is rounded up to 256 bytes. */
 size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dO.
@@ -121,7 +128,8 @@ attn_status attn_bwd(attn_dtype dtype,
                      void* stream);
 
 /* First phase of attn_bwd, query-tile parallel: writes D = rowsum(dO o O)
- * (float32, B*Hq*N) into `workspace`, then dq (recomputing P and dP for each
+ * (and, for bf16 inputs with d in {64, 128}, lse in base-2 units and fp16
+ * copies of q and dO) into `workspace`, then dq (recomputing P and dP for each
  * visible K/V tile). dk and dv are not touched. Arguments as for attn_bwd. */
 attn_status attn_bwd_dq(attn_dtype dtype,
                         const void* q, const void* k, const void* v,
@@ -131,8 +139,8 @@ attn_status attn_bwd_dq(attn_dtype dtype,
                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                         void* stream);
 
-/* Second phase of attn_bwd, K/V-tile parallel: dk and dv, reading D from
- * `workspace`. Requires attn_bwd_dq with the same arguments to have been
+/* Second phase of attn_bwd, K/V-tile parallel: dk and dv, reading what
+ * attn_bwd_dq left in `workspace`. Requires attn_bwd_dq with the same arguments to have been
  * enqueued before it on the same stream (or completed). dq is not touched.
  * Arguments as for attn_bwd. */
 attn_status attn_bwd_dkdv(attn_dtype dtype,

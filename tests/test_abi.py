@@ -63,9 +63,14 @@ def test_version_and_status_strings(L):
 
 def test_workspace_sizes(L):
     assert L.attn_fwd_workspace_bytes(BF16, 8, 12, 4, 1024, 64) == 0
+    rows = 8 * 12 * 1024
+    # matrix-core path: D and base-2 lse (float32 per row), fp16 copies of q and dO
     n = L.attn_bwd_workspace_bytes(BF16, 8, 12, 4, 1024, 64)
-    assert n >= 8 * 12 * 1024 * 4 and n % 256 == 0
+    assert n == 2 * rows * 4 + 2 * rows * 64 * 2 and n % 256 == 0
+    # float32 path (and bf16 with small d): D only, rounded up to 256 bytes
     assert L.attn_bwd_workspace_bytes(F32, 1, 2, 1, 3, 16) == 256
+    assert L.attn_bwd_workspace_bytes(BF16, 1, 2, 1, 3, 32) == 256
+    assert L.attn_bwd_workspace_bytes(BF16, 1, 2, 1, 3, 128) == 256 + 256 + 2 * (6 * 128 * 2)
 
 
 # A made-up, 16-byte-aligned address: never dereferenced because every call

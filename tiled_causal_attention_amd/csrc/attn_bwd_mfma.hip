@@ -24,6 +24,8 @@
 // exact for |x| >= 2^-14 -- with fp32 accumulation. P and dS, computed values,
 // are rounded to fp16 (not bf16) for the products that consume them; their
 // partner operands are converted to fp16 in registers or when staged to LDS.
+#include <type_traits>
+
 #include "tca_internal.h"
 
 namespace tca {
@@ -72,7 +74,8 @@ template <int D>
 __global__ void __launch_bounds__(256, (D == 64) ? 3 : 1)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
               const float* __restrict__ o, const float* __restrict__ lse,
-              const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ dq,
+              const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
+              _Float16* __restrict__ q16, _Float16* __restrict__ do16, float* __restrict__ dq,
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
@@ -110,8 +113,10 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             const u32x4 dv = *reinterpret_cast<const u32x4*>(drow + 16 * c);
             const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
             const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
-            qb[c] = qok ? __builtin_bit_cast(f16x8, bf16x8_to_f16x8(qv)) : f16x8{};
+            const u32x4 qh16 = bf16x8_to_f16x8(qv);
+            qb[c] = qok ? __builtin_bit_cast(f16x8, qh16) : f16x8{};
             db[c] = qok ? __builtin_bit_cast(bf16x8, dv) : bf16x8{};
+
             part = fmaf(bf16_lo(dv.x), o0[0], part);
             part = fmaf(bf16_hi(dv.x), o0[1], part);
             part = fmaf(bf16_lo(dv.y), o0[2], part);
@@ -125,6 +130,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = Di;
     }
     const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
+    if (qok && h == 0 && khalf == 0) l2[bh * N + qi] = Li;
 
     u32x4 kreg[KCH], vreg[KCH];
     f32x16 dqa[DB];
@@ -185,6 +191,18 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         __syncthreads();
     }
 
+    // key half 0 leaves fp16 copies of its Q and dO rows in the workspace for
+    // the dK/dV phase, which copies them into LDS without conversion (stored
+    // after the tile loop, where the writes overlap other workgroups' math)
+    if (qok && khalf == 0) {
+        _Float16* q16row = q16 + (bh * N + qi) * D + 8 * h;
+        _Float16* d16row = do16 + (bh * N + qi) * D + 8 * h;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            *reinterpret_cast<u32x4*>(q16row + 16 * c) = __builtin_bit_cast(u32x4, qb[c]);
+            *reinterpret_cast<u32x4*>(d16row + 16 * c) = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, db[c]));
+        }
+    }
     // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
     // after the last barrier) and store. Accumulator e of dim block x holds dim
     // 32x + 8(e/4) + 4h + e%4 of query qi.
@@ -229,29 +247,61 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 //   dV += P^T dO, dK += dS^T Q (B operands: dO, Q tiles read transposed)
 namespace bwdkv {
 constexpr int BC = 64;
-constexpr int PAD = 8;
 template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int NQW = 4; };   // 8 waves, 128-row query tiles
 template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles
+
+// LDS layout of the staged fp16 Q and dO tiles: unpadded rows of D elements
+// (the copies land whole 1 KB blocks, so rows cannot be padded), 16-byte chunk
+// c of row R at chunk position c ^ swz(R). Without it the row-per-lane operand
+// reads (32 rows, one chunk) and the transposing reads (rows R..R+3 and
+// R+8..R+11, four chunks) of a plain layout hit the same banks: on 64-element
+// rows the plain layout made this pass ~30% slower, and swz = 2(R mod 4) +
+// (R/4 mod 2) was the fastest of the XOR patterns measured. 128-element rows
+// span every bank; there the swizzle sends rows R..R+3 to four different
+// 64-byte quarters of the row.
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+    return (D == 64) ? (((row & 3) << 1) | ((row >> 2) & 1)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int qd_off(int row, int col) {   // element offset of (row, col)
+    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
+}
+// lds_tr_operand for a swizzled tile: lane (h, r) receives tile[row0 + 8h + t][col0 + r], t = 0..7
+template <int D>
+__device__ __forceinline__ f16x8 qd_tr_operand(const _Float16* tile, int row0, int col0, int h, int r) {
+    const int row = row0 + 8 * h + ((r & 15) >> 2), col = col0 + 16 * (r >> 4) + 4 * (r & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + qd_off<D>(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + qd_off<D>(row + 4, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(f16x8, v);
+}
 }  // namespace bwdkv
 
 template <int D>
 __global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, 1)
-bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                const float* __restrict__ lse, const bf16_t* __restrict__ dout,
-                const float* __restrict__ delta, float* __restrict__ dk, float* __restrict__ dv,
+bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
+                const float* __restrict__ l2, const float* __restrict__ delta,
+                float* __restrict__ dk, float* __restrict__ dv,
                 int Hq, int Hkv, int N, int causal, float scale, int ntiles, int wg_per_unit) {
     using namespace bwdkv;
     constexpr int NQW = Cfg<D>::NQW;
-    constexpr int NT = 64 * 2 * NQW;          // threads
+    constexpr int NW = 2 * NQW;               // waves
     constexpr int BQ = 32 * NQW;              // query rows per staged tile
-    constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
-    constexpr int CPR = D / 8;
-    constexpr int QCH = BQ * CPR / NT;        // 16-byte chunks per thread per tensor per tile
-    __shared__ __attribute__((aligned(16))) _Float16 Qs[2][BQ][LD];
-    __shared__ __attribute__((aligned(16))) _Float16 dOs[2][BQ][LD];
-    __shared__ __attribute__((aligned(16))) float Ls[2][BQ];
-    __shared__ __attribute__((aligned(16))) float Ds[2][BQ];
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int TILE_BYTES = BQ * D * 2;    // one staged Q or dO tile
+    constexpr int IPW = TILE_BYTES / 1024 / NW;   // 1 KB copy instructions per wave per tile
+    constexpr int NJ = BQ * 4 / 256;          // 256-byte copy instructions per row-statistic tile
+    static_assert(IPW * NW * 1024 == TILE_BYTES && NJ * 256 == BQ * 4 && 2 * NJ <= NW, "staging split");
+    // double buffer as distinct LDS objects, so the compiler can tell the copy
+    // into one buffer from the reads of the other and does not make the reads
+    // wait for the copy (the item loop is unrolled by two to name them statically)
+    __shared__ __attribute__((aligned(16))) _Float16 Qs0[BQ * D], Qs1[BQ * D];
+    __shared__ __attribute__((aligned(16))) _Float16 dOs0[BQ * D], dOs1[BQ * D];
+    __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
     __shared__ __attribute__((aligned(16))) float red[NQW / 2][2][BC][D];   // dK, dV partial sums
 
     const int group = Hq / Hkv;
@@ -284,8 +334,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
 
     // items: for each of the workgroup's K/V tiles, every head g of the group
     // and every query tile qt at or below the diagonal (qt from first_qt(tile)).
-    // Two cursors walk the sequence: `cur` (computed now) and `ld` (prefetched,
-    // two items ahead); advancing is a few scalar compares, no division.
+    // Two cursors walk the sequence: `cur` (computed now) and `ld` (being
+    // staged, one item ahead); advancing is a few scalar compares, no division.
     struct Cursor {
         int t, g, qt;   // t: 0 -> tile_a, 1 -> tile_b, 2 -> done
     };
@@ -305,37 +355,37 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
     };
     auto tile_of = [&](const Cursor& c) { return c.t == 0 ? tile_a : tile_b; };
 
-    u32x4 qreg[QCH], dreg[QCH];
-    float lreg = 0.f, dlreg = 0.f;
-    auto load_item = [&](const Cursor& c) {
+    // Staging is a direct global -> LDS copy (no registers, no conversion): the
+    // workspace already holds Q and dO in fp16 and lse in log2 units. Copy
+    // instruction i of a tile fills LDS bytes [1024 i, 1024 i + 1024), lane l
+    // the 16 bytes at 1024 i + 16 l, i.e. row R = (1024 i + 16 l) / (2D) and
+    // chunk position p; it reads source chunk p ^ swz(R) of that row. Rows past
+    // the end of the sequence lie outside the buffer resource and read as zero.
+    uint32_t src_off[IPW];
+#pragma unroll
+    for (int u = 0; u < IPW; ++u) {
+        const int o = (w * IPW + u) * 1024 + lane * 16;
+        const int row = o / (2 * D), p = (o % (2 * D)) / 16;
+        src_off[u] = (uint32_t)(row * (2 * D) + ((p ^ swz<D>(row)) * 16));
+    }
+    auto stage = [&](const Cursor& c, _Float16* Qd, _Float16* dOd, float* Ld, float* Dd) {
         const size_t bh = (size_t)b * Hq + hkv * group + c.g;
-        const bf16_t* qh = q + bh * N * D;
-        const bf16_t* dh = dout + bh * N * D;
+        const int q0 = c.qt * BQ;
+        const uint32_t rows = (uint32_t)(N - q0);
+        const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q16 + (bh * N + q0) * D, rows * (D * 2));
+        const __amdgpu_buffer_rsrc_t drs = make_rsrc(do16 + (bh * N + q0) * D, rows * (D * 2));
 #pragma unroll
-        for (int u = 0; u < QCH; ++u) {
-            const int cid = tid + NT * u;
-            const int row = min(c.qt * BQ + cid / CPR, N - 1);
-            const size_t off = (size_t)row * D + (cid % CPR) * 8;
-            qreg[u] = *reinterpret_cast<const u32x4*>(qh + off);
-            dreg[u] = *reinterpret_cast<const u32x4*>(dh + off);
+        for (int u = 0; u < IPW; ++u) {
+            const int i = w * IPW + u;
+            lds_copy16(qrs, Qd + i * 512, src_off[u]);
+            lds_copy16(drs, dOd + i * 512, src_off[u]);
         }
-        if (tid < BQ) {
-            const int rc = min(c.qt * BQ + tid, N - 1);
-            lreg = lse[bh * N + rc];       // scaled to log2 units when staged, so
-            dlreg = delta[bh * N + rc];    // the prefetch is not waited on here
-        }
-    };
-    auto store_item = [&](int buf) {
-#pragma unroll
-        for (int u = 0; u < QCH; ++u) {
-            const int cid = tid + NT * u;
-            const int row = cid / CPR, col = (cid % CPR) * 8;
-            *reinterpret_cast<u32x4*>(&Qs[buf][row][col]) = bf16x8_to_f16x8(qreg[u]);
-            *reinterpret_cast<u32x4*>(&dOs[buf][row][col]) = bf16x8_to_f16x8(dreg[u]);
-        }
-        if (tid < BQ) {
-            Ls[buf][tid] = lreg * kLog2e;
-            Ds[buf][tid] = dlreg;
+        if (w < 2 * NJ) {   // row statistics: waves 0 .. NJ-1 copy L, NJ .. 2NJ-1 copy D
+            const int j = (w < NJ) ? w : w - NJ;
+            const float* src = (w < NJ) ? l2 : delta;
+            float* dst = ((w < NJ) ? Ld : Dd) + j * 64;
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + bh * N + q0, rows * 4);
+            lds_copy4(rs, dst, (uint32_t)(j * 64 + lane) * 4);
         }
     };
 
@@ -345,18 +395,20 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
     Cursor cur = {0, 0, fa}, ld = cur;
 
     if (nitems > 0) {
-        load_item(ld);
-        store_item(0);
+        stage(ld, Qs0, dOs0, Ls0, Ds0);
         advance(ld);
-        if (nitems > 1) {
-            load_item(ld);
-            advance(ld);
-        }
     }
+    wait_vmem_all();   // the copies land before the barrier that publishes them
     __syncthreads();
 
-    for (int it = 0; it < nitems; ++it) {
-        const int buf = it & 1;
+    // one item; BUF (compile time) names the buffer it reads, the other one
+    // receives the next item
+    auto item = [&](const int it, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        const _Float16* Qt = BUF ? Qs1 : Qs0;
+        const _Float16* dOt = BUF ? dOs1 : dOs0;
+        const float* Lt = BUF ? Ls1 : Ls0;
+        const float* Dt = BUF ? Ds1 : Ds0;
         const int tile = tile_of(cur), qt = cur.qt;
         const int kw0 = tile * BC + 32 * kh_;   // first key of this wave
         const int kw = kw0 + r;                 // this lane's key
@@ -376,31 +428,25 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
                 dva[x] = f32x16{};
             }
         }
+        // stage the next item into the other buffer (free since the last barrier)
+        if (it + 1 < nitems) {
+            if (BUF)
+                stage(ld, Qs0, dOs0, Ls0, Ds0);
+            else
+                stage(ld, Qs1, dOs1, Ls1, Ds1);
+            advance(ld);
+        }
         const int q0 = qt * BQ + 32 * qw;        // first query row of this wave's block
         const bool live = !causal || q0 + 31 >= kw0;
-        // Staging the next item (fp16 conversion + LDS stores) is VALU work;
-        // the two waves sharing a SIMD (w and w+4) run it at opposite ends of
-        // the iteration, so one wave's VALU phase meets the other's matrix
-        // phase instead of both doing the same thing in lock step.
-        auto stage = [&]() {
-            if (it + 1 < nitems) {
-                store_item(buf ^ 1);
-                if (it + 2 < nitems) {
-                    load_item(ld);
-                    advance(ld);
-                }
-            }
-        };
-        const bool stage_first = w >= 4;
-        if (stage_first) stage();
         if (live) {
             // ---- S = Q K^T, dP = dO V^T (accumulator e: query q0 + 16(e/8) + 8h + e%8, key kw)
             f32x16 s = f32x16{}, dp = f32x16{};
             const int arow = 32 * qw + perm32(r);
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const f16x8 aq = *reinterpret_cast<const f16x8*>(&Qs[buf][arow][16 * c + 8 * h]);
-                const f16x8 ad = *reinterpret_cast<const f16x8*>(&dOs[buf][arow][16 * c + 8 * h]);
+                const int off = qd_off<D>(arow, 16 * c + 8 * h);
+                const f16x8 aq = *reinterpret_cast<const f16x8*>(Qt + off);
+                const f16x8 ad = *reinterpret_cast<const f16x8*>(dOt + off);
                 s = mfma_f16(aq, kb[c], s);
                 dp = mfma_f16(ad, vb[c], dp);
             }
@@ -408,10 +454,10 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int qq = 32 * qw + 16 * c2 + 8 * h;   // tile row of accumulator 8c2
-                const f32x4 l0 = *reinterpret_cast<const f32x4*>(&Ls[buf][qq]);
-                const f32x4 l1 = *reinterpret_cast<const f32x4*>(&Ls[buf][qq + 4]);
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(&Ds[buf][qq]);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(&Ds[buf][qq + 4]);
+                const f32x4 l0 = *reinterpret_cast<const f32x4*>(Lt + qq);
+                const f32x4 l1 = *reinterpret_cast<const f32x4*>(Lt + qq + 4);
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(Dt + qq);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(Dt + qq + 4);
                 const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
                 const float dl[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
@@ -436,14 +482,13 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
                                           dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
 #pragma unroll
                 for (int x = 0; x < DB; ++x) {
-                    const f16x8 bo = lds_tr_operand(&dOs[buf][0][0], LD, 32 * qw + 16 * c2, 32 * x, h, r);
-                    const f16x8 bq = lds_tr_operand(&Qs[buf][0][0], LD, 32 * qw + 16 * c2, 32 * x, h, r);
+                    const f16x8 bo = qd_tr_operand<D>(dOt, 32 * qw + 16 * c2, 32 * x, h, r);
+                    const f16x8 bq = qd_tr_operand<D>(Qt, 32 * qw + 16 * c2, 32 * x, h, r);
                     dva[x] = mfma_f16(pa, bo, dva[x]);
                     dka[x] = mfma_f16(da, bq, dka[x]);
                 }
             }
         }
-        if (!stage_first) stage();
         advance(cur);
         // ---- end of a K/V tile: fixed-order reduction of the query sub-block partials
         if (it + 1 == nitems || tile_of(cur) != tile) {
@@ -504,7 +549,12 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, cons
                     }
             }
         }
+        wait_vmem_all();   // the copies land before the barrier that publishes them
         __syncthreads();
+    };
+    for (int it = 0; it < nitems; it += 2) {
+        item(it, std::integral_constant<int, 0>{});
+        if (it + 1 < nitems) item(it + 1, std::integral_constant<int, 1>{});
     }
 }
 
@@ -512,10 +562,11 @@ template <int D>
 static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + bwdq::BQ - 1) / bwdq::BQ;
     const int units = a.B * a.Hkv;
+    const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
     hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0, st,
                        (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.o,
-                       (const float*)a.lse, (const bf16_t*)a.dout, (float*)a.workspace, a.dq, a.Hq,
-                       a.Hkv, a.N, a.causal, a.scale, nqt, units);
+                       (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, a.dq,
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units);
     return hipGetLastError();
 }
 
@@ -524,10 +575,10 @@ static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     const int ntiles = (a.N + bwdkv::BC - 1) / bwdkv::BC;
     const int per_unit = a.causal ? (ntiles + 1) / 2 : ntiles;
     const int threads = 64 * 2 * bwdkv::Cfg<D>::NQW;
+    const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
     hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
-                       (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.lse,
-                       (const bf16_t*)a.dout, (const float*)a.workspace, a.dk, a.dv, a.Hq, a.Hkv, a.N,
-                       a.causal, a.scale, ntiles, per_unit);
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, a.dk,
+                       a.dv, a.Hq, a.Hkv, a.N, a.causal, a.scale, ntiles, per_unit);
     return hipGetLastError();
 }
 

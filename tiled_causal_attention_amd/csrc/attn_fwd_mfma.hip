@@ -251,7 +251,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
 }
 
-bool mfma_path(const AttnArgs& a) { return a.dtype == ATTN_BF16 && (a.d == 64 || a.d == 128); }
+bool mfma_path(const AttnArgs& a) { return mfma_shape(a.dtype, a.d); }
 
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + fwd::BR - 1) / fwd::BR;

@@ -35,10 +35,6 @@ attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
     return ATTN_OK;
 }
 
-size_t bwd_ws_bytes(int B, int Hq, int N) {
-    const size_t bytes = (size_t)B * Hq * N * sizeof(float);
-    return (bytes + 255) & ~(size_t)255;
-}
 
 attn_status check_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
                       const float* lse, const void* dO, float* dq, float* dk, float* dv,
@@ -50,7 +46,7 @@ attn_status check_bwd(attn_dtype dtype, const void* q, const void* k, const void
     if (*noop) return ATTN_OK;
     s = check_ptrs({q, k, v, o, lse, dO, dq, dk, dv, ws});
     if (s != ATTN_OK) return s;
-    if (ws_bytes < bwd_ws_bytes(B, Hq, N)) return ATTN_EINVAL;
+    if (ws_bytes < tca::bwd_workspace_size(dtype, B, Hq, N, d)) return ATTN_EINVAL;
     return ATTN_OK;
 }
 
@@ -127,9 +123,9 @@ attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void*
 }
 
 size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d) {
-    (void)dtype; (void)Hkv; (void)d;
+    (void)Hkv;
     if (B < 0 || Hq < 0 || N < 0) return 0;
-    return bwd_ws_bytes(B, Hq, N);
+    return tca::bwd_workspace_size(dtype, B, Hq, N, d);
 }
 
 attn_status attn_bwd_dq(attn_dtype dtype, const void* q, const void* k, const void* v,

@@ -74,6 +74,19 @@ __device__ __forceinline__ float max16(const f32x16& s) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
+// Direct global -> LDS copy through a buffer resource (no registers): lane l
+// reads `bytes` (4 or 16) at byte offset voff and writes them to LDS at
+// lds_dst + l * bytes; lds_dst must be the same in every lane. Completion is
+// tracked by vmcnt: wait for it (s_waitcnt vmcnt(0)) and then barrier before
+// any wave reads the destination.
+__device__ __forceinline__ void lds_copy16(__amdgpu_buffer_rsrc_t rs, void* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void lds_copy4(__amdgpu_buffer_rsrc_t rs, void* lds_dst, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds_dst, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x3f70); }   // vmcnt(0)
+
 // One 16-byte chunk at byte offset voff (per lane) through a buffer resource.
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);

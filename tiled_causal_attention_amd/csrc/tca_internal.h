@@ -27,6 +27,43 @@ struct AttnArgs {
     float scale;
 };
 
+// True when the matrix-core kernels serve these inputs: bf16, d in {64, 128}.
+inline bool mfma_shape(attn_dtype dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
+
+// Backward workspace, each section starting on a 256-byte boundary:
+//   delta  D = rowsum(dO o O), float32 [B, Hq, N]           (both paths)
+//   l2     lse * log2(e), float32 [B, Hq, N]                (matrix-core path)
+//   q16    q converted to fp16, [B, Hq, N, d]               (matrix-core path)
+//   do16   dO converted to fp16, [B, Hq, N, d]              (matrix-core path)
+// The dQ phase writes all of them; the dK/dV phase reads them.
+struct BwdWorkspace {
+    float* delta;
+    float* l2;
+    _Float16* q16;
+    _Float16* do16;
+};
+inline size_t ws_round(size_t n) { return (n + 255) & ~(size_t)255; }
+inline size_t bwd_workspace_size(attn_dtype dtype, int B, int Hq, int N, int d) {
+    const size_t rows = (size_t)B * Hq * N;
+    size_t n = ws_round(rows * sizeof(float));
+    if (mfma_shape(dtype, d)) n += ws_round(rows * sizeof(float)) + 2 * ws_round(rows * d * 2);
+    return n;
+}
+inline BwdWorkspace bwd_workspace_layout(void* ws, attn_dtype dtype, int B, int Hq, int N, int d) {
+    const size_t rows = (size_t)B * Hq * N;
+    char* p = static_cast<char*>(ws);
+    BwdWorkspace w = {reinterpret_cast<float*>(p), nullptr, nullptr, nullptr};
+    if (mfma_shape(dtype, d)) {
+        p += ws_round(rows * sizeof(float));
+        w.l2 = reinterpret_cast<float*>(p);
+        p += ws_round(rows * sizeof(float));
+        w.q16 = reinterpret_cast<_Float16*>(p);
+        p += ws_round(rows * d * 2);
+        w.do16 = reinterpret_cast<_Float16*>(p);
+    }
+    return w;
+}
+
 // float32-arithmetic path (any supported d, either dtype). The backward's
 // first phase writes D = rowsum(dO o O) into the workspace and dq; the second
 // reads D and writes dk, dv.
