@@ -160,16 +160,20 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                 s = mfma_f16(ak, qb[c], s);
                 dp = mfma_bf16(av, db[c], dp);
             }
-            // ---- P, dS (accumulator e: key kw0 + 16(e/8) + 8h + e%8)
-            const bool need_mask = (kw0 + 32 > N) || (causal && kw0 + 31 > q0w);
+            // ---- mask, only on tiles crossing the diagonal or the end of the sequence
+            // (one wave-uniform branch; the common path carries no mask work):
+            // accumulator e holds key kw0 + 8h + c_e, c_e = 16(e/8) + e%8, kept iff
+            // key < N and (if causal) key <= qi
+            if ((kw0 + 32 > N) || (causal && kw0 + 31 > q0w)) {
+                const int lim = (causal ? min(qi, N - 1) : N - 1) - 8 * h - kw0;
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    s[e] = (16 * (e >> 3) + (e & 7) <= lim) ? s[e] : -INFINITY;
+            }
+            // ---- P, dS
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                float p = fast_exp2(fmaf(s[e], sl2, -Li));
-                if (need_mask) {   // wave-uniform; the select itself is branch-free
-                    const int key = kw0 + 16 * (e >> 3) + 8 * h + (e & 7);
-                    const bool keep = (key < N) & (!causal | (key <= qi));
-                    p = keep ? p : 0.f;
-                }
+                const float p = fast_exp2(fmaf(s[e], sl2, -Li));
                 s[e] = p * (dp[e] - Di);   // dS
             }
             // ---- dQ^T += K^T dS^T  (A: the wave's K rows read transposed; B: dS from registers)
@@ -450,7 +454,19 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 s = mfma_f16(aq, kb[c], s);
                 dp = mfma_f16(ad, vb[c], dp);
             }
-            const bool need_mask = (q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31);
+            // ---- mask, only on items crossing the diagonal or an end of the sequence
+            // (one wave-uniform branch; the common path carries no mask work):
+            // accumulator e holds query q0 + 8h + c_e, c_e = 16(e/8) + e%8, kept iff
+            // query < N, kw < N and (if causal) kw <= query
+            if ((q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31)) {
+                const int lo = (causal ? kw : 0) - q0 - 8 * h;
+                const int hi = (kw < N) ? N - q0 - 8 * h : lo;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int ce = 16 * (e >> 3) + (e & 7);
+                    s[e] = (ce >= lo && ce < hi) ? s[e] : -INFINITY;
+                }
+            }
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const int qq = 32 * qw + 16 * c2 + 8 * h;   // tile row of accumulator 8c2
@@ -463,12 +479,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int e = 8 * c2 + t;
-                    float p = fast_exp2(fmaf(s[e], sl2, -lv[t]));
-                    if (need_mask) {   // wave-uniform; the select itself is branch-free
-                        const int qrow = qt * BQ + qq + t;
-                        const bool keep = (qrow < N) & (kw < N) & (!causal | (kw <= qrow));
-                        p = keep ? p : 0.f;
-                    }
+                    const float p = fast_exp2(fmaf(s[e], sl2, -lv[t]));
                     s[e] = p;
                     dp[e] = p * (dp[e] - dl[t]);
                 }
