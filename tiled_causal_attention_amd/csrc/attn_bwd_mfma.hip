@@ -255,33 +255,6 @@ template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int NQW = 4; };   // 8 waves, 128-row query tiles
 template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles
 
-// LDS layout of the staged fp16 Q and dO tiles: unpadded rows of D elements
-// (the copies land whole 1 KB blocks, so rows cannot be padded), 16-byte chunk
-// c of row R at chunk position c ^ swz(R). Without it the row-per-lane operand
-// reads (32 rows, one chunk) and the transposing reads (rows R..R+3 and
-// R+8..R+11, four chunks) of a plain layout hit the same banks: on 64-element
-// rows the plain layout made this pass ~30% slower, and swz = 2(R mod 4) +
-// (R/4 mod 2) was the fastest of the XOR patterns measured. 128-element rows
-// span every bank; there the swizzle sends rows R..R+3 to four different
-// 64-byte quarters of the row.
-template <int D>
-__device__ __forceinline__ int swz(int row) {
-    return (D == 64) ? (((row & 3) << 1) | ((row >> 2) & 1)) : (((row & 3) << 2) | ((row >> 2) & 3));
-}
-template <int D>
-__device__ __forceinline__ int qd_off(int row, int col) {   // element offset of (row, col)
-    return row * D + ((((col >> 3) ^ swz<D>(row))) << 3) + (col & 7);
-}
-// lds_tr_operand for a swizzled tile: lane (h, r) receives tile[row0 + 8h + t][col0 + r], t = 0..7
-template <int D>
-__device__ __forceinline__ f16x8 qd_tr_operand(const _Float16* tile, int row0, int col0, int h, int r) {
-    const int row = row0 + 8 * h + ((r & 15) >> 2), col = col0 + 16 * (r >> 4) + 4 * (r & 3);
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + qd_off<D>(row, col)));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + qd_off<D>(row + 4, col)));
-    typedef short s16x8 __attribute__((ext_vector_type(8)));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(f16x8, v);
-}
 }  // namespace bwdkv
 
 template <int D>
@@ -363,15 +336,11 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     // workspace already holds Q and dO in fp16 and lse in log2 units. Copy
     // instruction i of a tile fills LDS bytes [1024 i, 1024 i + 1024), lane l
     // the 16 bytes at 1024 i + 16 l, i.e. row R = (1024 i + 16 l) / (2D) and
-    // chunk position p; it reads source chunk p ^ swz(R) of that row. Rows past
+    // chunk position p; it reads source chunk p ^ tile_swz(R) of that row. Rows past
     // the end of the sequence lie outside the buffer resource and read as zero.
     uint32_t src_off[IPW];
 #pragma unroll
-    for (int u = 0; u < IPW; ++u) {
-        const int o = (w * IPW + u) * 1024 + lane * 16;
-        const int row = o / (2 * D), p = (o % (2 * D)) / 16;
-        src_off[u] = (uint32_t)(row * (2 * D) + ((p ^ swz<D>(row)) * 16));
-    }
+    for (int u = 0; u < IPW; ++u) src_off[u] = tile_copy_src<D>(w * IPW + u, lane);
     auto stage = [&](const Cursor& c, _Float16* Qd, _Float16* dOd, float* Ld, float* Dd) {
         const size_t bh = (size_t)b * Hq + hkv * group + c.g;
         const int q0 = c.qt * BQ;
@@ -448,7 +417,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             const int arow = 32 * qw + perm32(r);
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const int off = qd_off<D>(arow, 16 * c + 8 * h);
+                const int off = tile_off<D>(arow, 16 * c + 8 * h);
                 const f16x8 aq = *reinterpret_cast<const f16x8*>(Qt + off);
                 const f16x8 ad = *reinterpret_cast<const f16x8*>(dOt + off);
                 s = mfma_f16(aq, kb[c], s);
@@ -493,8 +462,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                           dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
 #pragma unroll
                 for (int x = 0; x < DB; ++x) {
-                    const f16x8 bo = qd_tr_operand<D>(dOt, 32 * qw + 16 * c2, 32 * x, h, r);
-                    const f16x8 bq = qd_tr_operand<D>(Qt, 32 * qw + 16 * c2, 32 * x, h, r);
+                    const f16x8 bo = tile_tr_operand<D>(dOt, 32 * qw + 16 * c2, 32 * x, h, r);
+                    const f16x8 bq = tile_tr_operand<D>(Qt, 32 * qw + 16 * c2, 32 * x, h, r);
                     dva[x] = mfma_f16(pa, bo, dva[x]);
                     dka[x] = mfma_f16(da, bq, dka[x]);
                 }

@@ -127,6 +127,44 @@ __device__ __forceinline__ f16x8 lds_tr_operand(const _Float16* tile, int stride
     return __builtin_bit_cast(f16x8, v);
 }
 
+// LDS layout of tiles staged by direct global -> LDS copies (the Q and dO
+// tiles of the dK/dV pass): unpadded rows of D 16-bit
+// elements (the copies land whole 1 KB blocks, so rows cannot be padded),
+// 16-byte chunk c of row R at chunk position c ^ tile_swz(R). Without it the
+// row-per-lane operand reads (32 rows, one chunk) and the transposing reads
+// (rows R..R+3 and R+8..R+11, four chunks) of a plain layout hit the same
+// banks: on 64-element rows the plain layout made the dK/dV pass ~30% slower,
+// and 2(R mod 4) + (R/4 mod 2) was the fastest of the XOR patterns measured.
+// 128-element rows span every bank; there the swizzle sends rows R..R+3 to
+// four different 64-byte quarters of the row.
+template <int D>
+__device__ __forceinline__ int tile_swz(int row) {
+    return (D == 64) ? (((row & 3) << 1) | ((row >> 2) & 1)) : (((row & 3) << 2) | ((row >> 2) & 3));
+}
+template <int D>
+__device__ __forceinline__ int tile_off(int row, int col) {   // element offset of (row, col)
+    return row * D + ((((col >> 3) ^ tile_swz<D>(row))) << 3) + (col & 7);
+}
+// Source byte offset, within a tile of such rows, of the 16 bytes that lane
+// `lane` of copy instruction i lands at LDS byte 1024 i + 16 lane: row R and
+// chunk position p there hold source chunk p ^ tile_swz(R) of row R.
+template <int D>
+__device__ __forceinline__ uint32_t tile_copy_src(int i, int lane) {
+    const int o = i * 1024 + lane * 16;
+    const int row = o / (2 * D), p = (o % (2 * D)) / 16;
+    return (uint32_t)(row * (2 * D) + ((p ^ tile_swz<D>(row)) * 16));
+}
+// lds_tr_operand for such a tile: lane (h, r) receives tile[row0 + 8h + t][col0 + r], t = 0..7
+template <int D>
+__device__ __forceinline__ f16x8 tile_tr_operand(const _Float16* tile, int row0, int col0, int h, int r) {
+    const int row = row0 + 8 * h + ((r & 15) >> 2), col = col0 + 16 * (r >> 4) + 4 * (r & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tile_off<D>(row, col)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tile + tile_off<D>(row + 4, col)));
+    typedef short s16x8 __attribute__((ext_vector_type(8)));
+    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(f16x8, v);
+}
+
 // Reductions across the two half-waves with v_permlane32_swap: swapping a
 // register with itself leaves, in every lane, the pair {own value, value of
 // lane l ^ 32}, so max/sum over the pair combine the two halves.
