@@ -127,9 +127,10 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             part = fmaf(bf16_hi(dv.w), o1[3], part);
         }
         Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
-        if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = Di;
+        if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
     }
     const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
+    const f32x16 negD = f32x16{} - Di;   // -D_i in every accumulator of this lane's query column
     if (qok && h == 0 && khalf == 0) l2[bh * N + qi] = Li;
 
     u32x4 kreg[KCH], vreg[KCH];
@@ -151,8 +152,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         const int buf = j & 1, k0 = j * BC;
         const int kw0 = k0 + 32 * khalf;   // first key of this wave's half
         if (!causal || kw0 <= q0w + 31) {
-            // ---- S^T = K Q^T and dP^T = V dO^T (rows: the wave's keys, permuted; columns: queries)
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // ---- S^T = K Q^T and dP^T - D = V dO^T - D (rows: the wave's keys, permuted;
+            // columns: queries): the dP product accumulates onto -D_i, so no subtraction follows
+            f32x16 s = f32x16{}, dp = negD;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
                 const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
@@ -174,7 +176,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = fast_exp2(fmaf(s[e], sl2, -Li));
-                s[e] = p * (dp[e] - Di);   // dS
+                s[e] = p * dp[e];   // dS = P (dP - D)
             }
             // ---- dQ^T += K^T dS^T  (A: the wave's K rows read transposed; B: dS from registers)
 #pragma unroll
@@ -412,8 +414,18 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
         const int q0 = qt * BQ + 32 * qw;        // first query row of this wave's block
         const bool live = !causal || q0 + 31 >= kw0;
         if (live) {
-            // ---- S = Q K^T, dP = dO V^T (accumulator e: query q0 + 16(e/8) + 8h + e%8, key kw)
-            f32x16 s = f32x16{}, dp = f32x16{};
+            // ---- S = Q K^T, dP - D = dO V^T - D (accumulator e: query q0 + 16(e/8) + 8h + e%8,
+            // key kw): the row statistic arrives as -D, and the dP product accumulates onto it
+            f32x16 s = f32x16{}, dp;
+            {
+                const int qq = 32 * qw + 8 * h;
+                const f32x4 d0 = *reinterpret_cast<const f32x4*>(Dt + qq);
+                const f32x4 d1 = *reinterpret_cast<const f32x4*>(Dt + qq + 4);
+                const f32x4 d2 = *reinterpret_cast<const f32x4*>(Dt + qq + 16);
+                const f32x4 d3 = *reinterpret_cast<const f32x4*>(Dt + qq + 20);
+                dp = f32x16{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3],
+                            d2[0], d2[1], d2[2], d2[3], d3[0], d3[1], d3[2], d3[3]};
+            }
             const int arow = 32 * qw + perm32(r);
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
@@ -441,16 +453,13 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const int qq = 32 * qw + 16 * c2 + 8 * h;   // tile row of accumulator 8c2
                 const f32x4 l0 = *reinterpret_cast<const f32x4*>(Lt + qq);
                 const f32x4 l1 = *reinterpret_cast<const f32x4*>(Lt + qq + 4);
-                const f32x4 d0 = *reinterpret_cast<const f32x4*>(Dt + qq);
-                const f32x4 d1 = *reinterpret_cast<const f32x4*>(Dt + qq + 4);
                 const float lv[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
-                const float dl[8] = {d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
 #pragma unroll
                 for (int t = 0; t < 8; ++t) {
                     const int e = 8 * c2 + t;
                     const float p = fast_exp2(fmaf(s[e], sl2, -lv[t]));
                     s[e] = p;
-                    dp[e] = p * (dp[e] - dl[t]);
+                    dp[e] = p * dp[e];   // dS = P (dP - D)
                 }
             }
             // ---- dV += P^T dO, dK += dS^T Q (B: dO, Q tiles read transposed, rows = queries)

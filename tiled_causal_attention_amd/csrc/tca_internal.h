@@ -31,7 +31,8 @@ struct AttnArgs {
 inline bool mfma_shape(attn_dtype dtype, int d) { return dtype == ATTN_BF16 && (d == 64 || d == 128); }
 
 // Backward workspace, each section starting on a 256-byte boundary:
-//   delta  D = rowsum(dO o O), float32 [B, Hq, N]           (both paths)
+//   delta  D = rowsum(dO o O), float32 [B, Hq, N]           (both paths; the matrix-core
+//          path stores -D, the dK/dV pass's starting dP accumulator)
 //   l2     lse * log2(e), float32 [B, Hq, N]                (matrix-core path)
 //   q16    q converted to fp16, [B, Hq, N, d]               (matrix-core path)
 //   do16   dO converted to fp16, [B, Hq, N, d]              (matrix-core path)
