@@ -40,33 +40,31 @@ constexpr int BC = 64;           // keys per K/V tile
 constexpr int PAD = 8;
 }  // namespace bwdq
 
-// Global -> registers: K and V rows k0 .. k0 + BC - 1 (clamped to N - 1).
+// Global -> registers: the K and V chunks of one tile through buffer resources
+// over the head's N rows; voff is this thread's byte offset of chunk 0 in the
+// tile's first row. Thread tid owns chunks tid + 256u (a wave reads whole
+// rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
-__device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], const bf16_t* kh,
-                                            const bf16_t* vh, int k0, int N, int tid) {
-    constexpr int CPR = D / 8;
+__device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
+                                            __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        const int cid = tid + 256 * u;
-        const int key = min(k0 + cid / CPR, N - 1);
-        const size_t off = (size_t)key * D + (cid % CPR) * 8;
-        kreg[u] = *reinterpret_cast<const u32x4*>(kh + off);
-        vreg[u] = *reinterpret_cast<const u32x4*>(vh + off);
+        kreg[u] = buf_load16(kr, voff + u * 256 * 16);
+        vreg[u] = buf_load16(vr, voff + u * 256 * 16);
     }
 }
 
-// Registers -> LDS: K converted to fp16 rows, V kept as bf16 rows.
+// Registers -> LDS: K converted to fp16 rows, V kept as bf16 rows. kdst/vdst
+// point at this thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8)));
+// chunk u sits 256u / (D/8) rows further down.
 template <int D, int KCH>
 __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH],
-                                             _Float16 (*Ks)[D + bwdq::PAD], bf16_t (*Vs)[D + bwdq::PAD],
-                                             int tid) {
-    constexpr int CPR = D / 8;
+                                             _Float16* kdst, bf16_t* vdst) {
+    constexpr int ROWS_PER_U = 256 / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        const int cid = tid + 256 * u;
-        const int row = cid / CPR, col = (cid % CPR) * 8;
-        *reinterpret_cast<u32x4*>(&Ks[row][col]) = bf16x8_to_f16x8(kreg[u]);
-        *reinterpret_cast<u32x4*>(&Vs[row][col]) = vreg[u];
+        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::PAD)) = bf16x8_to_f16x8(kreg[u]);
+        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + bwdq::PAD)) = vreg[u];
     }
 }
 
@@ -143,9 +141,15 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const int ntile = (kend + BC - 1) / BC;
     const int krow_a = perm32(r);
 
-    bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, 0, N, tid);
-    bwd_store_kv<D, KCH>(kreg, vreg, Ks[0], Vs[0], tid);
-    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, BC, N, tid);
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)N * D * 2);
+    const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a tile
+    const int st_off = (tid / CPR) * LD + (tid % CPR) * 8;           // LDS slot of chunk 0 (elements)
+    constexpr int TBUF = BC * LD;                                      // elements per LDS tile buffer
+
+    bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
+    bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
+    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
 
     for (int j = 0; j < ntile; ++j) {
@@ -191,8 +195,10 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             }
         }
         if (j + 1 < ntile) {
-            bwd_store_kv<D, KCH>(kreg, vreg, Ks[buf ^ 1], Vs[buf ^ 1], tid);
-            if (j + 2 < ntile) bwd_load_kv<D, KCH>(kreg, vreg, kh, vh, (j + 2) * BC, N, tid);
+            bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + (buf ^ 1) * TBUF + st_off,
+                                 &Vs[0][0][0] + (buf ^ 1) * TBUF + st_off);
+            if (j + 2 < ntile)
+                bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + (uint32_t)(j + 2) * (BC * D * 2));
         }
         __syncthreads();
     }
