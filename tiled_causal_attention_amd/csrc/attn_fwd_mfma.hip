@@ -4,8 +4,9 @@
 // workgroup per query tile; for each K/V tile: stage it on chip, Q*K^T, online
 // softmax, accumulate the output), re-shaped for CDNA4:
 //
-//  * A workgroup covers 64 query rows with 4 waves: 2 row blocks of 32 rows x
-//    2 key halves. Wave (rb, kh) takes keys 32kh .. 32kh+31 of every K/V tile
+//  * A workgroup covers 64 query rows with 4 waves (d = 64) or 128 rows with 8
+//    waves (d = 128): row blocks of 32 rows x 2 key halves. Wave (rb, kh) takes
+//    keys 32kh .. 32kh+31 of every K/V tile
 //    for its 32 rows and runs its own online softmax over them; the two key
 //    halves of a row block are merged once, through LDS, at the end. Splitting
 //    the keys halves the serial work each wave does per tile, which is what
@@ -46,8 +47,14 @@
 namespace tca {
 
 namespace fwd {
-constexpr int NW = 4;            // waves per workgroup: 2 row blocks x 2 key halves
-constexpr int BR = 64;           // query rows per workgroup
+// Waves per workgroup: kWaves/2 row blocks of 32 query rows x 2 key halves. At
+// d = 128 a K/V tile is twice the bytes, so it is shared by 8 waves (128 query
+// rows: half the staging per wave, measured -10% on a long d = 128 shape); at
+// d = 64 the causal N = 1024 shape runs faster with 4 waves (64 rows), whose
+// twice as many workgroups leave a shorter tail.
+template <int D> constexpr int kWaves = (D == 128) ? 8 : 4;
+template <int D> constexpr int kThreads = 64 * kWaves<D>;
+template <int D> constexpr int kRows = 16 * kWaves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile (32 per key half)
 constexpr int PAD = 8;           // 16-bit elements of row padding (16 bytes)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
@@ -55,25 +62,25 @@ constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 
 // Global -> registers: the K and V chunks of one tile through buffer
 // resources over the head's N rows; voff is this thread's byte offset of chunk
-// 0 in the tile's first row. Thread tid owns chunks tid + 256u (a wave reads
+// 0 in the tile's first row. Thread tid owns chunks tid + T u, T threads (a wave reads
 // whole rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
 __device__ __forceinline__ void load_kv_tile(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
                                              __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        kreg[u] = buf_load16(kr, voff + u * 256 * 16);
-        vreg[u] = buf_load16(vr, voff + u * 256 * 16);
+        kreg[u] = buf_load16(kr, voff + u * fwd::kThreads<D> * 16);
+        vreg[u] = buf_load16(vr, voff + u * fwd::kThreads<D> * 16);
     }
 }
 
 // Registers -> LDS: K as bf16 rows, V converted to fp16 rows. kdst/vdst point
 // at this thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8))); chunk u
-// sits 256u / (D/8) rows further down.
+// sits T u / (D/8) rows further down (T threads).
 template <int D, int KCH>
 __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH], bf16_t* kdst,
                                               _Float16* vdst) {
-    constexpr int ROWS_PER_U = 256 / (D / 8);
+    constexpr int ROWS_PER_U = fwd::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + fwd::PAD)) = kreg[u];
@@ -82,7 +89,7 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, (D == 64) ? 4 : 2)
+__global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 1)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
                 int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
@@ -91,9 +98,16 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     constexpr int DB = D / 32;          // 32-wide blocks of the head dimension
     constexpr int LD = D + PAD;         // LDS row stride (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
-    constexpr int KCH = BC * CPR / 256; // chunks per thread per tensor per tile
-    __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BC][LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Vs[2][BC][LD];
+    constexpr int NT = kThreads<D>;     // threads
+    constexpr int BR = kRows<D>;        // query rows per workgroup
+    constexpr int NRB = kWaves<D> / 2;  // row blocks
+    constexpr int KCH = BC * CPR / NT;  // chunks per thread per tensor per tile
+    // K and V tile buffers, carved from one LDS block: after the loop the whole
+    // block is the merge area of the key halves (NRB row blocks of 32 x D floats)
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BC * LD * 2];
+    bf16_t (*Ks)[BC][LD] = reinterpret_cast<bf16_t (*)[BC][LD]>(smem);
+    _Float16 (*Vs)[BC][LD] = reinterpret_cast<_Float16 (*)[BC][LD]>(smem + 2 * BC * LD * 2);
+    static_assert(NRB * 32 * D * 4 + NRB * 64 * 4 <= (int)sizeof(smem), "merge area exceeds the tile buffers");
 
     const int group = Hq / Hkv;
     const TileMap tm = map_workgroup(blockIdx.x, nqt, units, Hkv, group);
@@ -118,7 +132,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
     }
 
-    // K/V tile prefetch registers: thread owns chunks tid + 256u (coalesced rows)
+    // K/V tile prefetch registers: thread owns chunks tid + NT u (coalesced rows)
     u32x4 kreg[KCH], vreg[KCH];
     f32x16 oacc[DB];
 #pragma unroll
@@ -215,8 +229,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // store O (fp32) and LSE (natural log). Accumulator e of dim block x holds
     // dim 32x + 8(e/4) + 4h + e%4 of query qi.
     float l_tot = sum_halves(l_run);
-    float* xo = reinterpret_cast<float*>(&Ks[0][0][0]) + rb * (32 * D);   // [32 rows][D]
-    float* xs = reinterpret_cast<float*>(&Ks[0][0][0]) + 2 * 32 * D + rb * 64;   // m[32], l[32]
+    float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);             // [32 rows][D]
+    float* xs = reinterpret_cast<float*>(smem) + NRB * 32 * D + rb * 64;    // m[32], l[32]
     if (khalf == 1) {
 #pragma unroll
         for (int x = 0; x < DB; ++x)
@@ -253,19 +267,19 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
 bool mfma_path(const AttnArgs& a) { return mfma_shape(a.dtype, a.d); }
 
-hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
-    const int nqt = (a.N + fwd::BR - 1) / fwd::BR;
+template <int D>
+static hipError_t launch_fwd_d(const AttnArgs& a, hipStream_t st) {
+    const int nqt = (a.N + fwd::kRows<D> - 1) / fwd::kRows<D>;
     const int units = a.B * a.Hkv;
     const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-    if (a.d == 64)
-        hipLaunchKernelGGL(fwd_mfma_kernel<64>, grid, dim3(256), 0, st, (const bf16_t*)a.q,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N,
-                           a.causal, a.scale, nqt, units);
-    else
-        hipLaunchKernelGGL(fwd_mfma_kernel<128>, grid, dim3(256), 0, st, (const bf16_t*)a.q,
-                           (const bf16_t*)a.k, (const bf16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N,
-                           a.causal, a.scale, nqt, units);
+    hipLaunchKernelGGL(fwd_mfma_kernel<D>, grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, a.causal,
+                       a.scale, nqt, units);
     return hipGetLastError();
+}
+
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
+    return (a.d == 64) ? launch_fwd_d<64>(a, st) : launch_fwd_d<128>(a, st);
 }
 
 }  // namespace tca
