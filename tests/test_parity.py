@@ -224,3 +224,38 @@ def test_empty_inputs_on_gpu():
     o, lse = tca.attn_fwd(q, k, k)
     dq, dk, dv = tca.attn_bwd(q, k, k, o, lse, q)
     assert dq.shape == q.shape and dk.shape == k.shape
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_workspace_contents(d):
+    """What attn_bwd_dq leaves in the workspace on the matrix-core path (the dK/dV
+    phase consumes it): -D with D = rowsum(dO o O) against the oracle's O, lse in
+    base-2 units, and q, dO converted to fp16 (bf16 -> fp16 is exact here)."""
+    s = workloads.make_shape(2, 6, 2, 200, d, dtype="bf16", seed=17)
+    q, k, v, do = workloads.make_inputs(s)
+    qd, kd, vd, dod = _dev(q, k, v, do)
+    o, lse = tca.attn_fwd(qd, kd, vd, causal=True, scale=s.scale)
+    ws = tca.bwd_workspace(qd, kd)
+    dq = torch.empty(q.shape, device="cuda")
+    dk = torch.empty(k.shape, device="cuda")
+    dv = torch.empty(k.shape, device="cuda")
+    tca.attn_bwd_dq(qd, kd, vd, o, lse, dod, dq, dk, dv, ws, True, s.scale)
+    torch.cuda.synchronize()
+    rows = s.B * s.Hq * s.N
+    rnd = lambda n: (n + 255) // 256 * 256
+    off_l2 = rnd(rows * 4)
+    off_q16 = off_l2 + rnd(rows * 4)
+    off_do16 = off_q16 + rnd(rows * d * 2)
+    assert ws.numel() == off_do16 + rnd(rows * d * 2)
+    w = ws.cpu()
+    neg_d = w[:rows * 4].view(torch.float32).double().numpy().reshape(s.B, s.Hq, s.N)
+    l2 = w[off_l2:off_l2 + rows * 4].view(torch.float32).numpy().reshape(s.B, s.Hq, s.N)
+    q16 = w[off_q16:off_q16 + rows * d * 2].view(torch.float16).reshape(q.shape)
+    do16 = w[off_do16:off_do16 + rows * d * 2].view(torch.float16).reshape(q.shape)
+    assert torch.equal(q16, q.to(torch.float16)) and torch.equal(do16, do.to(torch.float16))
+    lse_c = lse.cpu().numpy()
+    assert np.array_equal(l2, (lse_c * np.float32(math.log2(math.e))).astype(np.float32))
+    ro, _ = oracle.attn_fwd(q, k, v, 1, s.scale)
+    dref = (do.double().numpy() * ro).sum(-1)
+    # D from the kernel's own O (fp32) differs from the oracle's by the forward's rounding
+    assert np.abs(neg_d + dref).max() <= 1e-2 * max(1.0, np.abs(dref).max())
