@@ -224,7 +224,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h) =
+                *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
                     f32x4{dqa[x][4 * a4 + 0], dqa[x][4 * a4 + 1], dqa[x][4 * a4 + 2], dqa[x][4 * a4 + 3]};
     }
     __syncthreads();
@@ -234,7 +234,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h);
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
                 const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
                                    (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
                 *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;

@@ -236,7 +236,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h) =
+                *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
                     f32x4{oacc[x][4 * a4 + 0], oacc[x][4 * a4 + 1], oacc[x][4 * a4 + 2], oacc[x][4 * a4 + 3]};
         if (h == 0) {
             xs[r] = m_s;
@@ -256,7 +256,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + r * D + 32 * x + 8 * a4 + 4 * h);
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
                 const f32x4 val = {oacc[x][4 * a4 + 0] * c0 + o1[0] * c1, oacc[x][4 * a4 + 1] * c0 + o1[1] * c1,
                                    oacc[x][4 * a4 + 2] * c0 + o1[2] * c1, oacc[x][4 * a4 + 3] * c0 + o1[3] * c1};
                 *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;

@@ -127,19 +127,29 @@ __device__ __forceinline__ f16x8 lds_tr_operand(const _Float16* tile, int stride
     return __builtin_bit_cast(f16x8, v);
 }
 
-// LDS layout of tiles staged by direct global -> LDS copies (the Q and dO
-// tiles of the dK/dV pass): unpadded rows of D 16-bit
-// elements (the copies land whole 1 KB blocks, so rows cannot be padded),
-// 16-byte chunk c of row R at chunk position c ^ tile_swz(R). Without it the
-// row-per-lane operand reads (32 rows, one chunk) and the transposing reads
-// (rows R..R+3 and R+8..R+11, four chunks) of a plain layout hit the same
-// banks: on 64-element rows the plain layout made the dK/dV pass ~30% slower,
-// and 2(R mod 4) + (R/4 mod 2) was the fastest of the XOR patterns measured.
-// 128-element rows span every bank; there the swizzle sends rows R..R+3 to
-// four different 64-byte quarters of the row.
+// LDS layout of the Q and dO tiles of the dK/dV pass, staged by direct
+// global -> LDS copies: unpadded rows of D 16-bit elements (the copies land
+// whole 1 KB blocks, so rows cannot be padded), 16-byte chunk c of row R at
+// chunk position c ^ tile_swz(R). LDS serves a 16-byte read for 16
+// consecutive lanes per cycle and a transposing 8-byte read for 32, from 64
+// four-byte banks, so the two operand reads need:
+//  - row-per-lane reads (rows R..R+15 of an aligned block, one chunk each):
+//    the 16 rows on 16 different 16-byte bank groups;
+//  - transposing reads (rows R..R+3, R = 0 mod 4, four consecutive chunks
+//    from a multiple of 4): no bank shared by the four rows' chunks.
+// On 64-element rows (two rows per 64 banks) both hold for
+// tile_swz(R) = (R/4 mod 4) + 4 (R/2 mod 2): the rows of one parity in a
+// 16-row block take eight different XOR values, and rows R and R+2 differ in
+// the bit that moves a chunk to the other half of the row. 128-element rows
+// span every bank; there tile_swz(R) = 4 (R mod 4) + (R/4 mod 4) serves both.
+// rocprofv3's SQ_LDS_BANK_CONFLICT reads zero for both reads on both layouts.
+// (The register-staged K/V tiles of the forward and the dQ pass keep padded
+// rows, stride D + 8: conflict-free for row reads, two cycles per transposing
+// read, but with additive operand addresses. The swizzle there removed the
+// conflicts and cost more in address arithmetic than it saved.)
 template <int D>
 __device__ __forceinline__ int tile_swz(int row) {
-    return (D == 64) ? (((row & 3) << 1) | ((row >> 2) & 1)) : (((row & 3) << 2) | ((row >> 2) & 3));
+    return (D == 64) ? (((row >> 2) & 3) | ((row & 2) << 1)) : (((row & 3) << 2) | ((row >> 2) & 3));
 }
 template <int D>
 __device__ __forceinline__ int tile_off(int row, int col) {   // element offset of (row, col)
@@ -163,6 +173,18 @@ __device__ __forceinline__ f16x8 tile_tr_operand(const _Float16* tile, int row0,
     typedef short s16x8 __attribute__((ext_vector_type(8)));
     const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     return __builtin_bit_cast(f16x8, v);
+}
+
+// Float offset of 4-float chunk c of row r in a [rows][D] float32 exchange
+// area (the key-half merges at the end of the forward and the dQ pass): chunk
+// position c ^ (r mod 16). The 16 lanes of one LDS cycle write or read the
+// same chunk of 16 consecutive rows; with rows of 64 or 128 floats (whole
+// multiples of the 64 banks) they would all hit one bank group and serialise
+// 16-fold, the swizzle spreads them over all 16. Needs D >= 64.
+template <int D>
+__device__ __forceinline__ int merge_off(int r, int c) {
+    static_assert(D >= 64, "the swizzle spans 16 chunks");
+    return r * D + 4 * (c ^ (r & 15));
 }
 
 // Reductions across the two half-waves with v_permlane32_swap: swapping a
