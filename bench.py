@@ -7,6 +7,7 @@ rowsum(dO o O), dQ) and attn_bwd_dkdv (dK, dV) -- together exactly attn_bwd --
 all on torch's current stream, inputs resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa]
+    python bench.py --all-configs [--oracle]     # per-workload report, see below
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
 N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
@@ -17,6 +18,16 @@ for the dK/dV pass (S, dP, dV, dK) -- divided by its mean duration, measured
 with HIP events recorded on the launch stream around each launch in the timed
 region. cpu_baseline times the float64 oracle on this host on the same
 workload (fwd + bwd).
+
+--all-configs prints one JSON line per workload instead (tiny fp32 to the
+wide d=128 stress shape): median, p10 and p90 over R repetitions (after 10
+warm-up ones) of the forward, the backward and their sum, each repetition
+bracketed by HIP events on the launch stream, with TFLOP/s at the median
+against the published 2.5 PFLOP/s and against the dense bf16 matrix-core
+rate this GPU sustains in a register-only MFMA loop (measured first, as is
+the shader clock before and after). --oracle adds the float64 oracle's fwd and
+bwd wall times on this host for each workload (median of 3; once for the
+largest).
 """
 from __future__ import annotations
 
@@ -46,6 +57,9 @@ def parse():
     p.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.CONFIGS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-check", action="store_true")
+    p.add_argument("--all-configs", action="store_true",
+                   help="per-workload report (median/p10/p90) instead of the one-line benchmark")
+    p.add_argument("--oracle", action="store_true", help="with --all-configs: time the oracle per workload")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB device-to-device copy before the steps, so a "
                         "rocprofv3 --pmc run records FETCH_SIZE/WRITE_SIZE for a known byte count")
@@ -134,6 +148,111 @@ def sampled_check(s, inputs, out):
     return {f"max_abs_{kk}": float(vv) for kk, vv in err.items()}
 
 
+def shader_clocks():
+    """rocm-smi's current clocks (a child process), or None where it is unavailable."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=60)
+        card = next(iter(json.loads(r.stdout).values()))
+        return {k: v for k, v in card.items() if "sclk" in k.lower() or "mclk" in k.lower()}
+    except Exception as e:  # noqa: BLE001 -- the report goes on without clocks
+        return {"error": str(e)[:200]}
+
+
+def measured_mfma_peak():
+    """Dense bf16 matrix-core TFLOP/s of a register-only MFMA loop on this GPU."""
+    import ctypes
+    from tiled_causal_attention_amd import build as tca_build
+    L = ctypes.CDLL(tca_build.MEASURE_LIB)
+    L.tca_mfma_peak_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.tca_mfma_peak_launch.restype = ctypes.c_int
+    L.tca_mfma_peak_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    L.tca_mfma_peak_flops.restype = ctypes.c_double
+    blocks, iters = 256 * 8, 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        rc = L.tca_mfma_peak_launch(ctypes.c_void_p(out.data_ptr()), blocks, iters, st)
+        if rc != 0:
+            raise RuntimeError(f"mfma peak launch failed: {rc}")
+
+    for _ in range(3):
+        launch()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        launch()
+    e1.record()
+    torch.cuda.synchronize()
+    return L.tca_mfma_peak_flops(blocks, iters) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+
+
+def all_configs(args):
+    import numpy as np
+    report = {"report": "per-workload fwd/bwd timing", "clocks_before": shader_clocks()}
+    peak = measured_mfma_peak()
+    report["measured_mfma_bf16_tflops"] = peak
+    print(json.dumps(report), flush=True)
+    for name, s in workloads.CONFIGS.items():
+        inputs = workloads.make_inputs(s)
+        q, k, v, do = (t.cuda() for t in inputs)
+        o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=torch.float32, device=q.device)
+        lse = torch.empty((s.B, s.Hq, s.N), dtype=torch.float32, device=q.device)
+        dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device=q.device) for t in (q, k, v))
+        ws = tca.bwd_workspace(q, k)
+        causal, scale = bool(s.causal), s.scale
+        reps = 20 if s.N >= 8192 else 100
+
+        def one(ev):
+            ev[0].record()
+            tca.attn_fwd(q, k, v, causal, scale, out=(o, lse))
+            ev[1].record()
+            tca.attn_bwd_dq(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+            tca.attn_bwd_dkdv(q, k, v, o, lse, do, dq, dk, dv, ws, causal, scale)
+            ev[2].record()
+
+        for _ in range(10):
+            one([torch.cuda.Event(enable_timing=True) for _ in range(3)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        for ev in evs:
+            one(ev)
+        torch.cuda.synchronize()
+        fwd = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        bwd = np.array([e[1].elapsed_time(e[2]) for e in evs])
+        tot = fwd + bwd
+        stats = lambda a: {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+                           "p90_ms": float(np.percentile(a, 90))}
+        ff, fb = s.flops_fwd(), s.flops_bwd()
+        rec = {"workload": name, "B": s.B, "Hq": s.Hq, "Hkv": s.Hkv, "N": s.N, "d": s.d, "dtype": s.dtype,
+               "reps": reps, "fwd": stats(fwd), "bwd": stats(bwd), "fwd_bwd": stats(tot)}
+        for key, fl, arr in (("fwd", ff, fwd), ("bwd", fb, bwd), ("fwd_bwd", ff + fb, tot)):
+            tf = fl / (float(np.median(arr)) * 1e-3) / 1e12
+            rec[key].update({"tflops": tf, "pct_published_peak": 100 * tf / PEAK_MFMA_BF16_TFLOPS,
+                             "pct_measured_peak": 100 * tf / peak})
+        if args.oracle:
+            import oracle
+            runs = 1 if s.N >= 8192 else 3
+            tf_, tb_ = [], []
+            for i in range(runs):
+                print(f"oracle {name} run {i + 1}/{runs}", file=sys.stderr, flush=True)
+                t0 = time.perf_counter()
+                oracle.attn_fwd(*inputs[:3], s.causal, s.scale)
+                t1 = time.perf_counter()
+                oracle.attn_bwd(*inputs, s.causal, s.scale)
+                t2 = time.perf_counter()
+                tf_.append(t1 - t0)
+                tb_.append(t2 - t1)
+            rec["oracle"] = {"fwd_s": float(np.median(tf_)), "bwd_s": float(np.median(tb_)), "runs": runs,
+                             "threads": oracle.threads(),
+                             "gflops": (ff + fb) / (float(np.median(tf_)) + float(np.median(tb_))) / 1e9}
+        print(json.dumps(rec), flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    print(json.dumps({"clocks_after": shader_clocks()}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,6 +264,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
     tca.lib()  # fail loudly if the HIP library is missing
+    if args.all_configs:
+        all_configs(args)
+        return
 
     s = workloads.CONFIGS[args.workload]
     inputs = workloads.make_inputs(s)

@@ -17,6 +17,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtca.so")
+# the benchmark report's matrix-core throughput probe (not the attention library)
+MEASURE_SRC = os.path.join(HERE, "measure", "mfma_peak.hip")
+MEASURE_LIB = os.path.join(HERE, "libtca_measure.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -42,9 +45,9 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+def _compile(srcs, out: str, extra=(), verbose: bool = False) -> str:
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *sources(), "-o", tmp]
+    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -55,5 +58,60 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     return out
 
 
+def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
+    """The attention library (and, for the default output, the measurement probe)."""
+    _compile(sources(), out, extra, verbose)
+    if out == LIB:
+        _compile([MEASURE_SRC], MEASURE_LIB, extra, verbose)
+    return out
+
+
+def resource_usage() -> list:
+    """Per-kernel registers, LDS and occupancy as the compiler reports them
+    (hipcc -Rpass-analysis=kernel-resource-usage on the device code)."""
+    import re
+    rows, cur = [], None
+    for src in sources():
+        cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "-c", src,
+               "--offload-device-only", "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        for line in res.stderr.splitlines():
+            m = re.search(r"remark:\s+(.*?)\s+\[-Rpass", line)
+            if not m:
+                continue
+            key, _, val = m.group(1).partition(":")
+            if key.strip() == "Function Name":
+                cur = {"kernel": val.strip(), "source": os.path.basename(src)}
+                rows.append(cur)
+            elif cur is not None:
+                cur[key.strip()] = val.strip()
+    return rows
+
+
+def resource_usage_markdown() -> str:
+    import re
+
+    def short(n):   # tca::<name><D> from the mangled kernel name
+        m = re.match(r"_ZN3tca(\d+)", n)
+        if not m:
+            return n
+        ln = int(m.group(1))
+        t = re.match(r"I(f|t|DF16_)?Li(\d+)E", n[m.end() + ln:])
+        if not t:
+            return n[m.end():m.end() + ln]
+        ty = {"f": "float, ", "t": "bf16, ", "DF16_": "half, "}.get(t.group(1) or "", "")
+        return n[m.end():m.end() + ln] + f"<{ty}{t.group(2)}>"
+
+    out = ["| Kernel | Source | VGPRs | AGPRs | VGPR spills | LDS bytes per workgroup | Waves per SIMD |",
+           "|---|---|---|---|---|---|---|"]
+    for r in resource_usage():
+        out.append(f"| `{short(r['kernel'])}` | {r['source']} | {r.get('VGPRs')} | {r.get('AGPRs')} | "
+                   f"{r.get('VGPRs Spill')} | {r.get('LDS Size [bytes/block]')} | {r.get('Occupancy [waves/SIMD]')} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--resource-usage" in sys.argv:
+        print(resource_usage_markdown())
+    else:
+        print(build(verbose=True))
