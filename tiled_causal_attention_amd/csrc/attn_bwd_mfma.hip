@@ -30,37 +30,42 @@
 
 namespace tca {
 
-// dQ pass layout: a workgroup covers 64 query rows with 4 waves, 2 row blocks
-// of 32 rows x 2 key halves (wave (rb, kh) takes keys 32kh .. 32kh+31 of each
-// K/V tile); the two key halves' partial dQ are summed through LDS at the end.
+// dQ pass layout: a workgroup covers 16 NW query rows with NW waves, NW/2 row
+// blocks of 32 rows x 2 key halves (wave (rb, kh) takes keys 32kh .. 32kh+31 of
+// each K/V tile); the two key halves' partial dQ are summed through LDS at the
+// end. d = 64 uses 4 waves (64 rows, 3 workgroups per CU); d = 128 uses 8 waves
+// (128 rows): each wave stages half as many K/V chunks, which with D taken
+// from the workspace rather than held as a -D accumulator keeps it within 256
+// registers, i.e. two waves per SIMD instead of one.
 namespace bwdq {
-constexpr int NW = 4;            // waves per workgroup
-constexpr int BQ = 64;           // query rows per workgroup
+template <int D> constexpr int kWaves = (D == 128) ? 8 : 4;
+template <int D> constexpr int kThreads = 64 * kWaves<D>;
+template <int D> constexpr int kRows = 16 * kWaves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile
 constexpr int PAD = 8;
 }  // namespace bwdq
 
 // Global -> registers: the K and V chunks of one tile through buffer resources
 // over the head's N rows; voff is this thread's byte offset of chunk 0 in the
-// tile's first row. Thread tid owns chunks tid + 256u (a wave reads whole
-// rows); rows past the end of the sequence read as zero.
+// tile's first row. Thread tid owns chunks tid + T u, T threads (a wave reads
+// whole rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
 __device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
                                             __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        kreg[u] = buf_load16(kr, voff + u * 256 * 16);
-        vreg[u] = buf_load16(vr, voff + u * 256 * 16);
+        kreg[u] = buf_load16(kr, voff + u * bwdq::kThreads<D> * 16);
+        vreg[u] = buf_load16(vr, voff + u * bwdq::kThreads<D> * 16);
     }
 }
 
 // Registers -> LDS: K converted to fp16 rows, V kept as bf16 rows. kdst/vdst
 // point at this thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8)));
-// chunk u sits 256u / (D/8) rows further down.
+// chunk u sits T u / (D/8) rows further down (T threads).
 template <int D, int KCH>
 __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH],
                                              _Float16* kdst, bf16_t* vdst) {
-    constexpr int ROWS_PER_U = 256 / (D / 8);
+    constexpr int ROWS_PER_U = bwdq::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::PAD)) = bf16x8_to_f16x8(kreg[u]);
@@ -69,7 +74,7 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
 }
 
 template <int D>
-__global__ void __launch_bounds__(256, (D == 64) ? 3 : 1)
+__global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 1)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
               const float* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
@@ -77,9 +82,17 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
-    constexpr int CPR = D / 8, KCH = BC * CPR / 256;
-    __shared__ __attribute__((aligned(16))) _Float16 Ks[2][BC][LD];
-    __shared__ __attribute__((aligned(16))) bf16_t Vs[2][BC][LD];
+    constexpr int NT = kThreads<D>, BQ = kRows<D>, NRB = kWaves<D> / 2;
+    constexpr int CPR = D / 8, KCH = BC * CPR / NT;
+    // -D as the starting dP accumulator saves a subtraction per element but
+    // holds 16 more registers; at d = 128 the registers matter more
+    constexpr bool kNegDAcc = (D == 64);
+    // K and V tile buffers in one LDS block; after the loop it is the exchange
+    // area of the key halves' partial dQ (NRB row blocks of 32 x D floats)
+    constexpr int TILES_BYTES = 2 * 2 * BC * LD * 2, MERGE_BYTES = NRB * 32 * D * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[TILES_BYTES > MERGE_BYTES ? TILES_BYTES : MERGE_BYTES];
+    _Float16 (*Ks)[BC][LD] = reinterpret_cast<_Float16 (*)[BC][LD]>(smem);
+    bf16_t (*Vs)[BC][LD] = reinterpret_cast<bf16_t (*)[BC][LD]>(smem + 2 * BC * LD * 2);
 
     const int group = Hq / Hkv;
     const TileMap tm = map_workgroup(blockIdx.x, nqt, units, Hkv, group);
@@ -128,7 +141,6 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
     }
     const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
-    const f32x16 negD = f32x16{} - Di;   // -D_i in every accumulator of this lane's query column
     if (qok && h == 0 && khalf == 0) l2[bh * N + qi] = Li;
 
     u32x4 kreg[KCH], vreg[KCH];
@@ -158,7 +170,11 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         if (!causal || kw0 <= q0w + 31) {
             // ---- S^T = K Q^T and dP^T - D = V dO^T - D (rows: the wave's keys, permuted;
             // columns: queries): the dP product accumulates onto -D_i, so no subtraction follows
-            f32x16 s = f32x16{}, dp = negD;
+            f32x16 s = f32x16{}, dp;
+            if constexpr (kNegDAcc)
+                dp = f32x16{} - Di;   // -D_i in every accumulator of this lane's query column
+            else
+                dp = f32x16{};
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
                 const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
@@ -180,7 +196,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const float p = fast_exp2(fmaf(s[e], sl2, -Li));
-                s[e] = p * dp[e];   // dS = P (dP - D)
+                s[e] = kNegDAcc ? p * dp[e] : p * (dp[e] - Di);   // dS = P (dP - D)
             }
             // ---- dQ^T += K^T dS^T  (A: the wave's K rows read transposed; B: dS from registers)
 #pragma unroll
@@ -218,7 +234,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
     // after the last barrier) and store. Accumulator e of dim block x holds dim
     // 32x + 8(e/4) + 4h + e%4 of query qi.
-    float* xo = reinterpret_cast<float*>(&Ks[0][0][0]) + rb * (32 * D);   // [32 rows][D]
+    float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);   // [32 rows][D]
     if (khalf == 1) {
 #pragma unroll
         for (int x = 0; x < DB; ++x)
@@ -555,10 +571,10 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
 
 template <int D>
 static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
-    const int nqt = (a.N + bwdq::BQ - 1) / bwdq::BQ;
+    const int nqt = (a.N + bwdq::kRows<D> - 1) / bwdq::kRows<D>;
     const int units = a.B * a.Hkv;
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * a.B * a.Hq)), dim3(256), 0, st,
+    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
                        (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.o,
                        (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, a.dq,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units);
