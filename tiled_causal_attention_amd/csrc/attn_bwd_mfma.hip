@@ -501,64 +501,94 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             }
         }
         advance(cur);
-        // ---- end of a K/V tile: fixed-order reduction of the query sub-block partials
+        // ---- end of a K/V tile: combine the NQW query sub-blocks' partial dK, dV
         if (it + 1 == nitems || tile_of(cur) != tile) {
-            // Tree over the NQW query sub-blocks (fixed order -> deterministic):
-            // each round the upper half of the remaining sub-blocks writes its
-            // partials to LDS and the lower half adds them in registers; sub-block
-            // 0 ends with the full sums and stores dK (scaled) and dV rows.
-            // accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r
-#pragma unroll 1
-            for (int half = NQW / 2; half >= 1; half >>= 1) {
-                if (qw >= half && qw < 2 * half) {
-                    float* dst = &red[qw - half][0][0][0];
+            // Wave (kh, qw) owns accumulators e in [E qw, E qw + E) of both tensors (accumulator
+            // e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r). It hands every
+            // other owner its part through LDS, one (source, owner) block each, then adds the
+            // NQW - 1 blocks addressed to it in source order (fixed order: deterministic) and
+            // stores its keys. One exchange round; every wave shares the adds and the stores.
+            // A block is lane-major 16-byte chunks (16 lanes of a cycle hit 256 contiguous
+            // bytes: no bank conflicts). The blocks fill `red`, then (d = 64) this item's Q and
+            // dO buffers, which every wave has finished reading at the barrier below.
+            constexpr int E = 16 / NQW;                  // accumulators owned per wave
+            constexpr int BS = 2 * DB * E * 64;          // floats per block (16-byte chunks, 64 lanes)
+            constexpr int RED_FLOATS = (NQW / 2) * 2 * BC * D;
+            constexpr int QF = BQ * D / 2;               // floats in one staged Q (or dO) buffer
+            static_assert(2 * NQW * (NQW - 1) * BS <= RED_FLOATS + 2 * QF, "exchange blocks must fit");
+            float* const redf = &red[0][0][0][0];
+            float* const qf = reinterpret_cast<float*>(BUF ? Qs1 : Qs0);
+            float* const df = reinterpret_cast<float*>(BUF ? dOs1 : dOs0);
+            auto block = [&](int src, int owner) -> float* {
+                const int b = kh_ * NQW * (NQW - 1) + src * (NQW - 1) + (owner < src ? owner : owner - 1);
+                const int off = b * BS;
+                if (off < RED_FLOATS) return redf + off;
+                return (off - RED_FLOATS < QF) ? qf + (off - RED_FLOATS) : df + (off - RED_FLOATS - QF);
+            };
+            __syncthreads();
+            // chunk (t, x, j) of a block: tensor t (0 dK, 1 dV), dim block x, owner
+            // accumulators 4j .. 4j+3; chunk index (t DB + x) E/4 + j
+            constexpr int EQ = E / 4;
 #pragma unroll
-                    for (int x = 0; x < DB; ++x)
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int key = 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
-                            dst[(0 * BC + key) * D + 32 * x + r] = dka[x][e];
-                            dst[(1 * BC + key) * D + 32 * x + r] = dva[x][e];
-                        }
-                }
-                __syncthreads();
-                if (qw < half) {
-                    const float* src = &red[qw][0][0][0];
-#pragma unroll
-                    for (int x = 0; x < DB; ++x)
-#pragma unroll
-                        for (int e0 = 0; e0 < 16; e0 += 8) {
-                            // 16 loads in flight, then 16 adds (bounded register use)
-                            float tk[8], tv[8];
-#pragma unroll
-                            for (int e = e0; e < e0 + 8; ++e) {
-                                const int key = 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
-                                tk[e - e0] = src[(0 * BC + key) * D + 32 * x + r];
-                                tv[e - e0] = src[(1 * BC + key) * D + 32 * x + r];
-                            }
-#pragma unroll
-                            for (int e = e0; e < e0 + 8; ++e) {
-                                dka[x][e] += tk[e - e0];
-                                dva[x][e] += tv[e - e0];
-                            }
-                            __builtin_amdgcn_sched_barrier(0);
-                        }
-                }
-                __syncthreads();
-            }
-            if (qw == 0) {
+            for (int o = 0; o < NQW; ++o) {
+                if (o == qw) continue;
+                float* const dst = block(qw, o);
 #pragma unroll
                 for (int x = 0; x < DB; ++x)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if (key < N) {
-                            const size_t off = kvoff + (size_t)key * D + 32 * x + r;
-                            dk[off] = dka[x][e] * scale;
-                            dv[off] = dva[x][e];
+                    for (int j = 0; j < EQ; ++j) {
+                        const int e = E * o + 4 * j;
+                        *reinterpret_cast<f32x4*>(dst + (((0 * DB + x) * EQ + j) * 64 + lane) * 4) =
+                            f32x4{dka[x][e], dka[x][e + 1], dka[x][e + 2], dka[x][e + 3]};
+                        *reinterpret_cast<f32x4*>(dst + (((1 * DB + x) * EQ + j) * 64 + lane) * 4) =
+                            f32x4{dva[x][e], dva[x][e + 1], dva[x][e + 2], dva[x][e + 3]};
+                    }
+            }
+            // own part (wave-uniform select: register indices stay compile-time)
+            float sk[DB][E], sv[DB][E];
+#pragma unroll
+            for (int x = 0; x < DB; ++x)
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    sk[x][i] = dka[x][i];
+                    sv[x][i] = dva[x][i];
+#pragma unroll
+                    for (int o = 1; o < NQW; ++o)
+                        if (qw == o) {
+                            sk[x][i] = dka[x][E * o + i];
+                            sv[x][i] = dva[x][E * o + i];
+                        }
+                }
+            __syncthreads();
+#pragma unroll
+            for (int src = 0; src < NQW; ++src) {
+                if (src == qw) continue;
+                const float* const sb = block(src, qw);
+#pragma unroll
+                for (int x = 0; x < DB; ++x)
+#pragma unroll
+                    for (int j = 0; j < EQ; ++j) {
+                        const f32x4 ak = *reinterpret_cast<const f32x4*>(sb + (((0 * DB + x) * EQ + j) * 64 + lane) * 4);
+                        const f32x4 av = *reinterpret_cast<const f32x4*>(sb + (((1 * DB + x) * EQ + j) * 64 + lane) * 4);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            sk[x][4 * j + i] += ak[i];
+                            sv[x][4 * j + i] += av[i];
                         }
                     }
             }
+#pragma unroll
+            for (int x = 0; x < DB; ++x)
+#pragma unroll
+                for (int i = 0; i < E; ++i) {
+                    const int e = E * qw + i;
+                    const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
+                    if (key < N) {
+                        const size_t off = kvoff + (size_t)key * D + 32 * x + r;
+                        dk[off] = sk[x][i] * scale;
+                        dv[off] = sv[x][i];
+                    }
+                }
         }
         wait_vmem_all();   // the copies land before the barrier that publishes them
         __syncthreads();
