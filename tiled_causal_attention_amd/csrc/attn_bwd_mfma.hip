@@ -109,6 +109,15 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = scale * kLog2e;
 
+    // The first K/V tile's loads and this row's LSE go out before the Q, dO and O
+    // rows, so their latency overlaps the D computation instead of following it.
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (uint32_t)N * D * 2);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)N * D * 2);
+    const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a tile
+    u32x4 kreg[KCH], vreg[KCH];
+    bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
+    const float lse_i = lse[bh * N + qc];
+
     // Q (fp16) and dO (bf16) rows of this lane's query as B operands, and D_i
     f16x8 qb[DC];
     bf16x8 db[DC];
@@ -140,10 +149,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
         if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
     }
-    const float Li = qok ? lse[bh * N + qi] * kLog2e : 0.f;
+    const float Li = qok ? lse_i * kLog2e : 0.f;
     if (qok && h == 0 && khalf == 0) l2[bh * N + qi] = Li;
 
-    u32x4 kreg[KCH], vreg[KCH];
     f32x16 dqa[DB];
 #pragma unroll
     for (int x = 0; x < DB; ++x) dqa[x] = f32x16{};
@@ -153,13 +161,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const int ntile = (kend + BC - 1) / BC;
     const int krow_a = perm32(r);
 
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)N * D * 2);
-    const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a tile
     const int st_off = (tid / CPR) * LD + (tid % CPR) * 8;           // LDS slot of chunk 0 (elements)
     constexpr int TBUF = BC * LD;                                      // elements per LDS tile buffer
 
-    bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
     bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
     if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
