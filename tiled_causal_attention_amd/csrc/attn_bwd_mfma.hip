@@ -108,6 +108,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = scale * kLog2e;
+    __shared__ float dsh[BQ];   // D of each row, from key half 0
 
     // The first K/V tile's loads and this row's LSE go out before the Q, dO and O
     // rows, so their latency overlaps the D computation instead of following it.
@@ -118,7 +119,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
     const float lse_i = lse[bh * N + qc];
 
-    // Q (fp16) and dO (bf16) rows of this lane's query as B operands, and D_i
+    // Q (fp16) and dO (bf16) rows of this lane's query as B operands, and D_i:
+    // key half 0 loads the O rows and computes D, key half 1 takes it from LDS
+    // after the prologue barrier (half the O traffic at workgroup start)
     f16x8 qb[DC];
     bf16x8 db[DC];
     float Di;
@@ -126,28 +129,36 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         const bf16_t* qrow = q + (bh * N + qc) * D + 8 * h;
         const bf16_t* drow = dout + (bh * N + qc) * D + 8 * h;
         const float* orow = o + (bh * N + qc) * D + 8 * h;
-        float part = 0.f;
+        u32x4 dvr[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-            const u32x4 dv = *reinterpret_cast<const u32x4*>(drow + 16 * c);
-            const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
-            const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
+            dvr[c] = *reinterpret_cast<const u32x4*>(drow + 16 * c);
             const u32x4 qh16 = bf16x8_to_f16x8(qv);
             qb[c] = qok ? __builtin_bit_cast(f16x8, qh16) : f16x8{};
-            db[c] = qok ? __builtin_bit_cast(bf16x8, dv) : bf16x8{};
-
-            part = fmaf(bf16_lo(dv.x), o0[0], part);
-            part = fmaf(bf16_hi(dv.x), o0[1], part);
-            part = fmaf(bf16_lo(dv.y), o0[2], part);
-            part = fmaf(bf16_hi(dv.y), o0[3], part);
-            part = fmaf(bf16_lo(dv.z), o1[0], part);
-            part = fmaf(bf16_hi(dv.z), o1[1], part);
-            part = fmaf(bf16_lo(dv.w), o1[2], part);
-            part = fmaf(bf16_hi(dv.w), o1[3], part);
+            db[c] = qok ? __builtin_bit_cast(bf16x8, dvr[c]) : bf16x8{};
         }
-        Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
-        if (qok && h == 0 && khalf == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
+        Di = 0.f;
+        if (khalf == 0) {
+            float part = 0.f;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                const u32x4 dv = dvr[c];
+                const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
+                const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
+                part = fmaf(bf16_lo(dv.x), o0[0], part);
+                part = fmaf(bf16_hi(dv.x), o0[1], part);
+                part = fmaf(bf16_lo(dv.y), o0[2], part);
+                part = fmaf(bf16_hi(dv.y), o0[3], part);
+                part = fmaf(bf16_lo(dv.z), o1[0], part);
+                part = fmaf(bf16_hi(dv.z), o1[1], part);
+                part = fmaf(bf16_lo(dv.w), o1[2], part);
+                part = fmaf(bf16_hi(dv.w), o1[3], part);
+            }
+            Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
+            if (h == 0) dsh[32 * rb + r] = Di;
+            if (qok && h == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
+        }
     }
     const float Li = qok ? lse_i * kLog2e : 0.f;
     if (qok && h == 0 && khalf == 0) l2[bh * N + qi] = Li;
@@ -167,6 +178,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
     if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
+    if (khalf == 1) Di = dsh[32 * rb + r];
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
