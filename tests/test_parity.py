@@ -154,6 +154,14 @@ def test_small_shapes(B, Hq, Hkv, N, d, dtype, causal):
     full_parity(s, poison=True)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(2, 16, 4, 512, 64), (1, 8, 8, 384, 128), (3, 12, 4, 448, 64)])
+def test_noncausal_midsize(B, Hq, Hkv, N, d):
+    # non-causal at sizes that span many tiles: (2, 16, 4) gives 8 (batch, KV head)
+    # units, the count at which workgroups of a unit share an XCD; (3, 12, 4) gives 12
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype="bf16", seed=700 + N + d, causal=0)
+    full_parity(s, poison=True)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_stress_peaked_softmax_small(d):
     # the wide-head stress distribution (Q, K ~ N(0, 3^2)) at a size the full oracle covers
