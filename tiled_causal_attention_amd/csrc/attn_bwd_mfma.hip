@@ -282,23 +282,32 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 // every workgroup does the same amount of work -- or one tile otherwise. Its
 // waves are NKH = 2 key halves x NQW query sub-blocks: wave (kh, qw) handles
 // keys 32kh .. 32kh+31 of the tile and rows 32qw .. 32qw+31 of each staged
-// query tile (BQ = 32 NQW rows), accumulating partial dK, dV for its keys in
-// registers. At the end of a K/V tile the NQW partials of each key half are
-// summed in LDS in a fixed order (deterministic) and written out.
+// query tile (BQ = 32 NQW rows).
 //
 //   S  = Q K^T, dP = dO V^T  (rows: queries, permuted; columns: keys -> one key
 //                             per lane, so P and dS are A operands in place)
 //   dV += P^T dO, dK += dS^T Q (B operands: dO, Q tiles read transposed)
+//
+// d = 64: each wave accumulates partial dK and dV for its keys over its own
+// rows; at the end of a K/V tile the NQW partials of each key half are summed
+// in LDS in a fixed order (deterministic) and written out.
+// d = 128 (split by tensor): holding K, V, dK and dV in one wave takes ~490
+// registers, one wave per SIMD. Instead wave (kh, 0) accumulates only dV and
+// wave (kh, 1) only dK, each over all 64 rows of the query tile: each wave keeps
+// the fp16 operand it needs of its own 32-row block (P or dS) and passes the
+// other one to its partner through 8 KB of LDS, one extra barrier per item. That
+// is 256 registers and 73 KB of LDS: two workgroups per CU, two waves per SIMD
+// from different workgroups, and no end-of-tile exchange.
 namespace bwdkv {
 constexpr int BC = 64;
 template <int D> struct Cfg;
 template <> struct Cfg<64> { static constexpr int NQW = 4; };   // 8 waves, 128-row query tiles
-template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles
+template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles, 2 per CU
 
 }  // namespace bwdkv
 
 template <int D>
-__global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, 1)
+__global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, (D == 128) ? 2 : 1)
 bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
                 const float* __restrict__ l2, const float* __restrict__ delta,
@@ -319,7 +328,12 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     __shared__ __attribute__((aligned(16))) _Float16 Qs0[BQ * D], Qs1[BQ * D];
     __shared__ __attribute__((aligned(16))) _Float16 dOs0[BQ * D], dOs1[BQ * D];
     __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
-    __shared__ __attribute__((aligned(16))) float red[NQW / 2][2][BC][D];   // dK, dV partial sums
+    // d = 64: partial-sum exchange area. d = 128 (split by tensor): wave (kh, 0)
+    // accumulates dV, wave (kh, 1) dK, each over the whole query tile; they trade
+    // the fp16 dS (from qw 0) and P (from qw 1) operands of their blocks here
+    constexpr bool kSplit = (D == 128);
+    __shared__ __attribute__((aligned(16))) float red[kSplit ? 4 : (NQW / 2) * 2 * BC * D];
+    __shared__ __attribute__((aligned(16))) _Float16 xch[kSplit ? 2 * 2 * 2 * 64 * 8 : 8];   // [kh][qw][c2][lane][8]
 
     const int group = Hq / Hkv;
     // all workgroups of one (batch, KV head) unit on one XCD (w mod 8), so the
@@ -403,7 +417,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     };
 
     f16x8 kb[DC], vb[DC];
-    f32x16 dka[DB], dva[DB];
+    f32x16 dka[DB], dva[kSplit ? 1 : DB];   // split: dka is this wave's one tensor
     int cur_tile = -1;
     Cursor cur = {0, 0, fa}, ld = cur;
 
@@ -436,9 +450,10 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 vb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(vrow + 16 * c)));
             }
 #pragma unroll
-            for (int x = 0; x < DB; ++x) {
-                dka[x] = f32x16{};
-                dva[x] = f32x16{};
+            for (int x = 0; x < DB; ++x) dka[x] = f32x16{};
+            if constexpr (!kSplit) {
+#pragma unroll
+                for (int x = 0; x < DB; ++x) dva[x] = f32x16{};
             }
         }
         // stage the next item into the other buffer (free since the last barrier)
@@ -451,6 +466,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
         }
         const int q0 = qt * BQ + 32 * qw;        // first query row of this wave's block
         const bool live = !causal || q0 + 31 >= kw0;
+        f16x8 own[kSplit ? 2 : 1];
         if (live) {
             // ---- S = Q K^T, dP - D = dO V^T - D (accumulator e: query q0 + 16(e/8) + 8h + e%8,
             // key kw): the row statistic arrives as -D, and the dP product accumulates onto it
@@ -500,25 +516,74 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                     dp[e] = p * dp[e];   // dS = P (dP - D)
                 }
             }
-            // ---- dV += P^T dO, dK += dS^T Q (B: dO, Q tiles read transposed, rows = queries)
+            if constexpr (kSplit) {
+                // keep this wave's own operand (qw 0: P, qw 1: dS), hand the other one to
+                // the partner wave as lane-major 16-byte chunks (conflict-free)
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                const f16x8 pa = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
-                                          s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
-                const f16x8 da = to_f16x8(dp[8 * c2 + 0], dp[8 * c2 + 1], dp[8 * c2 + 2], dp[8 * c2 + 3],
-                                          dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const f16x8 pa = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                              s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+                    const f16x8 da = to_f16x8(dp[8 * c2 + 0], dp[8 * c2 + 1], dp[8 * c2 + 2], dp[8 * c2 + 3],
+                                              dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
+                    own[c2] = qw ? da : pa;
+                    *reinterpret_cast<f16x8*>(xch + (((kh_ * 2 + qw) * 2 + c2) * 64 + lane) * 8) = qw ? pa : da;
+                }
+            } else {
+                // ---- dV += P^T dO, dK += dS^T Q (B: dO, Q tiles read transposed, rows = queries)
 #pragma unroll
-                for (int x = 0; x < DB; ++x) {
-                    const f16x8 bo = tile_tr_operand<D>(dOt, 32 * qw + 16 * c2, 32 * x, h, r);
-                    const f16x8 bq = tile_tr_operand<D>(Qt, 32 * qw + 16 * c2, 32 * x, h, r);
-                    dva[x] = mfma_f16(pa, bo, dva[x]);
-                    dka[x] = mfma_f16(da, bq, dka[x]);
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const f16x8 pa = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
+                                              s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
+                    const f16x8 da = to_f16x8(dp[8 * c2 + 0], dp[8 * c2 + 1], dp[8 * c2 + 2], dp[8 * c2 + 3],
+                                              dp[8 * c2 + 4], dp[8 * c2 + 5], dp[8 * c2 + 6], dp[8 * c2 + 7]);
+#pragma unroll
+                    for (int x = 0; x < DB; ++x) {
+                        const f16x8 bo = tile_tr_operand<D>(dOt, 32 * qw + 16 * c2, 32 * x, h, r);
+                        const f16x8 bq = tile_tr_operand<D>(Qt, 32 * qw + 16 * c2, 32 * x, h, r);
+                        dva[x] = mfma_f16(pa, bo, dva[x]);
+                        dka[x] = mfma_f16(da, bq, dka[x]);
+                    }
+                }
+            }
+        }
+        if constexpr (kSplit) {
+            // ---- qw 0: dV += P^T dO, qw 1: dK += dS^T Q over both 32-row blocks of the
+            // query tile, own block first (B: dO or Q tile read transposed, rows = queries)
+            __syncthreads();
+            const _Float16* Bt = qw ? Qt : dOt;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                const int qb = pass ? 1 - qw : qw;
+                if (pass && !(!causal || qt * BQ + 32 * qb + 31 >= kw0)) break;
+                if (!pass && !live) continue;
+#pragma unroll
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    const f16x8 a = pass ? *reinterpret_cast<const f16x8*>(xch + (((kh_ * 2 + qb) * 2 + c2) * 64 + lane) * 8)
+                                         : own[c2];
+#pragma unroll
+                    for (int x = 0; x < DB; ++x)
+                        dka[x] = mfma_f16(a, tile_tr_operand<D>(Bt, 32 * qb + 16 * c2, 32 * x, h, r), dka[x]);
                 }
             }
         }
         advance(cur);
+        if constexpr (kSplit) {
+            // ---- end of a K/V tile: each wave holds its tensor's final values for its 32 keys
+            // (accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r)
+            if (it + 1 == nitems || tile_of(cur) != tile) {
+                float* const dst = qw ? dk : dv;
+                const float f = qw ? scale : 1.0f;
+#pragma unroll
+                for (int x = 0; x < DB; ++x)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = kw0 + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key < N) dst[kvoff + (size_t)key * D + 32 * x + r] = dka[x][e] * f;
+                    }
+            }
+        }
         // ---- end of a K/V tile: combine the NQW query sub-blocks' partial dK, dV
-        if (it + 1 == nitems || tile_of(cur) != tile) {
+        else if (it + 1 == nitems || tile_of(cur) != tile) {
             // Wave (kh, qw) owns accumulators e in [E qw, E qw + E) of both tensors (accumulator
             // e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r). It hands every
             // other owner its part through LDS, one (source, owner) block each, then adds the
@@ -532,7 +597,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             constexpr int RED_FLOATS = (NQW / 2) * 2 * BC * D;
             constexpr int QF = BQ * D / 2;               // floats in one staged Q (or dO) buffer
             static_assert(2 * NQW * (NQW - 1) * BS <= RED_FLOATS + 2 * QF, "exchange blocks must fit");
-            float* const redf = &red[0][0][0][0];
+            float* const redf = red;
             float* const qf = reinterpret_cast<float*>(BUF ? Qs1 : Qs0);
             float* const df = reinterpret_cast<float*>(BUF ? dOs1 : dOs0);
             auto block = [&](int src, int owner) -> float* {
