@@ -4,14 +4,18 @@
 // workgroup per query tile; for each K/V tile: stage it on chip, Q*K^T, online
 // softmax, accumulate the output), re-shaped for CDNA4:
 //
-//  * A workgroup covers 64 query rows with 4 waves (d = 64) or 128 rows with 8
-//    waves (d = 128): row blocks of 32 rows x 2 key halves. Wave (rb, kh) takes
-//    keys 32kh .. 32kh+31 of every K/V tile
-//    for its 32 rows and runs its own online softmax over them; the two key
+//  * d = 64: a workgroup covers 64 query rows with 4 waves, row blocks of 32
+//    rows x 2 key halves. Wave (rb, kh) takes keys 32kh .. 32kh+31 of every K/V
+//    tile for its 32 rows and runs its own online softmax over them; the two key
 //    halves of a row block are merged once, through LDS, at the end. Splitting
 //    the keys halves the serial work each wave does per tile, which is what
 //    bounds short-sequence shapes (the last query tile's walk over all K/V
 //    tiles), and doubles the waves available to hide latency.
+//    d = 128: a workgroup covers 128 rows with 4 waves, each taking all 64 keys
+//    of a tile for its 32 rows (no merge). Its ~190 registers allow two such
+//    workgroups per CU, so the two waves of a SIMD belong to different
+//    workgroups and do not wait at the same barriers (an 8-wave workgroup with
+//    key halves needs 155 registers, which fits only one per CU).
 //  * Each wave keeps its Q rows in registers as the B operand of
 //    S^T = K * Q^T, so the score accumulator holds one query per lane
 //    (lane = 32h + r -> query r): the row max and row sum are in-lane
@@ -47,14 +51,16 @@
 namespace tca {
 
 namespace fwd {
-// Waves per workgroup: kWaves/2 row blocks of 32 query rows x 2 key halves. At
-// d = 128 a K/V tile is twice the bytes, so it is shared by 8 waves (128 query
-// rows: half the staging per wave, measured -10% on a long d = 128 shape); at
-// d = 64 the causal N = 1024 shape runs faster with 4 waves (64 rows), whose
-// twice as many workgroups leave a shorter tail.
-template <int D> constexpr int kWaves = (D == 128) ? 8 : 4;
+// Waves per workgroup: 4, as kWaves/kKeyHalves row blocks of 32 query rows x
+// kKeyHalves key parts. d = 64: 2 key halves (64 rows): on the causal N = 1024
+// shape 64-row workgroups (twice as many) leave a shorter tail than 128-row
+// ones. d = 128: one wave per row block takes the whole tile (128 rows), so a
+// K/V tile still serves 128 rows and two workgroups share a CU: 7-8% faster
+// than 8-wave workgroups with key halves, which fit only one per CU.
+template <int D> constexpr int kWaves = 4;
+template <int D> constexpr int kKeyHalves = (D == 128) ? 1 : 2;   // waves sharing a row block
 template <int D> constexpr int kThreads = 64 * kWaves<D>;
-template <int D> constexpr int kRows = 16 * kWaves<D>;   // query rows per workgroup
+template <int D> constexpr int kRows = 32 * kWaves<D> / kKeyHalves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile (32 per key half)
 constexpr int PAD = 8;           // 16-bit elements of row padding (16 bytes)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
@@ -89,7 +95,7 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
 }
 
 template <int D>
-__global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 1)
+__global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
                 int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
@@ -100,7 +106,10 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     constexpr int CPR = D / 8;          // 16-byte chunks per row
     constexpr int NT = kThreads<D>;     // threads
     constexpr int BR = kRows<D>;        // query rows per workgroup
-    constexpr int NRB = kWaves<D> / 2;  // row blocks
+    constexpr int NKH = kKeyHalves<D>;  // key parts per tile (one wave each)
+    constexpr int NRB = kWaves<D> / NKH;  // row blocks
+    constexpr int KPW = BC / NKH;       // keys of a tile per wave
+    constexpr int KB = KPW / 32;        // 32-key blocks per wave
     constexpr int KCH = BC * CPR / NT;  // chunks per thread per tensor per tile
     // K and V tile buffers, carved from one LDS block: after the loop the whole
     // block is the merge area of the key halves (NRB row blocks of 32 x D floats)
@@ -115,7 +124,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const size_t bh = (size_t)tm.b * Hq + hq;
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
-    const int rb = w >> 1, khalf = w & 1;  // row block, key half
+    const int rb = (NKH == 2) ? (w >> 1) : w, khalf = (NKH == 2) ? (w & 1) : 0;   // row block, key half
     const int q0w = tm.qt * BR + 32 * rb;  // first query row of this wave
     const int qi = q0w + r;                // this lane's query row
     const bf16_t* qh = q + bh * N * D;
@@ -167,25 +176,41 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
-        const int kw0 = k0 + 32 * khalf;        // first key of this wave's half
+        const int kw0 = k0 + KPW * khalf;       // first key of this wave's part of the tile
         const bool active = !causal || kw0 <= q0w + 31;
         if (active) {
-            // ---- S^T = K * Q^T  (rows: this wave's 32 keys, permuted; columns: its queries)
-            f32x16 s = f32x16{};
+            // a wave with two 32-key blocks (d = 128) skips the second one where it lies wholly
+            // past the diagonal (the mask below then leaves it at -inf)
+            const bool act1 = (KB > 1) && (!causal || kw0 + 32 <= q0w + 31);
+            // ---- S^T = K * Q^T  (rows: 32 keys per block, permuted; columns: this wave's queries)
+            f32x16 s[KB];
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
-                s = mfma_bf16(a, qb[c], s);
+            for (int kb = 0; kb < KB; ++kb) {
+                s[kb] = f32x16{};
+                if (kb > 0 && !act1) continue;
+#pragma unroll
+                for (int c = 0; c < DC; ++c) {
+                    const bf16x8 a =
+                        *reinterpret_cast<const bf16x8*>(&Ks[buf][KPW * khalf + 32 * kb + krow_a][16 * c + 8 * h]);
+                    s[kb] = mfma_bf16(a, qb[c], s[kb]);
+                }
             }
-            // ---- mask: only tiles crossing the diagonal or the end of the sequence
-            if ((kw0 + 32 > N) || (causal && kw0 + 31 > q0w)) {
-                const int lim = lim_row - kw0;
+            // ---- mask: only blocks crossing the diagonal or the end of the sequence
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    s[e] = (16 * (e >> 3) + (e & 7) <= lim) ? s[e] : -INFINITY;
+            for (int kb = 0; kb < KB; ++kb) {
+                const int kwb = kw0 + 32 * kb;
+                if ((kwb + 32 > N) || (causal && kwb + 31 > q0w)) {
+                    const int lim = lim_row - kwb;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        s[kb][e] = (16 * (e >> 3) + (e & 7) <= lim) ? s[kb][e] : -INFINITY;
+                }
             }
             // ---- online softmax with lazy rescaling (log2 domain)
-            const float mt = max_halves(max16(s)) * sl2;
+            float mx = max16(s[0]);
+#pragma unroll
+            for (int kb = 1; kb < KB; ++kb) mx = vmax(mx, max16(s[kb]));
+            const float mt = max_halves(mx) * sl2;
             if (__any(mt > m_s + kTau)) {
                 const float m_new = vmax(m_s, mt);
                 const float alpha = fast_exp2(m_s - m_new);
@@ -197,23 +222,28 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 m_s = m_new;
             }
             const float mb = m_s;
-            // ---- P (fp16) and O^T += V^T * P^T over the wave's 32 keys
+            // ---- P (fp16) and O^T += V^T * P^T over the wave's keys
 #pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                float p[8];
+            for (int kb = 0; kb < KB; ++kb) {
+                if (kb > 0 && !act1) continue;
 #pragma unroll
-                for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[8 * c2 + t], sl2, -mb));
-                uint32_t pk[4];
+                for (int c2 = 0; c2 < 2; ++c2) {
+                    float p[8];
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    pk[t] = pack_f16(p[2 * t], p[2 * t + 1]);
-                    l_run = add_f16_pair(pk[t], l_run);
-                }
-                const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+                    for (int t = 0; t < 8; ++t) p[t] = fast_exp2(fmaf(s[kb][8 * c2 + t], sl2, -mb));
+                    uint32_t pk[4];
 #pragma unroll
-                for (int x = 0; x < DB; ++x) {
-                    const f16x8 a = lds_tr_operand(&Vs[buf][0][0], LD, 32 * khalf + 16 * c2, 32 * x, h, r);
-                    oacc[x] = mfma_f16(a, pb, oacc[x]);
+                    for (int t = 0; t < 4; ++t) {
+                        pk[t] = pack_f16(p[2 * t], p[2 * t + 1]);
+                        l_run = add_f16_pair(pk[t], l_run);
+                    }
+                    const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+                    for (int x = 0; x < DB; ++x) {
+                        const f16x8 a =
+                            lds_tr_operand(&Vs[buf][0][0], LD, KPW * khalf + 32 * kb + 16 * c2, 32 * x, h, r);
+                        oacc[x] = mfma_f16(a, pb, oacc[x]);
+                    }
                 }
             }
         }
@@ -224,44 +254,60 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();
     }
 
-    // ---- epilogue: merge the two key halves of each row block through LDS
-    // (the K tile buffers are free after the loop's last barrier), normalise,
-    // store O (fp32) and LSE (natural log). Accumulator e of dim block x holds
-    // dim 32x + 8(e/4) + 4h + e%4 of query qi.
+    // ---- epilogue: normalise, store O (fp32) and LSE (natural log). Accumulator e
+    // of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of query qi. With two key
+    // halves, they are first merged through LDS (the K tile buffers are free after
+    // the loop's last barrier).
     float l_tot = sum_halves(l_run);
-    float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);             // [32 rows][D]
-    float* xs = reinterpret_cast<float*>(smem) + NRB * 32 * D + rb * 64;    // m[32], l[32]
-    if (khalf == 1) {
+    if constexpr (NKH == 1) {
+        if (qi < N) {
+            const float inv = 1.f / l_tot;
+            float* orow = o + (bh * N + qi) * D;
 #pragma unroll
-        for (int x = 0; x < DB; ++x)
+            for (int x = 0; x < DB; ++x)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
-                    f32x4{oacc[x][4 * a4 + 0], oacc[x][4 * a4 + 1], oacc[x][4 * a4 + 2], oacc[x][4 * a4 + 3]};
-        if (h == 0) {
-            xs[r] = m_s;
-            xs[32 + r] = l_tot;
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 val = {oacc[x][4 * a4 + 0] * inv, oacc[x][4 * a4 + 1] * inv,
+                                       oacc[x][4 * a4 + 2] * inv, oacc[x][4 * a4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                }
+            if (h == 0) lse[bh * N + qi] = (m_s + __log2f(l_tot)) * kLn2;
         }
-    }
-    __syncthreads();
-    if (khalf == 0 && qi < N) {
-        const float m1 = xs[r], l1 = xs[32 + r];
-        const float m = vmax(m_s, m1);                // key half 0 always sees key 0
-        const float a0 = fast_exp2(m_s - m), a1 = fast_exp2(m1 - m);
-        const float l = l_tot * a0 + l1 * a1;
-        const float inv = 1.f / l;
-        const float c0 = a0 * inv, c1 = a1 * inv;
-        float* orow = o + (bh * N + qi) * D;
+    } else {
+        float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);             // [32 rows][D]
+        float* xs = reinterpret_cast<float*>(smem) + NRB * 32 * D + rb * 64;    // m[32], l[32]
+        if (khalf == 1) {
 #pragma unroll
-        for (int x = 0; x < DB; ++x)
+            for (int x = 0; x < DB; ++x)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
-                const f32x4 val = {oacc[x][4 * a4 + 0] * c0 + o1[0] * c1, oacc[x][4 * a4 + 1] * c0 + o1[1] * c1,
-                                   oacc[x][4 * a4 + 2] * c0 + o1[2] * c1, oacc[x][4 * a4 + 3] * c0 + o1[3] * c1};
-                *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                for (int a4 = 0; a4 < 4; ++a4)
+                    *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
+                        f32x4{oacc[x][4 * a4 + 0], oacc[x][4 * a4 + 1], oacc[x][4 * a4 + 2], oacc[x][4 * a4 + 3]};
+            if (h == 0) {
+                xs[r] = m_s;
+                xs[32 + r] = l_tot;
             }
-        if (h == 0) lse[bh * N + qi] = (m + __log2f(l)) * kLn2;
+        }
+        __syncthreads();
+        if (khalf == 0 && qi < N) {
+            const float m1 = xs[r], l1 = xs[32 + r];
+            const float m = vmax(m_s, m1);                // key half 0 always sees key 0
+            const float a0 = fast_exp2(m_s - m), a1 = fast_exp2(m1 - m);
+            const float l = l_tot * a0 + l1 * a1;
+            const float inv = 1.f / l;
+            const float c0 = a0 * inv, c1 = a1 * inv;
+            float* orow = o + (bh * N + qi) * D;
+#pragma unroll
+            for (int x = 0; x < DB; ++x)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
+                    const f32x4 val = {oacc[x][4 * a4 + 0] * c0 + o1[0] * c1, oacc[x][4 * a4 + 1] * c0 + o1[1] * c1,
+                                       oacc[x][4 * a4 + 2] * c0 + o1[2] * c1, oacc[x][4 * a4 + 3] * c0 + o1[3] * c1};
+                    *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                }
+            if (h == 0) lse[bh * N + qi] = (m + __log2f(l)) * kLn2;
+        }
     }
 }
 
