@@ -30,17 +30,19 @@
 
 namespace tca {
 
-// dQ pass layout: a workgroup covers 16 NW query rows with NW waves, NW/2 row
-// blocks of 32 rows x 2 key halves (wave (rb, kh) takes keys 32kh .. 32kh+31 of
-// each K/V tile); the two key halves' partial dQ are summed through LDS at the
-// end. d = 64 uses 4 waves (64 rows, 3 workgroups per CU); d = 128 uses 8 waves
-// (128 rows): each wave stages half as many K/V chunks, which with D taken
-// from the workspace rather than held as a -D accumulator keeps it within 256
-// registers, i.e. two waves per SIMD instead of one.
+// dQ pass layout: 4 waves per workgroup. d = 64: 64 query rows, row blocks of 32
+// rows x 2 key halves (wave (rb, kh) takes keys 32kh .. 32kh+31 of each K/V
+// tile); the two key halves' partial dQ are summed through LDS at the end; 3
+// workgroups per CU. d = 128: 128 rows, one wave per row block taking both
+// 32-key blocks of each tile in turn (P comes from the saved LSE, so the blocks
+// are independent), no merge; with D taken from the workspace rather than held
+// as a -D accumulator it stays within 256 registers, and two workgroups share a
+// CU, so the two waves of a SIMD do not wait at the same barriers.
 namespace bwdq {
-template <int D> constexpr int kWaves = (D == 128) ? 8 : 4;
+template <int D> constexpr int kWaves = 4;
+template <int D> constexpr int kKeyHalves = (D == 128) ? 1 : 2;   // waves sharing a row block
 template <int D> constexpr int kThreads = 64 * kWaves<D>;
-template <int D> constexpr int kRows = 16 * kWaves<D>;   // query rows per workgroup
+template <int D> constexpr int kRows = 32 * kWaves<D> / kKeyHalves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile
 constexpr int PAD = 8;
 }  // namespace bwdq
@@ -74,7 +76,7 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
 }
 
 template <int D>
-__global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 1)
+__global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 2)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
               const float* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
@@ -82,7 +84,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
-    constexpr int NT = kThreads<D>, BQ = kRows<D>, NRB = kWaves<D> / 2;
+    constexpr int NKH = kKeyHalves<D>;   // key parts per tile (one wave each)
+    constexpr int NT = kThreads<D>, BQ = kRows<D>, NRB = kWaves<D> / NKH;
+    constexpr int KPW = BC / NKH, KB = KPW / 32;   // keys of a tile per wave, in 32-key blocks
     constexpr int CPR = D / 8, KCH = BC * CPR / NT;
     // -D as the starting dP accumulator saves a subtraction per element but
     // holds 16 more registers; at d = 128 the registers matter more
@@ -100,7 +104,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const size_t bh = (size_t)tm.b * Hq + hq;
     const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
-    const int rb = w >> 1, khalf = w & 1;   // row block, key half
+    const int rb = (NKH == 2) ? (w >> 1) : w, khalf = (NKH == 2) ? (w & 1) : 0;   // row block, key half
     const int q0w = tm.qt * BQ + 32 * rb;
     const int qi = q0w + r;
     const int qc = min(qi, N - 1);
@@ -108,7 +112,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = scale * kLog2e;
-    __shared__ float dsh[BQ];   // D of each row, from key half 0
+    __shared__ float dsh[NKH == 2 ? BQ : 1];   // D of each row, from key half 0
 
     // The first K/V tile's loads and this row's LSE go out before the Q, dO and O
     // rows, so their latency overlaps the D computation instead of following it.
@@ -156,7 +160,9 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                 part = fmaf(bf16_hi(dv.w), o1[3], part);
             }
             Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
-            if (h == 0) dsh[32 * rb + r] = Di;
+            if constexpr (NKH == 2) {
+                if (h == 0) dsh[32 * rb + r] = Di;
+            }
             if (qok && h == 0) delta[bh * N + qi] = -Di;   // -D: the dK/dV pass starts dP from it
         }
     }
@@ -178,13 +184,18 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
     if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
-    if (khalf == 1) Di = dsh[32 * rb + r];
+    if constexpr (NKH == 2) {
+        if (khalf == 1) Di = dsh[32 * rb + r];
+    }
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
-        const int kw0 = k0 + 32 * khalf;   // first key of this wave's half
-        if (!causal || kw0 <= q0w + 31) {
-            // ---- S^T = K Q^T and dP^T - D = V dO^T - D (rows: the wave's keys, permuted;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const int kbr = KPW * khalf + 32 * kb;   // tile row of this wave's 32-key block
+            const int kw0 = k0 + kbr;                // its first key
+            if (causal && kw0 > q0w + 31) continue;
+            // ---- S^T = K Q^T and dP^T - D = V dO^T - D (rows: the block's keys, permuted;
             // columns: queries): the dP product accumulates onto -D_i, so no subtraction follows
             f32x16 s = f32x16{}, dp;
             if constexpr (kNegDAcc)
@@ -193,12 +204,12 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                 dp = f32x16{};
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][32 * khalf + krow_a][16 * c + 8 * h]);
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[buf][32 * khalf + krow_a][16 * c + 8 * h]);
+                const f16x8 ak = *reinterpret_cast<const f16x8*>(&Ks[buf][kbr + krow_a][16 * c + 8 * h]);
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(&Vs[buf][kbr + krow_a][16 * c + 8 * h]);
                 s = mfma_f16(ak, qb[c], s);
                 dp = mfma_bf16(av, db[c], dp);
             }
-            // ---- mask, only on tiles crossing the diagonal or the end of the sequence
+            // ---- mask, only on blocks crossing the diagonal or the end of the sequence
             // (one wave-uniform branch; the common path carries no mask work):
             // accumulator e holds key kw0 + 8h + c_e, c_e = 16(e/8) + e%8, kept iff
             // key < N and (if causal) key <= qi
@@ -214,14 +225,14 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                 const float p = fast_exp2(fmaf(s[e], sl2, -Li));
                 s[e] = kNegDAcc ? p * dp[e] : p * (dp[e] - Di);   // dS = P (dP - D)
             }
-            // ---- dQ^T += K^T dS^T  (A: the wave's K rows read transposed; B: dS from registers)
+            // ---- dQ^T += K^T dS^T  (A: the block's K rows read transposed; B: dS from registers)
 #pragma unroll
             for (int c2 = 0; c2 < 2; ++c2) {
                 const f16x8 dsb = to_f16x8(s[8 * c2 + 0], s[8 * c2 + 1], s[8 * c2 + 2], s[8 * c2 + 3],
                                            s[8 * c2 + 4], s[8 * c2 + 5], s[8 * c2 + 6], s[8 * c2 + 7]);
 #pragma unroll
                 for (int x = 0; x < DB; ++x) {
-                    const f16x8 a = lds_tr_operand(&Ks[buf][0][0], LD, 32 * khalf + 16 * c2, 32 * x, h, r);
+                    const f16x8 a = lds_tr_operand(&Ks[buf][0][0], LD, kbr + 16 * c2, 32 * x, h, r);
                     dqa[x] = mfma_f16(a, dsb, dqa[x]);
                 }
             }
@@ -247,30 +258,46 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             *reinterpret_cast<u32x4*>(d16row + 16 * c) = bf16x8_to_f16x8(__builtin_bit_cast(u32x4, db[c]));
         }
     }
-    // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
-    // after the last barrier) and store. Accumulator e of dim block x holds dim
-    // 32x + 8(e/4) + 4h + e%4 of query qi.
-    float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);   // [32 rows][D]
-    if (khalf == 1) {
+    // ---- store dQ (accumulator e of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of
+    // query qi); with two key halves, their partial sums are first added through LDS
+    if constexpr (NKH == 1) {
+        if (qok) {
+            float* row = dq + (bh * N + qi) * D;
 #pragma unroll
-        for (int x = 0; x < DB; ++x)
+            for (int x = 0; x < DB; ++x)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4)
-                *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
-                    f32x4{dqa[x][4 * a4 + 0], dqa[x][4 * a4 + 1], dqa[x][4 * a4 + 2], dqa[x][4 * a4 + 3]};
-    }
-    __syncthreads();
-    if (khalf == 0 && qok) {
-        float* row = dq + (bh * N + qi) * D;
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 val = {dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
+                                       dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
+                    *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
+                }
+        }
+    } else {
+        // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
+        // after the last barrier) and store. Accumulator e of dim block x holds dim
+        // 32x + 8(e/4) + 4h + e%4 of query qi.
+        float* xo = reinterpret_cast<float*>(smem) + rb * (32 * D);   // [32 rows][D]
+        if (khalf == 1) {
 #pragma unroll
-        for (int x = 0; x < DB; ++x)
+            for (int x = 0; x < DB; ++x)
 #pragma unroll
-            for (int a4 = 0; a4 < 4; ++a4) {
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
-                const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
-                                   (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
-                *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
-            }
+                for (int a4 = 0; a4 < 4; ++a4)
+                    *reinterpret_cast<f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
+                        f32x4{dqa[x][4 * a4 + 0], dqa[x][4 * a4 + 1], dqa[x][4 * a4 + 2], dqa[x][4 * a4 + 3]};
+        }
+        __syncthreads();
+        if (khalf == 0 && qok) {
+            float* row = dq + (bh * N + qi) * D;
+#pragma unroll
+            for (int x = 0; x < DB; ++x)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
+                    const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
+                                       (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
+                    *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
+                }
+        }
     }
 }
 
