@@ -44,7 +44,7 @@ template <int D> constexpr int kKeyHalves = (D == 128) ? 1 : 2;   // waves shari
 template <int D> constexpr int kThreads = 64 * kWaves<D>;
 template <int D> constexpr int kRows = 32 * kWaves<D> / kKeyHalves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile
-constexpr int PAD = 8;
+template <int D> constexpr int kPad = (D == 128) ? 24 : 8;   // K/V tile row padding, as the forward's
 }  // namespace bwdq
 
 // Global -> registers: the K and V chunks of one tile through buffer resources
@@ -70,8 +70,8 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
     constexpr int ROWS_PER_U = bwdq::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::PAD)) = bf16x8_to_f16x8(kreg[u]);
-        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + bwdq::PAD)) = vreg[u];
+        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::kPad<D>)) = bf16x8_to_f16x8(kreg[u]);
+        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + bwdq::kPad<D>)) = vreg[u];
     }
 }
 
@@ -83,7 +83,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
               _Float16* __restrict__ q16, _Float16* __restrict__ do16, float* __restrict__ dq,
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
-    constexpr int DC = D / 16, DB = D / 32, LD = D + PAD;
+    constexpr int DC = D / 16, DB = D / 32, LD = D + kPad<D>;
     constexpr int NKH = kKeyHalves<D>;   // key parts per tile (one wave each)
     constexpr int NT = kThreads<D>, BQ = kRows<D>, NRB = kWaves<D> / NKH;
     constexpr int KPW = BC / NKH, KB = KPW / 32;   // keys of a tile per wave, in 32-key blocks

@@ -62,7 +62,11 @@ template <int D> constexpr int kKeyHalves = (D == 128) ? 1 : 2;   // waves shari
 template <int D> constexpr int kThreads = 64 * kWaves<D>;
 template <int D> constexpr int kRows = 32 * kWaves<D> / kKeyHalves<D>;   // query rows per workgroup
 constexpr int BC = 64;           // keys per K/V tile (32 per key half)
-constexpr int PAD = 8;           // 16-bit elements of row padding (16 bytes)
+// Row padding of the K/V tiles (16-bit elements). With 64 banks of 4 bytes, a
+// stride of d + 8 leaves the 16-byte operand reads conflict-free and the
+// transposing reads 2-way at d = 64 but 4-way at d = 128; d + 24 brings d = 128
+// to 2-way as well (and two workgroups' tiles still fit one CU's LDS).
+template <int D> constexpr int kPad = (D == 128) ? 24 : 8;
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 }  // namespace fwd
 
@@ -89,8 +93,8 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
     constexpr int ROWS_PER_U = fwd::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + fwd::PAD)) = kreg[u];
-        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + fwd::PAD)) = bf16x8_to_f16x8(vreg[u]);
+        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + fwd::kPad<D>)) = kreg[u];
+        *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + fwd::kPad<D>)) = bf16x8_to_f16x8(vreg[u]);
     }
 }
 
@@ -102,7 +106,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     using namespace fwd;
     constexpr int DC = D / 16;          // 16-deep chunks of the head dimension
     constexpr int DB = D / 32;          // 32-wide blocks of the head dimension
-    constexpr int LD = D + PAD;         // LDS row stride (elements)
+    constexpr int LD = D + kPad<D>;     // LDS row stride (elements)
     constexpr int CPR = D / 8;          // 16-byte chunks per row
     constexpr int NT = kThreads<D>;     // threads
     constexpr int BR = kRows<D>;        // query rows per workgroup
