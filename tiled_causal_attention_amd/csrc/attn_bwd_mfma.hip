@@ -91,8 +91,8 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     // -D as the starting dP accumulator saves a subtraction per element but
     // holds 16 more registers; at d = 128 the registers matter more
     constexpr bool kNegDAcc = (D == 64);
-    // K and V tile buffers in one LDS block; after the loop it is the exchange
-    // area of the key halves' partial dQ (NRB row blocks of 32 x D floats)
+    // K and V tile buffers in one LDS block; after the loop (d = 64) it is the
+    // exchange area of the key halves' partial dQ (NRB row blocks of 32 x D floats)
     constexpr int TILES_BYTES = 2 * 2 * BC * LD * 2, MERGE_BYTES = NRB * 32 * D * 4;
     __shared__ __attribute__((aligned(16))) unsigned char smem[TILES_BYTES > MERGE_BYTES ? TILES_BYTES : MERGE_BYTES];
     _Float16 (*Ks)[BC][LD] = reinterpret_cast<_Float16 (*)[BC][LD]>(smem);

@@ -115,8 +115,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     constexpr int KPW = BC / NKH;       // keys of a tile per wave
     constexpr int KB = KPW / 32;        // 32-key blocks per wave
     constexpr int KCH = BC * CPR / NT;  // chunks per thread per tensor per tile
-    // K and V tile buffers, carved from one LDS block: after the loop the whole
-    // block is the merge area of the key halves (NRB row blocks of 32 x D floats)
+    // K and V tile buffers, carved from one LDS block: after the loop (d = 64) the
+    // whole block is the merge area of the key halves (NRB row blocks of 32 x D floats)
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BC * LD * 2];
     bf16_t (*Ks)[BC][LD] = reinterpret_cast<bf16_t (*)[BC][LD]>(smem);
     _Float16 (*Vs)[BC][LD] = reinterpret_cast<_Float16 (*)[BC][LD]>(smem + 2 * BC * LD * 2);
