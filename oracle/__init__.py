@@ -53,6 +53,8 @@ def load(path: str = _LIB):
     lib.oracle_attn_sampled.argtypes = [dp, dp, dp, dp, i, i, i, i, ctypes.c_double,
                                         i, ip, ip, dp, dp, dp, i, ip, dp, dp]
     lib.oracle_attn_sampled.restype = None
+    lib.oracle_attn_decode.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_attn_decode.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     if path == _LIB:
@@ -93,6 +95,25 @@ def attn_fwd(q, k, v, causal: int = 1, scale: float | None = None, lib=None
     lse = np.zeros((B, Hq, N))
     (lib or load()).oracle_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                     B, Hq, Hkv, N, d, int(causal), float(scale))
+    return o, lse
+
+
+def attn_decode(q, k, v, causal: int = 1, scale: float | None = None, lib=None
+                ) -> Tuple[np.ndarray, np.ndarray]:
+    """Few-query attention over a cache: q [B,Hq,Nq,d] are the last Nq positions of
+    the Nk-token sequence whose keys and values k, v [B,Hkv,Nk,d] hold (Nq <= Nk).
+    Return (o [B,Hq,Nq,d], lse [B,Hq,Nq]) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if (B, d) != (Bk, dk) or v.shape != k.shape or Hkv < 1 or Hq % Hkv or Nq > Nk:
+        raise ValueError(f"bad shapes q{q.shape} k{k.shape} v{v.shape}")
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    o = np.zeros((B, Hq, Nq, d))
+    lse = np.zeros((B, Hq, Nq))
+    (lib or load()).oracle_attn_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                       B, Hq, Hkv, Nq, Nk, d, int(causal), float(scale))
     return o, lse
 
 

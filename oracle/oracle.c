@@ -258,3 +258,50 @@ void oracle_attn_sampled(const double* q, const double* k, const double* v, cons
     free(lse_all);
     free(d_all);
 }
+
+/*
+ * Few-query attention over a cached sequence (inference; the blog page's FAQ
+ * says inference works and runs on 8 GB cards): Nq query rows that are the
+ * last Nq positions of a sequence of Nk >= Nq tokens, whose keys and values
+ * are all present in k and v. Query row i sits at sequence position
+ * p_i = Nk - Nq + i; causally it sees keys j <= p_i, otherwise every key.
+ * The definitions are those of the forward above:
+ *
+ *     s_ij  = scale * <q_i, k_j>            for visible j
+ *     LSE_i = log sum_j exp(s_ij)
+ *     O_i   = sum_j exp(s_ij - LSE_i) v_j
+ *
+ * With Nq = Nk this is exactly oracle_attn_fwd.
+ * Layout: q, o [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d]; lse [B, Hq, Nq].
+ */
+void oracle_attn_decode(const double* q, const double* k, const double* v,
+                        double* o, double* lse,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, double scale) {
+    const int group = Hq / Hkv;
+    const int units = B * Hkv;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int u = 0; u < units; ++u) {
+        const int b = u / Hkv, hkv = u % Hkv;
+        double* s = (double*)malloc(sizeof(double) * (size_t)(Nk > 0 ? Nk : 1));
+        const double* kh = k + ((size_t)b * Hkv + hkv) * Nk * d;
+        const double* vh = v + ((size_t)b * Hkv + hkv) * Nk * d;
+        for (int g = 0; g < group; ++g) {
+            const int hq = hkv * group + g;
+            const size_t qoff = ((size_t)b * Hq + hq) * Nq;
+            for (int i = 0; i < Nq; ++i) {
+                const int pos = Nk - Nq + i;   /* sequence position of this query */
+                const double* qi = q + (qoff + i) * d;
+                double L = row_scores(qi, kh, Nk, d, causal, pos, scale, s);
+                lse[qoff + i] = L;
+                double* oi = o + (qoff + i) * d;
+                for (int c = 0; c < d; ++c) oi[c] = 0.0;
+                for (int j = 0; j < Nk; ++j) {
+                    if (!visible(causal, pos, j)) continue;
+                    double p = exp(s[j] - L);
+                    for (int c = 0; c < d; ++c) oi[c] += p * vh[(size_t)j * d + c];
+                }
+            }
+        }
+        free(s);
+    }
+}

@@ -10,6 +10,9 @@ The oracle is checked against things other than itself:
   * invariants of the mathematics (softmax shift invariance, sum of dV, the
     Q/K rescaling identity, GQA equals MHA with repeated K/V);
   * hand-worked examples under tests/golden/;
+  * few-query (decode) attention over a cache: torch's SDPA with an explicit
+    bottom-right causal mask, the last rows of a full-sequence forward, and
+    closed forms;
   * planted mistakes: mutated copies of oracle.c must fail at least one pin.
 """
 import json
@@ -95,6 +98,7 @@ def _pin_failures(lib=None, shapes=SHAPES, atol=1e-10):
                 if not np.allclose(a, b, atol=atol, rtol=0):
                     fails.append(f"{nm} vs autograd {B,Hq,Hkv,N,d,causal}: {np.nanmax(np.abs(a - b))}")
     fails += _sampled_failures(lib, atol)
+    fails += _decode_failures(lib, atol)
     for fname in sorted(os.listdir(GOLDEN)):
         if not fname.endswith(".json"):
             continue
@@ -106,6 +110,93 @@ def _pin_failures(lib=None, shapes=SHAPES, atol=1e-10):
             if not np.allclose(a, arr[nm], atol=1e-12, rtol=0):
                 fails.append(f"golden {fname} {nm}: got {a.ravel()} want {arr[nm].ravel()}")
     return fails
+
+
+DECODE_SHAPES = [
+    # B, Hq, Hkv, Nq, Nk, d
+    (1, 2, 1, 1, 1, 4),
+    (2, 6, 2, 1, 37, 8),
+    (1, 4, 1, 3, 20, 5),
+    (2, 4, 4, 7, 7, 6),
+    (1, 12, 4, 5, 64, 16),
+]
+
+
+def _bottom_right_mask(Nq, Nk):
+    """Query row i (sequence position Nk - Nq + i) sees keys j <= Nk - Nq + i."""
+    return torch.ones(Nq, Nk, dtype=torch.bool).tril(diagonal=Nk - Nq)
+
+
+def _decode_failures(lib=None, atol=1e-10):
+    """Few-query attention over a cache against torch's float64 CPU
+    scaled_dot_product_attention with an explicit bottom-right causal mask, and
+    LSE against torch.logsumexp of the same masked scores."""
+    fails = []
+    for (B, Hq, Hkv, Nq, Nk, d) in DECODE_SHAPES:
+        G = Hq // Hkv
+        for causal in (1, 0):
+            gen = torch.Generator("cpu").manual_seed(Nq * 131 + Nk + causal)
+            q = torch.randn(B, Hq, Nq, d, generator=gen, dtype=torch.float64)
+            k = torch.randn(B, Hkv, Nk, d, generator=gen, dtype=torch.float64)
+            v = torch.randn(B, Hkv, Nk, d, generator=gen, dtype=torch.float64)
+            scale = 1.0 / math.sqrt(d)
+            o, lse = oracle.attn_decode(q, k, v, causal, scale, lib=lib)
+            kr, vr = k.repeat_interleave(G, dim=1), v.repeat_interleave(G, dim=1)
+            mask = _bottom_right_mask(Nq, Nk) if causal else torch.ones(Nq, Nk, dtype=torch.bool)
+            ro = F.scaled_dot_product_attention(q, kr, vr, attn_mask=mask, scale=scale).numpy()
+            sc = (scale * torch.matmul(q, kr.transpose(-1, -2).contiguous())).masked_fill(~mask, float("-inf"))
+            rl = torch.logsumexp(sc, dim=-1).numpy()
+            if not np.allclose(o, ro, atol=atol, rtol=0):
+                fails.append(f"decode O vs sdpa {B,Hq,Hkv,Nq,Nk,d,causal}: {np.nanmax(np.abs(o - ro))}")
+            if not np.allclose(lse, rl, atol=atol, rtol=0):
+                fails.append(f"decode LSE vs logsumexp {B,Hq,Hkv,Nq,Nk,d,causal}: {np.nanmax(np.abs(lse - rl))}")
+    return fails
+
+
+def test_decode_matches_library():
+    assert _decode_failures() == []
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_decode_rows_equal_last_rows_of_full_sequence(causal):
+    # the last Nq rows of attention over the whole sequence do not depend on the
+    # earlier query rows: a full-length query block whose tail is the decode
+    # queries gives the decode result in its last Nq rows
+    B, Hq, Hkv, Nq, Nk, d = 2, 6, 2, 4, 45, 8
+    g = torch.Generator("cpu").manual_seed(77)
+    qf = torch.randn(B, Hq, Nk, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float64)
+    of, lf = oracle.attn_fwd(qf, k, v, causal, 0.4)
+    od, ld = oracle.attn_decode(qf[:, :, Nk - Nq:].contiguous(), k, v, causal, 0.4)
+    assert np.allclose(od, of[:, :, Nk - Nq:], atol=1e-13, rtol=0)
+    assert np.allclose(ld, lf[:, :, Nk - Nq:], atol=1e-13, rtol=0)
+
+
+def test_decode_closed_forms():
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 5, 12, 3
+    g = torch.Generator("cpu").manual_seed(5)
+    q = torch.randn(B, Hq, Nq, d, generator=g, dtype=torch.float64)
+    k = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float64)
+    v = torch.randn(B, Hkv, Nk, d, generator=g, dtype=torch.float64)
+    # scale 0: uniform weights over the visible prefix of each query's position
+    o, lse = oracle.attn_decode(q, k, v, 1, 0.0)
+    vn = v.numpy()
+    for hq in range(Hq):
+        for i in range(Nq):
+            p = Nk - Nq + i
+            assert np.allclose(o[0, hq, i], vn[0, hq // 2, :p + 1].mean(0), atol=1e-14)
+            assert abs(lse[0, hq, i] - math.log(p + 1)) < 1e-14
+    o, lse = oracle.attn_decode(q, k, v, 0, 0.0)
+    assert np.allclose(o[0, 0, 0], vn[0, 0].mean(0), atol=1e-14) and np.allclose(lse, math.log(Nk))
+    # V = ones: O = 1
+    o, _ = oracle.attn_decode(q, k, torch.ones_like(v), 1, 0.7)
+    assert np.allclose(o, 1.0, atol=1e-14)
+    # a single cached key: O = V_0, LSE = scale <q, k_0>
+    o, lse = oracle.attn_decode(q[:, :, :1].contiguous(), k[:, :, :1].contiguous(), v[:, :, :1].contiguous(), 1, 0.7)
+    assert np.allclose(o[0, :, 0], vn[0, [0, 0, 1, 1], 0], atol=1e-14)
+    kq = (q[0, :, 0].numpy() * k[0, [0, 0, 1, 1], 0].numpy()).sum(-1)
+    assert np.allclose(lse[0, :, 0], 0.7 * kq, atol=1e-14)
 
 
 def _sampled_failures(lib=None, atol=1e-10):
@@ -326,6 +417,8 @@ MUTANTS = [
     ("sampled: dropped scale in dK", "dkj[c] += scale * ds * qi[c];", "dkj[c] += ds * qi[c];"),
     ("sampled: D without P", "D += exp(s[j] - L) * acc;", "D += acc;"),
     ("sampled: O row uses K", "oi[c] += s[j] * v[(size_t)j * d + c];", "oi[c] += s[j] * k[(size_t)j * d + c];"),
+    ("decode: queries aligned to the start", "const int pos = Nk - Nq + i;", "const int pos = i;"),
+    ("decode: position off by one", "const int pos = Nk - Nq + i;", "const int pos = Nk - Nq + i - 1;"),
     ("transposed V index", "acc += doi[c] * vh[(size_t)j * d + c];", "acc += doi[c] * vh[(size_t)c * d + j % d];"),
 ]
 
