@@ -6,7 +6,7 @@ attn_fwd (O, LSE), then the backward's two phases, attn_bwd_dq (D =
 rowsum(dO o O), dQ) and attn_bwd_dkdv (dK, dV) -- together exactly attn_bwd --
 all on torch's current stream, inputs resident in HBM.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa] [--out-dtype f32|bf16]
     python bench.py --all-configs [--oracle]     # per-workload report, see below
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
@@ -48,6 +48,7 @@ import tiled_causal_attention_amd as tca  # noqa: E402
 import workloads  # noqa: E402
 
 PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X published dense bf16/fp16 matrix peak
+OUT_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 METRIC = "causal attn fwd+bwd TFLOP/s + % bf16 MFMA peak, B8 Hq12/Hkv4 N1024 d64"
 
 
@@ -68,6 +69,8 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="per-workload report (median/p10/p90) instead of the one-line benchmark")
     p.add_argument("--oracle", action="store_true", help="with --all-configs: time the oracle per workload")
+    p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
+                   help="element type of o, dq, dk, dv (lse is always float32)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run one plain 256 MiB device-to-device copy before the steps, so a "
                         "rocprofv3 --pmc run records FETCH_SIZE/WRITE_SIZE for a known byte count")
@@ -91,14 +94,16 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from the committed PMC record, if it matches the current source."""
+def counted_traffic(kernel: str, workload: str, out_dtype: str = "f32"):
+    """HBM bytes per launch from the committed PMC record, if it matches the current source
+    (records of the float32-output runs are keyed by the workload alone)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as fh:
         rec = json.load(fh)
-    ent = rec.get(workload, {}).get(kernel)
+    key = workload if out_dtype == "f32" else f"{workload}/{out_dtype}_out"
+    ent = rec.get(key, {}).get(kernel)
     if not ent or ent.get("source_digest") != source_digest(kernel):
         return None
     return ent["hbm_bytes_per_launch"]
@@ -198,16 +203,18 @@ def measured_mfma_peak():
 
 def all_configs(args):
     import numpy as np
-    report = {"report": "per-workload fwd/bwd timing", "clocks_before": shader_clocks()}
+    out_dt = OUT_DTYPES[args.out_dtype]
+    report = {"report": "per-workload fwd/bwd timing", "out_dtype": args.out_dtype,
+              "clocks_before": shader_clocks()}
     peak = measured_mfma_peak()
     report["measured_mfma_bf16_tflops"] = peak
     print(json.dumps(report), flush=True)
     for name, s in workloads.CONFIGS.items():
         inputs = workloads.make_inputs(s)
         q, k, v, do = (t.cuda() for t in inputs)
-        o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=torch.float32, device=q.device)
+        o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=out_dt, device=q.device)
         lse = torch.empty((s.B, s.Hq, s.N), dtype=torch.float32, device=q.device)
-        dq, dk, dv = (torch.empty(t.shape, dtype=torch.float32, device=q.device) for t in (q, k, v))
+        dq, dk, dv = (torch.empty(t.shape, dtype=out_dt, device=q.device) for t in (q, k, v))
         ws = tca.bwd_workspace(q, k)
         causal, scale = bool(s.causal), s.scale
         reps = 20 if s.N >= 8192 else 100
@@ -234,7 +241,7 @@ def all_configs(args):
                            "p90_ms": float(np.percentile(a, 90))}
         ff, fb = s.flops_fwd(), s.flops_bwd()
         rec = {"workload": name, "B": s.B, "Hq": s.Hq, "Hkv": s.Hkv, "N": s.N, "d": s.d, "dtype": s.dtype,
-               "reps": reps, "fwd": stats(fwd), "bwd": stats(bwd), "fwd_bwd": stats(tot)}
+               "out_dtype": args.out_dtype, "reps": reps, "fwd": stats(fwd), "bwd": stats(bwd), "fwd_bwd": stats(tot)}
         for key, fl, arr in (("fwd", ff, fwd), ("bwd", fb, bwd), ("fwd_bwd", ff + fb, tot)):
             tf = fl / (float(np.median(arr)) * 1e-3) / 1e12
             rec[key].update({"tflops": tf, "pct_published_peak": 100 * tf / PEAK_MFMA_BF16_TFLOPS,
@@ -280,11 +287,12 @@ def main():
     inputs = workloads.make_inputs(s)
     q, k, v, do = (t.cuda() for t in inputs)
     dev = q.device
-    o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=torch.float32, device=dev)
+    out_dt = OUT_DTYPES[args.out_dtype]
+    o = torch.empty((s.B, s.Hq, s.N, s.d), dtype=out_dt, device=dev)
     lse = torch.empty((s.B, s.Hq, s.N), dtype=torch.float32, device=dev)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
-    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=out_dt, device=dev)
+    dk = torch.empty(k.shape, dtype=out_dt, device=dev)
+    dv = torch.empty(v.shape, dtype=out_dt, device=dev)
     ws = tca.bwd_workspace(q, k)
     causal, scale = bool(s.causal), s.scale
     if args.calibrate_copy:
@@ -348,7 +356,7 @@ def main():
     kernel_flops = {"attn_fwd": flops_fwd, "attn_bwd_dq": 1.5 * flops_fwd, "attn_bwd_dkdv": 2.0 * flops_fwd}
     achieved = kernel_flops[dom] / (kernels[dom] * 1e-3) / 1e12
     roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": counted_traffic(dom, s.name),
+            "frac": achieved / PEAK_MFMA_BF16_TFLOPS, "traffic": counted_traffic(dom, s.name, args.out_dtype),
             "kernel": dom, "flops_per_launch": kernel_flops[dom]}
 
     result = {
@@ -365,7 +373,7 @@ def main():
         "dtype": "bf16" if s.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": f"{s.name}: causal GQA attention fwd+bwd, B={s.B} Hq={s.Hq} "
-                               f"Hkv={s.Hkv} N={s.N} d={s.d} {s.dtype} in, fp32 out",
+                               f"Hkv={s.Hkv} N={s.N} d={s.d} {s.dtype} in, {args.out_dtype} out",
                    "global_batch": s.B, "seq_len": s.N, "parallelism": "single-gpu"},
         "pct_peak": 100.0 * tflops / PEAK_MFMA_BF16_TFLOPS,
         "fwd_tflops": flops_fwd / (t_fwd * 1e-3) / 1e12,

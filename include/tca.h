@@ -28,8 +28,15 @@
  * k, v, dk, dv: [B, Hkv, N, d]; lse: [B, Hq, N]. The head dimension d is the
  * fastest-moving index.
  *
- * Precision: inputs q, k, v, dO are float32 (ATTN_F32) or bfloat16 (ATTN_BF16).
- * Outputs o, lse, dq, dk, dv are always float32. With ATTN_F32 every step is
+ * Precision: inputs q, k, v, dO are float32 (ATTN_F32) or bfloat16 (ATTN_BF16)
+ * (`dtype`). Outputs o, dq, dk, dv are float32 or bfloat16 (`out_dtype`); lse
+ * is always float32. Every result is formed in float32 and, for bfloat16
+ * outputs, rounded to nearest even only when it is stored: o in bfloat16 is
+ * exactly the float32 o rounded. The backward takes o in `out_dtype`, as
+ * attn_fwd wrote it, and forms D = rowsum(dO o O) from those values (what a
+ * bfloat16 trainer holds). bfloat16 outputs serve the trainer step that follows
+ * (the pages' hand-written GPT-2 trainer consumes these tensors); their extra
+ * error is one bfloat16 rounding (relative 2^-9) per element. With ATTN_F32 every step is
  * computed in float32. With ATTN_BF16 and d in {64, 128} every product runs on
  * the matrix cores with float32 accumulation. Products of two inputs take them
  * as they are: in the forward Q*K^T is a bf16 product, in the backward dO*V^T
@@ -55,6 +62,8 @@
  * enqueueing began. No exception crosses this interface and nothing is
  * printed. Inputs and outputs must not alias.
  *
+ * Invalid dtype or out_dtype codes give ATTN_EINVAL.
+ *
  * Supported shapes: B >= 0, N >= 0 (B*N == 0 is a no-op that returns ATTN_OK
  * and ignores every pointer), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
  * d in {16, 32, 64, 128}, (N+64)*d < 2^31, B*Hq*N < 2^31, causal in {0, 1},
@@ -70,8 +79,8 @@ extern "C" {
 #endif
 
 typedef enum attn_dtype {
-    ATTN_F32 = 0,   /* float32 inputs  */
-    ATTN_BF16 = 1   /* bfloat16 inputs */
+    ATTN_F32 = 0,   /* float32  */
+    ATTN_BF16 = 1   /* bfloat16 */
 } attn_dtype;
 
 typedef enum attn_status {
@@ -81,7 +90,8 @@ typedef enum attn_status {
     ATTN_EHIP = 3           /* the HIP runtime reported an error while enqueueing */
 } attn_status;
 
-/* Version of this interface; bumped on any incompatible change. */
+/* Version of this interface; bumped on any incompatible change (2: the
+ * out_dtype argument). */
 int attn_abi_version(void);
 
 /* Static, human-readable name of a status code (never NULL). */
@@ -93,13 +103,13 @@ size_t attn_fwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N,
 
 /* Forward: o and lse from q, k, v.
  *   q [B,Hq,N,d], k and v [B,Hkv,N,d] in `dtype`;
- *   o [B,Hq,N,d] float32 and lse [B,Hq,N] float32 are fully overwritten.
+ *   o [B,Hq,N,d] in `out_dtype` and lse [B,Hq,N] float32 are fully overwritten.
  * This is the tile loop of the "Tiled FlashAttention" section: per query tile,
  * K/V tiles in on-chip memory, Q*K^T, online softmax, output accumulation; the
  * causal variant visits only the K/V tiles at or below the diagonal. */
-attn_status attn_fwd(attn_dtype dtype,
+attn_status attn_fwd(attn_dtype dtype, attn_dtype out_dtype,
                      const void* q, const void* k, const void* v,
-                     float* o, float* lse,
+                     void* o, float* lse,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      void* stream);
@@ -112,17 +122,18 @@ attn_status attn_fwd(attn_dtype dtype,
 size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d);
 
 /* Backward: dq, dk, dv from q, k, v, the forward's o and lse, and dO.
- *   q, k, v, dO in `dtype`; o, lse exactly as written by attn_fwd with the same
- *   q, k, v, sizes, causal flag and scale; dq [B,Hq,N,d], dk and dv [B,Hkv,N,d]
- *   float32, fully overwritten. `workspace` holds at least
- *   attn_bwd_workspace_bytes(...) bytes of device memory; its contents on entry
- *   do not matter. Every output element is written exactly once (no atomics),
- *   so dq, dk and dv are bitwise reproducible for fixed inputs.
+ *   q, k, v, dO in `dtype`; o (in `out_dtype`) and lse exactly as written by
+ *   attn_fwd with the same q, k, v, dtypes, sizes, causal flag and scale;
+ *   dq [B,Hq,N,d], dk and dv [B,Hkv,N,d] in `out_dtype`, fully overwritten.
+ *   `workspace` holds at least attn_bwd_workspace_bytes(...) bytes of device
+ *   memory; its contents on entry do not matter. Every output element is
+ *   written exactly once (no atomics), so dq, dk and dv are bitwise
+ *   reproducible for fixed inputs.
  * Equivalent to attn_bwd_dq followed by attn_bwd_dkdv on `stream`. */
-attn_status attn_bwd(attn_dtype dtype,
+attn_status attn_bwd(attn_dtype dtype, attn_dtype out_dtype,
                      const void* q, const void* k, const void* v,
-                     const float* o, const float* lse, const void* dO,
-                     float* dq, float* dk, float* dv,
+                     const void* o, const float* lse, const void* dO,
+                     void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes,
                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                      void* stream);
@@ -131,10 +142,10 @@ attn_status attn_bwd(attn_dtype dtype,
  * (and, for bf16 inputs with d in {64, 128}, lse in base-2 units and fp16
  * copies of q and dO) into `workspace`, then dq (recomputing P and dP for each
  * visible K/V tile). dk and dv are not touched. Arguments as for attn_bwd. */
-attn_status attn_bwd_dq(attn_dtype dtype,
+attn_status attn_bwd_dq(attn_dtype dtype, attn_dtype out_dtype,
                         const void* q, const void* k, const void* v,
-                        const float* o, const float* lse, const void* dO,
-                        float* dq, float* dk, float* dv,
+                        const void* o, const float* lse, const void* dO,
+                        void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                         void* stream);
@@ -143,10 +154,10 @@ attn_status attn_bwd_dq(attn_dtype dtype,
  * attn_bwd_dq left in `workspace`. Requires attn_bwd_dq with the same arguments to have been
  * enqueued before it on the same stream (or completed). dq is not touched.
  * Arguments as for attn_bwd. */
-attn_status attn_bwd_dkdv(attn_dtype dtype,
+attn_status attn_bwd_dkdv(attn_dtype dtype, attn_dtype out_dtype,
                           const void* q, const void* k, const void* v,
-                          const float* o, const float* lse, const void* dO,
-                          float* dq, float* dk, float* dv,
+                          const void* o, const float* lse, const void* dO,
+                          void* dq, void* dk, void* dv,
                           void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           void* stream);

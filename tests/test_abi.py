@@ -55,7 +55,7 @@ def test_exports_are_c_symbols():
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 1
+    assert L.attn_abi_version() == 2
     for s in (OK, EINVAL, EUNSUP, tca.ATTN_EHIP):
         assert L.attn_status_str(s)
     assert b"unknown" in L.attn_status_str(99)
@@ -78,21 +78,24 @@ def test_workspace_sizes(L):
 FAKE = 0x10000
 
 
-def fwd(L, dtype=BF16, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125,
+def fwd(L, dtype=BF16, out_dtype=F32, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125,
         q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=None, wsb=0):
-    return L.attn_fwd(dtype, q, k, v, o, lse, ws, wsb, B, Hq, Hkv, N, d, causal, scale, None)
+    return L.attn_fwd(dtype, out_dtype, q, k, v, o, lse, ws, wsb, B, Hq, Hkv, N, d, causal, scale, None)
 
 
-def bwd(L, name="attn_bwd", dtype=BF16, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125,
-        ptrs=None, ws=FAKE, wsb=1 << 20):
+def bwd(L, name="attn_bwd", dtype=BF16, out_dtype=F32, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1,
+        scale=0.125, ptrs=None, ws=FAKE, wsb=1 << 20):
     p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, dO=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
     p.update(ptrs or {})
-    return getattr(L, name)(dtype, p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"],
+    return getattr(L, name)(dtype, out_dtype, p["q"], p["k"], p["v"], p["o"], p["lse"], p["dO"], p["dq"],
                             p["dk"], p["dv"], ws, wsb, B, Hq, Hkv, N, d, causal, scale, None)
 
 
 @pytest.mark.parametrize("kw,want", [
     (dict(dtype=7), EINVAL),
+    (dict(out_dtype=2), EINVAL),
+    (dict(out_dtype=-1), EINVAL),
+    (dict(out_dtype=BF16, o=FAKE + 8), EINVAL),   # bf16 o: still 16-byte aligned
     (dict(B=-1), EINVAL),
     (dict(N=-5), EINVAL),
     (dict(Hq=0), EINVAL),
@@ -125,6 +128,8 @@ def test_fwd_rejects(L, kw, want):
 @pytest.mark.parametrize("name", ["attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"])
 @pytest.mark.parametrize("kw,want", [
     (dict(dtype=3), EINVAL),
+    (dict(out_dtype=5), EINVAL),
+    (dict(out_dtype=BF16, ptrs=dict(dq=FAKE + 2)), EINVAL),
     (dict(Hq=6, Hkv=4), EINVAL),
     (dict(causal=5), EINVAL),
     (dict(d=96), EUNSUP),
@@ -150,8 +155,9 @@ def test_empty_inputs_are_noops(L):
     for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         assert bwd(L, name, B=0, ptrs=nul, ws=None, wsb=0) == OK
         assert bwd(L, name, N=0, ptrs=nul, ws=None, wsb=0) == OK
-    # but an empty call with an invalid flag is still rejected
+    # but an empty call with an invalid flag or dtype is still rejected
     assert fwd(L, B=0, causal=3) == EINVAL
+    assert fwd(L, B=0, out_dtype=9) == EINVAL
 
 
 def test_outputs_untouched_on_error(L):
@@ -161,6 +167,22 @@ def test_outputs_untouched_on_error(L):
     st = fwd(L, B=1, Hq=4, Hkv=3, N=64, d=64, o=o.ctypes.data, lse=lse.ctypes.data)
     assert st == EINVAL
     assert (o == 7.0).all() and (lse == 7.0).all()
+
+
+def test_python_binding_checks_output_dtypes():
+    import torch
+    q = torch.zeros(1, 2, 8, 16)
+    with pytest.raises(TypeError):
+        tca._code(torch.float16)
+    o32, obf = torch.zeros(1, 2, 8, 16), torch.zeros(1, 2, 8, 16, dtype=torch.bfloat16)
+    lse = torch.zeros(1, 2, 8)
+    # out tensors that disagree with out_dtype, or a non-float32 lse, are refused before any call
+    with pytest.raises(TypeError):
+        tca.attn_fwd(q, q, q, out=(o32, lse), out_dtype=torch.bfloat16)
+    with pytest.raises(TypeError):
+        tca.attn_fwd(q, q, q, out=(obf, lse.bfloat16()))
+    with pytest.raises(TypeError):
+        tca.attn_bwd(q, q, q, obf, lse, q, out=(obf, o32, obf), workspace=torch.zeros(1))
 
 
 def test_python_binding_refuses_cpu_tensors():

@@ -8,7 +8,9 @@ not built, every call raises.
     o, lse = attn_fwd(q, k, v, causal=True)             # q [B,Hq,N,d], k/v [B,Hkv,N,d]
     dq, dk, dv = attn_bwd(q, k, v, o, lse, dO, causal=True)
 
-Inputs are float32 or bfloat16 CUDA tensors, contiguous; outputs are float32.
+Inputs are float32 or bfloat16 CUDA tensors, contiguous. Outputs o, dq, dk, dv
+are float32 by default or bfloat16 (attn_fwd(..., out_dtype=torch.bfloat16);
+the backward follows o's dtype); lse is always float32.
 """
 from __future__ import annotations
 
@@ -52,9 +54,9 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_bwd_workspace_bytes.restype = sz
-    L.attn_fwd.argtypes = [i, vp, vp, vp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_fwd.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
     L.attn_fwd.restype = i
-    bwd_args = [i, vp, vp, vp, fp, fp, vp, fp, fp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    bwd_args = [i, i, vp, vp, vp, vp, fp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, vp]
     for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         getattr(L, name).argtypes = bwd_args
         getattr(L, name).restype = i
@@ -71,12 +73,16 @@ def _check(status: int):
         raise AttnError(status, status_str(status))
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.float32:
+def _code(dtype: torch.dtype) -> int:
+    if dtype == torch.float32:
         return ATTN_F32
-    if t.dtype == torch.bfloat16:
+    if dtype == torch.bfloat16:
         return ATTN_BF16
-    raise TypeError(f"unsupported input dtype {t.dtype}; use float32 or bfloat16")
+    raise TypeError(f"unsupported dtype {dtype}; use float32 or bfloat16")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    return _code(t.dtype)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -105,21 +111,26 @@ def default_scale(d: int) -> float:
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
-             scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None
-             ) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Forward: returns (o float32 [B,Hq,N,d], lse float32 [B,Hq,N])."""
+             scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+             out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward: returns (o [B,Hq,N,d] in out_dtype (float32 unless given, or
+    the dtype of out[0]), lse float32 [B,Hq,N])."""
     B, Hq, Hkv, N, d = _dims(q, k)
     scale = default_scale(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     if out is None:
-        o = torch.empty((B, Hq, N, d), dtype=torch.float32, device=q.device)
+        o = torch.empty((B, Hq, N, d), dtype=out_dtype or torch.float32, device=q.device)
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+        if out_dtype is not None and o.dtype != out_dtype:
+            raise TypeError(f"out[0] is {o.dtype}, out_dtype is {out_dtype}")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
     L = lib()
     ws_bytes = L.attn_fwd_workspace_bytes(dt, B, Hq, Hkv, N, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
-    _check(L.attn_fwd(dt, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
+    _check(L.attn_fwd(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(ws), ws_bytes,
                       B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
     return o, lse
 
@@ -133,18 +144,23 @@ def bwd_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
 def _bwd_call(name, q, k, v, o, lse, dO, dq, dk, dv, ws, causal, scale):
     B, Hq, Hkv, N, d = _dims(q, k)
     scale = default_scale(d) if scale is None else float(scale)
-    _check(getattr(lib(), name)(_dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    for t in (dq, dk, dv):
+        if t.dtype != o.dtype:
+            raise TypeError(f"dq, dk, dv must have o's dtype {o.dtype}, got {t.dtype}")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(getattr(lib(), name)(_dtype_code(q), _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                 _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
                                 B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
 
 
 def attn_bwd(q, k, v, o, lse, dO, causal: bool = True, scale: Optional[float] = None,
              out=None, workspace: Optional[torch.Tensor] = None):
-    """Backward: returns (dq float32 [B,Hq,N,d], dk, dv float32 [B,Hkv,N,d])."""
+    """Backward: returns (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]) in o's dtype."""
     if out is None:
-        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-        dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+        dq = torch.empty(q.shape, dtype=o.dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=o.dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=o.dtype, device=q.device)
     else:
         dq, dk, dv = out
     ws = bwd_workspace(q, k) if workspace is None else workspace

@@ -91,16 +91,30 @@ def resource_usage() -> list:
 def resource_usage_markdown() -> str:
     import re
 
-    def short(n):   # tca::<name><D> from the mangled kernel name
+    def short(n):   # tca::<name><template arguments> from the mangled kernel name
         m = re.match(r"_ZN3tca(\d+)", n)
         if not m:
             return n
         ln = int(m.group(1))
-        t = re.match(r"I(f|t|DF16_)?Li(\d+)E", n[m.end() + ln:])
-        if not t:
-            return n[m.end():m.end() + ln]
-        ty = {"f": "float, ", "t": "bf16, ", "DF16_": "half, "}.get(t.group(1) or "", "")
-        return n[m.end():m.end() + ln] + f"<{ty}{t.group(2)}>"
+        name, rest = n[m.end():m.end() + ln], n[m.end() + ln:]
+        if not rest.startswith("I"):
+            return name
+        args, i = [], 1
+        names = {"f": "float", "t": "bf16", "DF16_": "half"}
+        while i < len(rest) and rest[i] != "E":
+            lit = re.match(r"Li(\d+)E", rest[i:])
+            if lit:
+                args.append(lit.group(1))
+                i += lit.end()
+                continue
+            for code, ty in names.items():
+                if rest.startswith(code, i):
+                    args.append(ty)
+                    i += len(code)
+                    break
+            else:
+                return name
+        return f"{name}<{', '.join(args)}>"
 
     out = ["| Kernel | Source | VGPRs | AGPRs | VGPR spills | LDS bytes per workgroup | Waves per SIMD |",
            "|---|---|---|---|---|---|---|"]

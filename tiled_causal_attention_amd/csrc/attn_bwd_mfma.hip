@@ -75,12 +75,13 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
     }
 }
 
-template <int D>
+// OT: element type of o (read) and dq (written): float32 or bfloat16
+template <int D, typename OT>
 __global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 2)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-              const float* __restrict__ o, const float* __restrict__ lse,
+              const OT* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
-              _Float16* __restrict__ q16, _Float16* __restrict__ do16, float* __restrict__ dq,
+              _Float16* __restrict__ q16, _Float16* __restrict__ do16, OT* __restrict__ dq,
               int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + kPad<D>;
@@ -132,7 +133,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     {
         const bf16_t* qrow = q + (bh * N + qc) * D + 8 * h;
         const bf16_t* drow = dout + (bh * N + qc) * D + 8 * h;
-        const float* orow = o + (bh * N + qc) * D + 8 * h;
+        const OT* orow = o + (bh * N + qc) * D + 8 * h;
         u32x4 dvr[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
@@ -148,16 +149,16 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
                 const u32x4 dv = dvr[c];
-                const f32x4 o0 = *reinterpret_cast<const f32x4*>(orow + 16 * c);
-                const f32x4 o1 = *reinterpret_cast<const f32x4*>(orow + 16 * c + 4);
-                part = fmaf(bf16_lo(dv.x), o0[0], part);
-                part = fmaf(bf16_hi(dv.x), o0[1], part);
-                part = fmaf(bf16_lo(dv.y), o0[2], part);
-                part = fmaf(bf16_hi(dv.y), o0[3], part);
-                part = fmaf(bf16_lo(dv.z), o1[0], part);
-                part = fmaf(bf16_hi(dv.z), o1[1], part);
-                part = fmaf(bf16_lo(dv.w), o1[2], part);
-                part = fmaf(bf16_hi(dv.w), o1[3], part);
+                float ov[8];
+                load8_f32(orow + 16 * c, ov);
+                part = fmaf(bf16_lo(dv.x), ov[0], part);
+                part = fmaf(bf16_hi(dv.x), ov[1], part);
+                part = fmaf(bf16_lo(dv.y), ov[2], part);
+                part = fmaf(bf16_hi(dv.y), ov[3], part);
+                part = fmaf(bf16_lo(dv.z), ov[4], part);
+                part = fmaf(bf16_hi(dv.z), ov[5], part);
+                part = fmaf(bf16_lo(dv.w), ov[6], part);
+                part = fmaf(bf16_hi(dv.w), ov[7], part);
             }
             Di = sum_halves(part);   // the two half-waves hold complementary dims of the row
             if constexpr (NKH == 2) {
@@ -262,14 +263,14 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     // query qi); with two key halves, their partial sums are first added through LDS
     if constexpr (NKH == 1) {
         if (qok) {
-            float* row = dq + (bh * N + qi) * D;
+            OT* row = dq + (bh * N + qi) * D;
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const f32x4 val = {dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
                                        dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
-                    *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
+                    store_out4(row + 32 * x + 8 * a4 + 4 * h, val);
                 }
         }
     } else {
@@ -287,7 +288,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         }
         __syncthreads();
         if (khalf == 0 && qok) {
-            float* row = dq + (bh * N + qi) * D;
+            OT* row = dq + (bh * N + qi) * D;
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
@@ -295,7 +296,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                     const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
                     const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
                                        (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
-                    *reinterpret_cast<f32x4*>(row + 32 * x + 8 * a4 + 4 * h) = val;
+                    store_out4(row + 32 * x + 8 * a4 + 4 * h, val);
                 }
         }
     }
@@ -333,12 +334,13 @@ template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-r
 
 }  // namespace bwdkv
 
-template <int D>
+// OT: element type of dk and dv (float32, or bfloat16 rounded to nearest even)
+template <int D, typename OT>
 __global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, (D == 128) ? 2 : 1)
 bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
                 const float* __restrict__ l2, const float* __restrict__ delta,
-                float* __restrict__ dk, float* __restrict__ dv,
+                OT* __restrict__ dk, OT* __restrict__ dv,
                 int Hq, int Hkv, int N, int causal, float scale, int ntiles, int wg_per_unit) {
     using namespace bwdkv;
     constexpr int NQW = Cfg<D>::NQW;
@@ -598,14 +600,14 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // ---- end of a K/V tile: each wave holds its tensor's final values for its 32 keys
             // (accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r)
             if (it + 1 == nitems || tile_of(cur) != tile) {
-                float* const dst = qw ? dk : dv;
+                OT* const dst = qw ? dk : dv;
                 const float f = qw ? scale : 1.0f;
 #pragma unroll
                 for (int x = 0; x < DB; ++x)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = kw0 + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if (key < N) dst[kvoff + (size_t)key * D + 32 * x + r] = dka[x][e] * f;
+                        if (key < N) store_out1(dst + kvoff + (size_t)key * D + 32 * x + r, dka[x][e] * f);
                     }
             }
         }
@@ -693,8 +695,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                     const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
                     if (key < N) {
                         const size_t off = kvoff + (size_t)key * D + 32 * x + r;
-                        dk[off] = sk[x][i] * scale;
-                        dv[off] = sv[x][i];
+                        store_out1(dk + off, sk[x][i] * scale);
+                        store_out1(dv + off, sv[x][i]);
                     }
                 }
         }
@@ -707,35 +709,39 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     }
 }
 
-template <int D>
+template <int D, typename OT>
 static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + bwdq::kRows<D> - 1) / bwdq::kRows<D>;
     const int units = a.B * a.Hkv;
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
-                       (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const float*)a.o,
-                       (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, a.dq,
+    hipLaunchKernelGGL((bwd_dq_kernel<D, OT>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
+                       (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const OT*)a.o,
+                       (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, (OT*)a.dq,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename OT>
 static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     const int ntiles = (a.N + bwdkv::BC - 1) / bwdkv::BC;
     const int per_unit = a.causal ? (ntiles + 1) / 2 : ntiles;
     const int threads = 64 * 2 * bwdkv::Cfg<D>::NQW;
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
-                       (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, a.dk,
-                       a.dv, a.Hq, a.Hkv, a.N, a.causal, a.scale, ntiles, per_unit);
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, (OT*)a.dk,
+                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, a.scale, ntiles, per_unit);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st) {
-    return (a.d == 64) ? launch_bwd_dq_d<64>(a, st) : launch_bwd_dq_d<128>(a, st);
+    if (a.out_dtype == ATTN_BF16)
+        return (a.d == 64) ? launch_bwd_dq_d<64, bf16_t>(a, st) : launch_bwd_dq_d<128, bf16_t>(a, st);
+    return (a.d == 64) ? launch_bwd_dq_d<64, float>(a, st) : launch_bwd_dq_d<128, float>(a, st);
 }
 hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st) {
-    return (a.d == 64) ? launch_bwd_dkdv_d<64>(a, st) : launch_bwd_dkdv_d<128>(a, st);
+    if (a.out_dtype == ATTN_BF16)
+        return (a.d == 64) ? launch_bwd_dkdv_d<64, bf16_t>(a, st) : launch_bwd_dkdv_d<128, bf16_t>(a, st);
+    return (a.d == 64) ? launch_bwd_dkdv_d<64, float>(a, st) : launch_bwd_dkdv_d<128, float>(a, st);
 }
 
 }  // namespace tca

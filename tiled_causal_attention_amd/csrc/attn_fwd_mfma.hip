@@ -98,10 +98,11 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
     }
 }
 
-template <int D>
+// OT: element type of o (float32, or bfloat16 rounded to nearest even at the store)
+template <int D, typename OT>
 __global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-                const bf16_t* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
+                const bf16_t* __restrict__ v, OT* __restrict__ o, float* __restrict__ lse,
                 int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
     using namespace fwd;
     constexpr int DC = D / 16;          // 16-deep chunks of the head dimension
@@ -258,7 +259,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         __syncthreads();
     }
 
-    // ---- epilogue: normalise, store O (fp32) and LSE (natural log). Accumulator e
+    // ---- epilogue: normalise, store O (element type OT) and LSE (natural log). Accumulator e
     // of dim block x holds dim 32x + 8(e/4) + 4h + e%4 of query qi. With two key
     // halves, they are first merged through LDS (the K tile buffers are free after
     // the loop's last barrier).
@@ -266,14 +267,14 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     if constexpr (NKH == 1) {
         if (qi < N) {
             const float inv = 1.f / l_tot;
-            float* orow = o + (bh * N + qi) * D;
+            OT* orow = o + (bh * N + qi) * D;
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const f32x4 val = {oacc[x][4 * a4 + 0] * inv, oacc[x][4 * a4 + 1] * inv,
                                        oacc[x][4 * a4 + 2] * inv, oacc[x][4 * a4 + 3] * inv};
-                    *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                    store_out4(orow + 32 * x + 8 * a4 + 4 * h, val);
                 }
             if (h == 0) lse[bh * N + qi] = (m_s + __log2f(l_tot)) * kLn2;
         }
@@ -300,7 +301,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             const float l = l_tot * a0 + l1 * a1;
             const float inv = 1.f / l;
             const float c0 = a0 * inv, c1 = a1 * inv;
-            float* orow = o + (bh * N + qi) * D;
+            OT* orow = o + (bh * N + qi) * D;
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
@@ -308,7 +309,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                     const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
                     const f32x4 val = {oacc[x][4 * a4 + 0] * c0 + o1[0] * c1, oacc[x][4 * a4 + 1] * c0 + o1[1] * c1,
                                        oacc[x][4 * a4 + 2] * c0 + o1[2] * c1, oacc[x][4 * a4 + 3] * c0 + o1[3] * c1};
-                    *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) = val;
+                    store_out4(orow + 32 * x + 8 * a4 + 4 * h, val);
                 }
             if (h == 0) lse[bh * N + qi] = (m + __log2f(l)) * kLn2;
         }
@@ -317,19 +318,21 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
 bool mfma_path(const AttnArgs& a) { return mfma_shape(a.dtype, a.d); }
 
-template <int D>
+template <int D, typename OT>
 static hipError_t launch_fwd_d(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + fwd::kRows<D> - 1) / fwd::kRows<D>;
     const int units = a.B * a.Hkv;
     const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-    hipLaunchKernelGGL(fwd_mfma_kernel<D>, grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
-                       (const bf16_t*)a.k, (const bf16_t*)a.v, a.o, a.lse, a.Hq, a.Hkv, a.N, a.causal,
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, OT>), grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, (OT*)a.o, a.lse, a.Hq, a.Hkv, a.N, a.causal,
                        a.scale, nqt, units);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
-    return (a.d == 64) ? launch_fwd_d<64>(a, st) : launch_fwd_d<128>(a, st);
+    if (a.out_dtype == ATTN_BF16)
+        return (a.d == 64) ? launch_fwd_d<64, bf16_t>(a, st) : launch_fwd_d<128, bf16_t>(a, st);
+    return (a.d == 64) ? launch_fwd_d<64, float>(a, st) : launch_fwd_d<128, float>(a, st);
 }
 
 }  // namespace tca

@@ -14,10 +14,12 @@ namespace tca {
 constexpr int kGenRows = 64;   // rows (queries or keys) per block = one wave
 constexpr int kGenTile = 32;   // K/V (or Q/dO) rows staged per LDS tile
 
-template <typename T, int D>
+// T: input element type; OT: output element type of o, dq, dk, dv (float32,
+// or bfloat16 rounded to nearest even when stored)
+template <typename T, typename OT, int D>
 __global__ void __launch_bounds__(kGenRows)
 fwd_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                   float* __restrict__ o, float* __restrict__ lse,
+                   OT* __restrict__ o, float* __restrict__ lse,
                    int Hq, int Hkv, int N, int causal, float scale) {
     __shared__ float Ks[kGenTile][D];
     __shared__ float Vs[kGenTile][D];
@@ -70,21 +72,21 @@ fwd_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __
     }
     if (i < N) {
         const float inv = 1.f / l;
-        float* oi = o + ((size_t)bh * N + i) * D;
+        OT* oi = o + ((size_t)bh * N + i) * D;
 #pragma unroll
-        for (int c = 0; c < D; ++c) oi[c] = acc[c] * inv;
+        for (int c = 0; c < D; ++c) store_out1(oi + c, acc[c] * inv);
         lse[(size_t)bh * N + i] = m + logf(l);
     }
 }
 
 // dK, dV for one KV head: one lane per key, looping over every query head of
 // the group and every visible query. No atomics: each key row is owned by one lane.
-template <typename T, int D>
+template <typename T, typename OT, int D>
 __global__ void __launch_bounds__(kGenRows)
 bwd_dkdv_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                         const float* __restrict__ lse, const T* __restrict__ dout,
                         const float* __restrict__ delta,
-                        float* __restrict__ dk, float* __restrict__ dv,
+                        OT* __restrict__ dk, OT* __restrict__ dv,
                         int Hq, int Hkv, int N, int causal, float scale) {
     __shared__ float Qs[kGenTile][D];
     __shared__ float dOs[kGenTile][D];
@@ -144,23 +146,23 @@ bwd_dkdv_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const 
         }
     }
     if (j < N) {
-        float* dkj = dk + kvoff + (size_t)j * D;
-        float* dvj = dv + kvoff + (size_t)j * D;
+        OT* dkj = dk + kvoff + (size_t)j * D;
+        OT* dvj = dv + kvoff + (size_t)j * D;
 #pragma unroll
         for (int c = 0; c < D; ++c) {
-            dkj[c] = scale * dkr[c];
-            dvj[c] = dvr[c];
+            store_out1(dkj + c, scale * dkr[c]);
+            store_out1(dvj + c, dvr[c]);
         }
     }
 }
 
 // dQ: one lane per query row, looping over the visible keys. The lane first
 // forms D_i = <dO_i, O_i> and publishes it (the dK/dV kernel reads it).
-template <typename T, int D>
+template <typename T, typename OT, int D>
 __global__ void __launch_bounds__(kGenRows)
 bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                      const float* __restrict__ o, const float* __restrict__ lse,
-                      const T* __restrict__ dout, float* __restrict__ delta, float* __restrict__ dq,
+                      const OT* __restrict__ o, const float* __restrict__ lse,
+                      const T* __restrict__ dout, float* __restrict__ delta, OT* __restrict__ dq,
                       int Hq, int Hkv, int N, int causal, float scale) {
     __shared__ float Ks[kGenTile][D];
     __shared__ float Vs[kGenTile][D];
@@ -182,7 +184,7 @@ bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     float Di = 0.f;
     if (i < N) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) Di = fmaf(dor[c], o[qrow * D + c], Di);
+        for (int c = 0; c < D; ++c) Di = fmaf(dor[c], load_as_f32(o + qrow * D + c), Di);
         delta[qrow] = Di;
     }
     const int last_row = min(N, (int)(blockIdx.x + 1) * kGenRows) - 1;
@@ -215,69 +217,63 @@ bwd_dq_generic_kernel(const T* __restrict__ q, const T* __restrict__ k, const T*
     }
     if (i < N) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) dq[qrow * D + c] = scale * dqr[c];
+        for (int c = 0; c < D; ++c) store_out1(dq + qrow * D + c, scale * dqr[c]);
     }
 }
 
 // ---------------------------------------------------------------- launchers
-template <typename T, int D>
+template <typename T, typename OT, int D>
 static hipError_t launch_fwd_generic_t(const AttnArgs& a, hipStream_t st) {
     dim3 grid((a.N + kGenRows - 1) / kGenRows, a.B * a.Hq);
-    hipLaunchKernelGGL((fwd_generic_kernel<T, D>), grid, dim3(kGenRows), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.o, a.lse,
+    hipLaunchKernelGGL((fwd_generic_kernel<T, OT, D>), grid, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (OT*)a.o, a.lse,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename OT, int D>
 static hipError_t launch_bwd_generic_dq_t(const AttnArgs& a, hipStream_t st) {
     dim3 gq((a.N + kGenRows - 1) / kGenRows, a.B * a.Hq);
-    hipLaunchKernelGGL((bwd_dq_generic_kernel<T, D>), gq, dim3(kGenRows), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.o,
-                       (const float*)a.lse, (const T*)a.dout, (float*)a.workspace, a.dq,
+    hipLaunchKernelGGL((bwd_dq_generic_kernel<T, OT, D>), gq, dim3(kGenRows), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (const OT*)a.o,
+                       (const float*)a.lse, (const T*)a.dout, (float*)a.workspace, (OT*)a.dq,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale);
     return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, typename OT, int D>
 static hipError_t launch_bwd_generic_dkdv_t(const AttnArgs& a, hipStream_t st) {
     dim3 gkv((a.N + kGenRows - 1) / kGenRows, a.B * a.Hkv);
-    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, D>), gkv, dim3(kGenRows), 0, st,
+    hipLaunchKernelGGL((bwd_dkdv_generic_kernel<T, OT, D>), gkv, dim3(kGenRows), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (const float*)a.lse,
-                       (const T*)a.dout, (const float*)a.workspace, a.dk, a.dv,
+                       (const T*)a.dout, (const float*)a.workspace, (OT*)a.dk, (OT*)a.dv,
                        a.Hq, a.Hkv, a.N, a.causal, a.scale);
     return hipGetLastError();
 }
 
-#define TCA_DISPATCH_D(D_, FN, ...)                                   \
-    switch (D_) {                                                     \
-        case 16: return FN<16>(__VA_ARGS__);                          \
-        case 32: return FN<32>(__VA_ARGS__);                          \
-        case 64: return FN<64>(__VA_ARGS__);                          \
-        case 128: return FN<128>(__VA_ARGS__);                        \
-        default: return hipErrorInvalidValue;                         \
-    }
+// (input type, output type, head dimension) -> one instantiation
+#define TCA_DISPATCH(A_, ST_, LAUNCH)                                                        \
+    do {                                                                                     \
+        const bool in32 = (A_).dtype == ATTN_F32, out32 = (A_).out_dtype == ATTN_F32;         \
+        switch ((A_).d) {                                                                    \
+            case 16:                                                                         \
+                return in32 ? (out32 ? LAUNCH<float, float, 16>(A_, ST_) : LAUNCH<float, bf16_t, 16>(A_, ST_))   \
+                            : (out32 ? LAUNCH<bf16_t, float, 16>(A_, ST_) : LAUNCH<bf16_t, bf16_t, 16>(A_, ST_)); \
+            case 32:                                                                         \
+                return in32 ? (out32 ? LAUNCH<float, float, 32>(A_, ST_) : LAUNCH<float, bf16_t, 32>(A_, ST_))   \
+                            : (out32 ? LAUNCH<bf16_t, float, 32>(A_, ST_) : LAUNCH<bf16_t, bf16_t, 32>(A_, ST_)); \
+            case 64:                                                                         \
+                return in32 ? (out32 ? LAUNCH<float, float, 64>(A_, ST_) : LAUNCH<float, bf16_t, 64>(A_, ST_))   \
+                            : (out32 ? LAUNCH<bf16_t, float, 64>(A_, ST_) : LAUNCH<bf16_t, bf16_t, 64>(A_, ST_)); \
+            case 128:                                                                        \
+                return in32 ? (out32 ? LAUNCH<float, float, 128>(A_, ST_) : LAUNCH<float, bf16_t, 128>(A_, ST_)) \
+                            : (out32 ? LAUNCH<bf16_t, float, 128>(A_, ST_) : LAUNCH<bf16_t, bf16_t, 128>(A_, ST_)); \
+            default: return hipErrorInvalidValue;                                            \
+        }                                                                                    \
+    } while (0)
 
-template <int D> static hipError_t fwd_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<float, D>(a, s); }
-template <int D> static hipError_t fwd_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_fwd_generic_t<bf16_t, D>(a, s); }
-template <int D> static hipError_t dq_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dq_t<float, D>(a, s); }
-template <int D> static hipError_t dq_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dq_t<bf16_t, D>(a, s); }
-template <int D> static hipError_t kv_gen_f32(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dkdv_t<float, D>(a, s); }
-template <int D> static hipError_t kv_gen_bf16(const AttnArgs& a, hipStream_t s) { return launch_bwd_generic_dkdv_t<bf16_t, D>(a, s); }
-
-hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st) {
-    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, fwd_gen_f32, a, st) }
-    TCA_DISPATCH_D(a.d, fwd_gen_bf16, a, st)
-}
-
-hipError_t launch_bwd_generic_dq(const AttnArgs& a, hipStream_t st) {
-    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, dq_gen_f32, a, st) }
-    TCA_DISPATCH_D(a.d, dq_gen_bf16, a, st)
-}
-
-hipError_t launch_bwd_generic_dkdv(const AttnArgs& a, hipStream_t st) {
-    if (a.dtype == ATTN_F32) { TCA_DISPATCH_D(a.d, kv_gen_f32, a, st) }
-    TCA_DISPATCH_D(a.d, kv_gen_bf16, a, st)
-}
+hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st) { TCA_DISPATCH(a, st, launch_fwd_generic_t); }
+hipError_t launch_bwd_generic_dq(const AttnArgs& a, hipStream_t st) { TCA_DISPATCH(a, st, launch_bwd_generic_dq_t); }
+hipError_t launch_bwd_generic_dkdv(const AttnArgs& a, hipStream_t st) { TCA_DISPATCH(a, st, launch_bwd_generic_dkdv_t); }
 
 }  // namespace tca

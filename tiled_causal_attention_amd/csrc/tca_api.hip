@@ -10,15 +10,18 @@ using tca::AttnArgs;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 
 // Shape, flag and scalar checks shared by every entry point.
-attn_status check_sizes(attn_dtype dtype, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
-    if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_EINVAL;
+bool known_dtype(attn_dtype t) { return t == ATTN_F32 || t == ATTN_BF16; }
+
+attn_status check_sizes(attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d, int causal,
+                        float scale) {
+    if (!known_dtype(dtype) || !known_dtype(out_dtype)) return ATTN_EINVAL;
     if (B < 0 || N < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_EINVAL;
     if (Hq % Hkv != 0) return ATTN_EINVAL;
     if (causal != 0 && causal != 1) return ATTN_EINVAL;
@@ -36,11 +39,11 @@ attn_status check_ptrs(std::initializer_list<const void*> ptrs) {
 }
 
 
-attn_status check_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
-                      const float* lse, const void* dO, float* dq, float* dk, float* dv,
+attn_status check_bwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                      const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                       void* ws, size_t ws_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
                       float scale, bool* noop) {
-    attn_status s = check_sizes(dtype, B, Hq, Hkv, N, d, causal, scale);
+    attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
     if (s != ATTN_OK) return s;
     *noop = ((int64_t)B * N == 0);
     if (*noop) return ATTN_OK;
@@ -50,15 +53,16 @@ attn_status check_bwd(attn_dtype dtype, const void* q, const void* k, const void
     return ATTN_OK;
 }
 
-AttnArgs make_args(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
-                   const float* lse, const void* dO, float* dq, float* dk, float* dv, void* ws,
+AttnArgs make_args(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                   const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
                    size_t ws_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
     AttnArgs a;
     a.dtype = dtype;
+    a.out_dtype = out_dtype;
     a.q = q;
     a.k = k;
     a.v = v;
-    a.o = const_cast<float*>(o);
+    a.o = const_cast<void*>(o);
     a.lse = const_cast<float*>(lse);
     a.dout = dO;
     a.dq = dq;
@@ -107,16 +111,16 @@ size_t attn_fwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N,
     return 0;
 }
 
-attn_status attn_fwd(attn_dtype dtype, const void* q, const void* k, const void* v, float* o,
-                     float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+attn_status attn_fwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                     void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                      int N, int d, int causal, float scale, void* stream) {
-    attn_status s = check_sizes(dtype, B, Hq, Hkv, N, d, causal, scale);
+    attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
     if (s != ATTN_OK) return s;
     if ((int64_t)B * N == 0) return ATTN_OK;
     s = check_ptrs({q, k, v, o, lse});
     if (s != ATTN_OK) return s;
     if (workspace_bytes < attn_fwd_workspace_bytes(dtype, B, Hq, Hkv, N, d)) return ATTN_EINVAL;
-    const AttnArgs a = make_args(dtype, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr,
+    const AttnArgs a = make_args(dtype, out_dtype, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr,
                                  workspace, workspace_bytes, B, Hq, Hkv, N, d, causal, scale);
     hipStream_t st = (hipStream_t)stream;
     return from_hip(tca::mfma_path(a) ? tca::launch_fwd_mfma(a, st) : tca::launch_fwd_generic(a, st));
@@ -128,42 +132,41 @@ size_t attn_bwd_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int N,
     return tca::bwd_workspace_size(dtype, B, Hq, N, d);
 }
 
-attn_status attn_bwd_dq(attn_dtype dtype, const void* q, const void* k, const void* v,
-                                const float* o, const float* lse, const void* dO, float* dq,
-                                float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                                int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                                void* stream) {
+attn_status attn_bwd_dq(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                        int causal, float scale, void* stream) {
     bool noop = false;
-    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+    attn_status s = check_bwd(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
                               Hq, Hkv, N, d, causal, scale, &noop);
     if (s != ATTN_OK || noop) return s;
-    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+    const AttnArgs a = make_args(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
     return run_dq(a, (hipStream_t)stream);
 }
 
-attn_status attn_bwd_dkdv(attn_dtype dtype, const void* q, const void* k, const void* v,
-                          const float* o, const float* lse, const void* dO, float* dq, float* dk,
-                          float* dv, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
-                          int N, int d, int causal, float scale, void* stream) {
+attn_status attn_bwd_dkdv(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                          const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
+                          int causal, float scale, void* stream) {
     bool noop = false;
-    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+    attn_status s = check_bwd(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
                               Hq, Hkv, N, d, causal, scale, &noop);
     if (s != ATTN_OK || noop) return s;
-    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+    const AttnArgs a = make_args(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
     return run_dkdv(a, (hipStream_t)stream);
 }
 
-attn_status attn_bwd(attn_dtype dtype, const void* q, const void* k, const void* v, const float* o,
-                     const float* lse, const void* dO, float* dq, float* dk, float* dv,
+attn_status attn_bwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d,
                      int causal, float scale, void* stream) {
     bool noop = false;
-    attn_status s = check_bwd(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
+    attn_status s = check_bwd(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes, B,
                               Hq, Hkv, N, d, causal, scale, &noop);
     if (s != ATTN_OK || noop) return s;
-    const AttnArgs a = make_args(dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
+    const AttnArgs a = make_args(dtype, out_dtype, q, k, v, o, lse, dO, dq, dk, dv, workspace, workspace_bytes,
                                  B, Hq, Hkv, N, d, causal, scale);
     hipStream_t st = (hipStream_t)stream;
     s = run_dq(a, st);

@@ -240,6 +240,34 @@ __device__ __forceinline__ TileMap map_workgroup(int w, int nqt, int units, int 
     return m;
 }
 
+// Output element stores: float32 as is, bfloat16 rounded to nearest even
+// (v_cvt_pk_bf16_f32). store_out4 writes 4 consecutive elements (16 or 8 bytes).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    bf16x2 h = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ void store_out4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store_out4(bf16_t* p, f32x4 v) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    *reinterpret_cast<u32x2*>(p) = u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+__device__ __forceinline__ void store_out1(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_out1(bf16_t* p, float v) {
+    *p = (bf16_t)(pack_bf16(v, 0.f) & 0xffffu);
+}
+// Eight consecutive elements (float32 or bfloat16) at p -> float32.
+__device__ __forceinline__ void load8_f32(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+    x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+    x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+__device__ __forceinline__ void load8_f32(const bf16_t* p, float (&x)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+}
+
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p);
 template <>

@@ -11,16 +11,17 @@
 namespace tca {
 
 struct AttnArgs {
-    attn_dtype dtype;
+    attn_dtype dtype;      // q, k, v, dO
+    attn_dtype out_dtype;  // o, dq, dk, dv
     const void* q;
     const void* k;
     const void* v;
-    float* o;            // forward output; backward input
+    void* o;             // forward output; backward input
     float* lse;          // forward output; backward input
     const void* dout;
-    float* dq;
-    float* dk;
-    float* dv;
+    void* dq;
+    void* dk;
+    void* dv;
     void* workspace;
     size_t workspace_bytes;
     int B, Hq, Hkv, N, d, causal;
