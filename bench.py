@@ -8,6 +8,7 @@ all on torch's current stream, inputs resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa] [--out-dtype f32|bf16]
     python bench.py --all-configs [--oracle]     # per-workload report, see below
+    python bench.py --decode                     # few-query attention over a K/V cache
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
 N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
@@ -69,6 +70,8 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="per-workload report (median/p10/p90) instead of the one-line benchmark")
     p.add_argument("--oracle", action="store_true", help="with --all-configs: time the oracle per workload")
+    p.add_argument("--decode", action="store_true",
+                   help="one JSON line per decode workload (few queries over a K/V cache) instead")
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                    help="element type of o, dq, dk, dv (lse is always float32)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -268,6 +271,54 @@ def all_configs(args):
     print(json.dumps({"clocks_after": shader_clocks()}), flush=True)
 
 
+def decode_report(args):
+    """Few-query attention over a K/V cache: HBM-bound, so reported as GB/s of the
+    minimum traffic (K and V once, Q, O, LSE) against the 8 TB/s HBM peak. Each
+    repetition (both kernels of a call: key splits, then their merge) is bracketed
+    by HIP events on the launch stream; median over the repetitions."""
+    import numpy as np
+    import oracle
+    out_dt = OUT_DTYPES[args.out_dtype]
+    for name, s in workloads.DECODE_CONFIGS.items():
+        inputs = workloads.make_decode_inputs(s)
+        q, k, v = (t.cuda() for t in inputs)
+        o = torch.empty((s.B, s.Hq, s.Nq, s.d), dtype=out_dt, device=q.device)
+        lse = torch.empty((s.B, s.Hq, s.Nq), dtype=torch.float32, device=q.device)
+        nws = int(tca.lib().attn_decode_workspace_bytes(tca.ATTN_BF16 if s.dtype == "bf16" else tca.ATTN_F32,
+                                                        s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        causal, scale = bool(s.causal), s.scale
+        for _ in range(20):
+            tca.attn_decode(q, k, v, causal, scale, out=(o, lse), workspace=ws)
+        reps = 200
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            tca.attn_decode(q, k, v, causal, scale, out=(o, lse), workspace=ws)
+            e1.record()
+        torch.cuda.synchronize()
+        t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+        med = float(np.median(t))
+        nbytes = s.min_bytes(2 if args.out_dtype == "bf16" else 4)
+        ro, rl = oracle.attn_decode(*inputs, s.causal, s.scale)
+        t0 = time.perf_counter()
+        oracle.attn_decode(*inputs, s.causal, s.scale)
+        t_or = time.perf_counter() - t0
+        rec = {"workload": name, "B": s.B, "Hq": s.Hq, "Hkv": s.Hkv, "Nq": s.Nq, "Nk": s.Nk, "d": s.d,
+               "dtype": s.dtype, "out_dtype": args.out_dtype, "causal": s.causal, "reps": reps,
+               "median_ms": med, "p10_ms": float(np.percentile(t, 10)), "p90_ms": float(np.percentile(t, 90)),
+               "min_hbm_bytes": nbytes, "gb_per_s": nbytes / (med * 1e-3) / 1e9,
+               "frac_hbm_peak": nbytes / (med * 1e-3) / 8e12,
+               "max_abs_o": float(np.abs(o.float().cpu().double().numpy() - ro).max()),
+               "max_abs_lse": float(np.abs(lse.cpu().double().numpy() - rl).max()),
+               "oracle": {"seconds": t_or, "threads": oracle.threads(),
+                          "gb_per_s": nbytes / t_or / 1e9}}
+        print(json.dumps(rec), flush=True)
+        del q, k, v, o, lse, ws
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -281,6 +332,9 @@ def main():
     tca.lib()  # fail loudly if the HIP library is missing
     if args.all_configs:
         all_configs(args)
+        return
+    if args.decode:
+        decode_report(args)
         return
 
     s = workloads.CONFIGS[args.workload]

@@ -162,6 +162,38 @@ attn_status attn_bwd_dkdv(attn_dtype dtype, attn_dtype out_dtype,
                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           void* stream);
 
+/* Workspace bytes attn_decode needs for these sizes: the per-split partial
+ * outputs and log-sum-exps when the keys are split (nsplit * B*Hq*Nq * (d + 1)
+ * floats, each part rounded up to 256 bytes), else 0. A function of the sizes
+ * only; 0 for invalid sizes. */
+size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/* Few-query attention over a key/value cache (decode): o and lse for Nq query
+ * rows that are the LAST Nq positions of a sequence of Nk tokens, whose keys
+ * and values are all in k and v. This is the forward used for inference (the
+ * blog page's FAQ: inference works and runs on 8 GB cards), one or a few new
+ * tokens per step against the cache.
+ *   q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d] in `dtype`; o [B,Hq,Nq,d] in
+ *   `out_dtype`; lse [B,Hq,Nq] float32 (natural log), fully overwritten.
+ *   Query row i sits at sequence position Nk - Nq + i: causally it sees keys
+ *   j <= Nk - Nq + i (bottom-right alignment); causal = 0 sees all Nk keys.
+ *   With Nq = Nk the result is attn_fwd's (up to rounding order).
+ *   GQA head map, scale and the definitions of o and lse as for attn_fwd.
+ * The keys are split into ranges processed in parallel; each writes a partial
+ * output and its log-sum-exp into `workspace` (at least
+ * attn_decode_workspace_bytes(...) bytes of device memory, 16-byte aligned;
+ * NULL allowed when that is 0), and a second kernel merges them through the
+ * log-sum-exps. Arithmetic is float32 on the vector units for every dtype.
+ * Sizes: B >= 0, Nq >= 0 (B*Nq == 0 is a no-op), Nq <= Nk, Hq % Hkv == 0,
+ * d in {16, 32, 64, 128}, (Nk+256)*d*4 < 2^31; otherwise ATTN_EINVAL (or
+ * ATTN_EUNSUPPORTED for d). Results are bitwise reproducible. */
+attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype,
+                        const void* q, const void* k, const void* v,
+                        void* o, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

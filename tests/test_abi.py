@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
                      "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_workspace_bytes",
-                     "attn_abi_version"):
+                     "attn_abi_version", "attn_decode", "attn_decode_workspace_bytes"):
         assert required in names
 
 
@@ -197,3 +197,46 @@ def test_python_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tca, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         tca.lib()
+
+
+def dec(L, dtype=BF16, out_dtype=F32, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=64, causal=1, scale=0.125,
+        q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 20):
+    return L.attn_decode(dtype, out_dtype, q, k, v, o, lse, ws, wsb, B, Hq, Hkv, Nq, Nk, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=4), EINVAL),
+    (dict(out_dtype=3), EINVAL),
+    (dict(B=-1), EINVAL),
+    (dict(Nq=-1), EINVAL),
+    (dict(Nq=65, Nk=64), EINVAL),              # more queries than cached positions
+    (dict(Hq=6, Hkv=4), EINVAL),
+    (dict(causal=2), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(Nk=1 << 22, d=128), EINVAL),         # K/V byte offsets of a head pass 2^31
+    (dict(d=80), EUNSUP),
+    (dict(q=None), EINVAL),
+    (dict(k=FAKE + 8), EINVAL),
+    (dict(o=None), EINVAL),
+    (dict(lse=FAKE + 4), EINVAL),
+    (dict(Nk=4096, ws=None), EINVAL),          # split keys need the workspace
+    (dict(Nk=4096, wsb=64), EINVAL),
+    (dict(Nk=4096, ws=FAKE + 8), EINVAL),
+])
+def test_decode_rejects(L, kw, want):
+    assert dec(L, **kw) == want
+
+
+def test_decode_noops_and_workspace(L):
+    nul = dict(q=None, k=None, v=None, o=None, lse=None, ws=None, wsb=0)
+    assert dec(L, B=0, **nul) == OK
+    assert dec(L, Nq=0, **nul) == OK
+    assert dec(L, B=0, causal=3, **nul) == EINVAL
+    # one split: no workspace; many splits: partial outputs and LSEs, 256-byte parts
+    assert L.attn_decode_workspace_bytes(BF16, 1, 2, 1, 1, 64, 64) == 0
+    n = L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 1, 1024, 64)
+    rows = 8 * 12
+    assert n > 0 and n % 256 == 0
+    nsplit = round(n / (rows * 64 * 4 + rows * 4))
+    assert n == ((nsplit * rows * 64 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
+    assert L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 2, 1, 64) == 0   # invalid: Nq > Nk

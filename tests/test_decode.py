@@ -1,0 +1,135 @@
+"""GPU parity of few-query attention over a key/value cache (attn_decode),
+through the C ABI, against the float64 oracle's attn_decode.
+
+Query row i of Nq is sequence position Nk - Nq + i and, causally, sees keys
+j <= Nk - Nq + i. Tolerances per output tensor (o, lse): float32 inputs and
+outputs max |x - ref| <= 1e-4; bfloat16 inputs max |x - ref| <= 2e-2 and
+||x - ref||_2 / ||ref||_2 <= 1e-2; bfloat16 outputs add half a bfloat16 ulp
+(<= 2^-8 |x|) per element. The kernels compute in float32 from exactly
+widened inputs, so the errors seen are float32 rounding, far inside these.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tiled_causal_attention_amd as tca
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tca.lib()
+    yield
+
+
+def check(name, got, ref, in_dtype, out_bf16, ctx):
+    g = got.float().cpu().double().numpy()
+    assert np.isfinite(g).all(), f"{ctx} {name}: non-finite"
+    diff = np.abs(g - ref)
+    base = 1e-4 if in_dtype == "f32" and not out_bf16 else 2e-2
+    bound = base + (2.0 ** -8 * np.maximum(np.abs(g), np.abs(ref)) if out_bf16 else 0.0)
+    if diff.size:
+        w = int(np.argmax(diff / bound))
+        assert diff.flat[w] <= np.broadcast_to(bound, diff.shape).flat[w], \
+            f"{ctx} {name}: |x - ref| {diff.flat[w]:.3e} at ref {ref.flat[w]:.4f}"
+    if in_dtype == "bf16" or out_bf16:
+        den = float(np.linalg.norm(ref))
+        rel = float(np.linalg.norm(g - ref)) / den if den > 0 else 0.0
+        assert rel <= 1e-2, f"{ctx} {name}: rel rms {rel:.3e}"
+    return float(diff.max()) if diff.size else 0.0
+
+
+def run(s, out_dtype=torch.float32, seed=None):
+    q, k, v = workloads.make_decode_inputs(s, seed)
+    qd, kd, vd = (t.cuda() for t in (q, k, v))
+    nan = float("nan")
+    o = torch.full((s.B, s.Hq, s.Nq, s.d), nan, dtype=out_dtype, device="cuda")
+    lse = torch.full((s.B, s.Hq, s.Nq), nan, device="cuda")
+    tca.attn_decode(qd, kd, vd, causal=bool(s.causal), scale=s.scale, out=(o, lse))
+    torch.cuda.synchronize()
+    return (q, k, v), o, lse
+
+
+def parity(s, out_dtype=torch.float32):
+    (q, k, v), o, lse = run(s, out_dtype)
+    ro, rl = oracle.attn_decode(q, k, v, s.causal, s.scale)
+    ctx = f"decode {s.B,s.Hq,s.Hkv,s.Nq,s.Nk,s.d} {s.dtype} causal={s.causal} out={out_dtype}"
+    ob = out_dtype == torch.bfloat16
+    return check("o", o, ro, s.dtype, ob, ctx), check("lse", lse, rl, s.dtype, False, ctx)
+
+
+SHAPES = [
+    # B, Hq, Hkv, Nq, Nk, d, dtype
+    (1, 2, 1, 1, 1, 64, "bf16"),       # one cached key
+    (2, 6, 2, 1, 37, 64, "bf16"),      # ragged cache, GQA group 3
+    (8, 12, 4, 1, 1024, 64, "bf16"),   # several key splits
+    (2, 12, 12, 1, 700, 64, "bf16"),   # MHA
+    (1, 8, 1, 1, 2000, 128, "bf16"),   # group 8 (rows fill a chunk of 8)
+    (2, 32, 4, 2, 3000, 64, "bf16"),   # 16 rows: two row chunks
+    (3, 8, 1, 4, 513, 128, "bf16"),    # 32 rows, Nq = 4 (speculative decode)
+    (1, 4, 2, 5, 5, 32, "bf16"),       # Nq = Nk: the full causal forward
+    (2, 6, 3, 3, 77, 16, "bf16"),
+    (1, 2, 2, 64, 64, 64, "bf16"),     # Nq = Nk = 64
+    (2, 4, 2, 1, 333, 16, "f32"),
+    (1, 6, 2, 3, 150, 64, "f32"),
+    (2, 4, 1, 2, 1000, 128, "f32"),
+    (1, 2, 1, 17, 17, 32, "f32"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype", SHAPES)
+@pytest.mark.parametrize("causal", [1, 0])
+def test_decode_small(B, Hq, Hkv, Nq, Nk, d, dtype, causal):
+    s = workloads.make_decode_shape(B, Hq, Hkv, Nq, Nk, d, dtype=dtype, seed=Nk * 7 + d + Nq, causal=causal)
+    parity(s)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d,dtype", [SHAPES[2], SHAPES[4], SHAPES[6], SHAPES[12]])
+def test_decode_bf16_out(B, Hq, Hkv, Nq, Nk, d, dtype):
+    s = workloads.make_decode_shape(B, Hq, Hkv, Nq, Nk, d, dtype=dtype, seed=11 + Nk)
+    parity(s, torch.bfloat16)
+
+
+def test_decode_peaked_softmax():
+    # the stress distribution (Q, K ~ N(0, 3^2)) over a long cache: the running
+    # max moves often and the lazy rescale must keep every split exact
+    s = workloads.make_decode_shape(2, 16, 4, 2, 4096, 128, seed=21, qk_std=3.0)
+    parity(s)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.DECODE_CONFIGS))
+def test_decode_named_full_size(name):
+    print(f"[decode parity] {name}", flush=True)
+    parity(workloads.DECODE_CONFIGS[name])
+
+
+def test_decode_bf16_out_is_rounded_f32():
+    s = workloads.make_decode_shape(2, 12, 4, 3, 900, 64, seed=5)
+    q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
+    o32, l32 = tca.attn_decode(q, k, v, scale=s.scale)
+    o16, l16 = tca.attn_decode(q, k, v, scale=s.scale, out_dtype=torch.bfloat16)
+    assert torch.equal(l16, l32) and torch.equal(o16, o32.to(torch.bfloat16))
+
+
+def test_decode_deterministic_and_stream():
+    s = workloads.DECODE_CONFIGS["decode_gpt2_gqa"]
+    q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
+    o1, l1 = tca.attn_decode(q, k, v, scale=s.scale)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        o2, l2 = tca.attn_decode(q, k, v, scale=s.scale)
+    st.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_empty():
+    q = torch.empty(2, 4, 0, 64, dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros(2, 2, 10, 64, dtype=torch.bfloat16, device="cuda")
+    o, lse = tca.attn_decode(q, k, k)
+    assert o.shape == (2, 4, 0, 64) and lse.shape == (2, 4, 0)

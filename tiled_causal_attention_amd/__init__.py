@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         getattr(L, name).argtypes = bwd_args
         getattr(L, name).restype = i
+    L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    L.attn_decode.restype = i
     _lib = L
     return L
 
@@ -176,3 +180,36 @@ def attn_bwd_dq(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=N
 def attn_bwd_dkdv(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale=None):
     """Second backward phase (dk, dv; reads D from the workspace)."""
     _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
+
+
+def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Few-query attention over a cache: q [B,Hq,Nq,d] are the last Nq positions of
+    the sequence whose keys/values k, v [B,Hkv,Nk,d] hold. Returns (o [B,Hq,Nq,d]
+    in out_dtype (float32 unless given, or out[0]'s dtype), lse float32 [B,Hq,Nq])."""
+    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+        raise ValueError("q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    scale = default_scale(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=out_dtype or torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if out_dtype is not None and o.dtype != out_dtype:
+            raise TypeError(f"out[0] is {o.dtype}, out_dtype is {out_dtype}")
+    if lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    L = lib()
+    ws_bytes = int(L.attn_decode_workspace_bytes(dt, B, Hq, Hkv, Nq, Nk, d))
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    wsn = workspace.numel() if workspace is not None else 0
+    _check(L.attn_decode(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                         _ptr(workspace), wsn, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+                         _stream(q.device)))
+    return o, lse

@@ -36,10 +36,10 @@ namespace tca {
 
 namespace dec {
 constexpr int kWaves = 4;        // waves per workgroup; each runs its own work item
-constexpr int kUnroll = 4;       // keys per slot loaded ahead of the math
+constexpr int kUnroll = 2;       // keys per slot per batch (two batches in flight)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 constexpr int kTargetWaves = 4096;   // work items aimed for (4 per SIMD)
-constexpr int kMinSplitKeys = 256;   // keys per split at least
+constexpr int kMinSplitKeys = 64;    // keys per split at least
 }  // namespace dec
 
 // DPP lane moves within rows of 16 lanes (gfx9 encodings).
@@ -97,7 +97,7 @@ __global__ void __launch_bounds__(64 * dec::kWaves)
 decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
                     OT* __restrict__ o, float* __restrict__ lse, float* __restrict__ opart,
                     float* __restrict__ lpart, int Hq, int Hkv, int Nq, int Nk, int causal, float scale,
-                    int nrc, int nsplit, int split_len, int nitems) {
+                    int nrc, int nsplit, int split_len, int nitems, int nrows) {
     using namespace dec;
     constexpr int CPR = D / 8;        // lanes per key row
     constexpr int KS = 64 / CPR;      // key slots per wave
@@ -109,17 +109,34 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     const int b = unit / Hkv, hkv = unit % Hkv;
     const int G = Hq / Hkv, R = G * Nq;
     const int slot = lane / CPR, c = lane % CPR;
-    const int rows_total = (int)((size_t)gridDim.y * 0) + 0;   // (unused; rows indexed globally below)
-    (void)rows_total;
     const float sl2 = scale * kLog2e;
+
+    const size_t kvoff = (size_t)unit * Nk * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * sizeof(T)));
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff, (uint32_t)((size_t)Nk * D * sizeof(T)));
+    // one batch: kUnroll keys per slot, i.e. KS * kUnroll consecutive keys
+    constexpr int STEP = KS * kUnroll;
+    auto load_batch = [&](Chunk<T> (&kc)[kUnroll], Chunk<T> (&vc)[kUnroll], int base) {
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            // rows past Nk read as zero through the buffer resource; they are masked below
+            const uint32_t off = (uint32_t)(((base + u * KS + slot) * D + 8 * c) * (int)sizeof(T));
+            kc[u].load(krs, off);
+            vc[u].load(vrs, off);
+        }
+    };
+    // the split's first batch goes out before the query rows are read (every key
+    // of it lies below Nk + STEP, inside the buffer or reading zero past it)
+    const int k0 = split * split_len;
+    const int k1 = min(Nk, k0 + split_len);
+    Chunk<T> ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
+    load_batch(ka, va, k0);
 
     // this lane's chunk of every row's query, pre-scaled to log2 units
     float qr[RM][8];
     int lim[RM];          // keys j < lim[r] are visible to row r in this split
     size_t grow[RM];      // global row index (b, hq, i) of row r
     bool ok[RM];
-    const int k0 = split * split_len;
-    const int k1 = min(Nk, k0 + split_len);
     int kend = k0;        // keys this wave must visit
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
@@ -130,12 +147,12 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
         const int pos = Nk - Nq + i;
         lim[r] = !ok[r] ? k0 : (causal ? min(k1, pos + 1) : k1);
         kend = max(kend, lim[r]);
+        Chunk<T> qc;   // 8 consecutive elements: one (bf16) or two (float) 16-byte loads
+        qc.load(make_rsrc(q + grow[r] * D, (uint32_t)(D * sizeof(T))), (uint32_t)(8 * c * (int)sizeof(T)));
         float x[8];
-        const T* qp = q + grow[r] * D + 8 * c;
+        qc.unpack(x);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = ok[r] ? load_as_f32(qp + t) * sl2 : 0.f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qr[r][t] = x[t];
+        for (int t = 0; t < 8; ++t) qr[r][t] = ok[r] ? x[t] * sl2 : 0.f;
     }
 
     float m[RM], l[RM], acc[RM][8];
@@ -147,46 +164,67 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
         for (int t = 0; t < 8; ++t) acc[r][t] = 0.f;
     }
 
-    const size_t kvoff = (size_t)unit * Nk * D;
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * sizeof(T)));
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff, (uint32_t)((size_t)Nk * D * sizeof(T)));
-
-    for (int base = k0; base < kend; base += KS * kUnroll) {
-        Chunk<T> kc[kUnroll], vc[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            // rows past Nk read as zero through the buffer resource; they are masked below
-            const uint32_t off = (uint32_t)(((base + u * KS + slot) * D + 8 * c) * (int)sizeof(T));
-            kc[u].load(krs, off);
-            vc[u].load(vrs, off);
-        }
+    // a batch's scores first (independent products), then one rescale check per
+    // batch, then the probabilities and the output columns
+    auto compute_batch = [&](const Chunk<T> (&kc)[kUnroll], const Chunk<T> (&vc)[kUnroll], int base) {
+        float sc[kUnroll][RM];
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int j = base + u * KS + slot;
-            float kf[8], vf[8];
+            float kf[8];
             kc[u].unpack(kf);
-            vc[u].unpack(vf);
 #pragma unroll
             for (int r = 0; r < RM; ++r) {
                 float part = 0.f;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) part = fmaf(qr[r][t], kf[t], part);
-                float s = slot_sum<CPR>(part);
-                s = (j < lim[r]) ? s : -INFINITY;
-                if (__any(s > m[r] + kTau)) {
-                    const float mn = vmax(m[r], s);
-                    const float alpha = fast_exp2(m[r] - mn);
-                    l[r] *= alpha;
+                const float s = slot_sum<CPR>(part);
+                sc[u][r] = (j < lim[r]) ? s : -INFINITY;
+            }
+        }
+        bool grow_max = false;
+        float mb[RM];
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) acc[r][t] *= alpha;
-                    m[r] = mn;
-                }
-                const float p = fast_exp2(s - m[r]);
+        for (int r = 0; r < RM; ++r) {
+            mb[r] = sc[0][r];
+#pragma unroll
+            for (int u = 1; u < kUnroll; ++u) mb[r] = vmax(mb[r], sc[u][r]);
+            grow_max |= mb[r] > m[r] + kTau;
+        }
+        if (__any(grow_max)) {
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const float mn = vmax(m[r], mb[r]);
+                const float alpha = fast_exp2(m[r] - mn);   // 1 where the max did not move
+                l[r] *= alpha;
+#pragma unroll
+                for (int t = 0; t < 8; ++t) acc[r][t] *= alpha;
+                m[r] = mn;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float vf[8];
+            vc[u].unpack(vf);
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+                const float p = fast_exp2(sc[u][r] - m[r]);
                 l[r] += p;
 #pragma unroll
                 for (int t = 0; t < 8; ++t) acc[r][t] = fmaf(p, vf[t], acc[r][t]);
             }
         }
+    };
+    // two register batches in turn: the loads of batch n + 1 are in flight while
+    // batch n is computed (the wait for batch n leaves the younger loads pending)
+    for (int base = k0; base < kend;) {
+        if (base + STEP < kend) load_batch(kb, vb, base + STEP);
+        compute_batch(ka, va, base);
+        base += STEP;
+        if (base >= kend) break;
+        if (base + STEP < kend) load_batch(ka, va, base + STEP);
+        compute_batch(kb, vb, base);
+        base += STEP;
     }
 
     // merge the KS slots of the wave (lanes c, c + CPR, c + 2 CPR, ... hold the same
@@ -206,8 +244,6 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     }
 
     if (slot != 0) return;
-    const size_t rows_all = (size_t)(gridDim.x == 0 ? 0 : 1) * 0;   // placeholder removed below
-    (void)rows_all;
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
         if (!ok[r]) continue;
@@ -222,10 +258,159 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
             store_out4(orow + 4, hi4);
             if (c == 0) lse[grow[r]] = l2 * kLn2;
         } else {
-            const size_t nrows = (size_t)(unit / Hkv + 1) * 0;   // (see launcher: rows passed implicitly)
-            (void)nrows;
+            const size_t prow = (size_t)split * nrows + grow[r];
+            *reinterpret_cast<f32x4*>(opart + prow * D + 8 * c) = lo4;
+            *reinterpret_cast<f32x4*>(opart + prow * D + 8 * c + 4) = hi4;
+            if (c == 0) lpart[prow] = l2;
         }
     }
+}
+
+// Merge of the splits of one row: LSE = log2 sum_s 2^LSE_s (log2 units in lpart),
+// O = sum_s 2^(LSE_s - LSE) O_s. One workgroup of 4 waves per row, one row's
+// merge being a short reduction whose cost is load latency: thread t takes the
+// maximum and weight sum over splits t, t + 256, ... (workgroup reductions
+// through LDS), then wave w accumulates columns 2 lane, 2 lane + 1 over splits
+// w, w + 4, ..., with all of its loads issued before the adds; the four partial
+// columns are summed through LDS. Split 0 holds key 0, visible to every row, so
+// the maximum is finite.
+constexpr int kMergeThreads = 256;
+template <typename OT, int D>
+__global__ void __launch_bounds__(kMergeThreads)
+decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ lpart, OT* __restrict__ o,
+                    float* __restrict__ lse, int nrows, int nsplit) {
+    constexpr int NW = kMergeThreads / 64;
+    constexpr int MAXS = 256;                 // splits per row at most (decode_plan caps it)
+    constexpr int PER_WAVE = MAXS / NW;       // splits a wave may own
+    __shared__ float red[NW];
+    __shared__ float wsh[MAXS];
+    __shared__ float part[NW][D];
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const float ls = tid < nsplit ? lpart[(size_t)tid * nrows + row] : -INFINITY;
+    float mx = ls;
+#pragma unroll
+    for (int st = 32; st > 0; st >>= 1) mx = vmax(mx, __shfl_xor(mx, st, 64));
+    if (lane == 0) red[w] = mx;
+    __syncthreads();
+    mx = vmax(vmax(red[0], red[1]), vmax(red[2], red[3]));
+    const float wt = tid < nsplit ? fast_exp2(ls - mx) : 0.f;
+    wsh[tid] = wt;
+    float sum = wt;
+#pragma unroll
+    for (int st = 32; st > 0; st >>= 1) sum += __shfl_xor(sum, st, 64);
+    __syncthreads();
+    if (lane == 0) red[w] = sum;
+    __syncthreads();
+    sum = (red[0] + red[1]) + (red[2] + red[3]);
+    const bool col = 2 * lane < D;
+    float x0[PER_WAVE], x1[PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int sidx = w + NW * i;
+        const bool on = col && sidx < nsplit;
+        const float* src = opart + ((size_t)(on ? sidx : 0) * nrows + row) * D + (col ? 2 * lane : 0);
+        x0[i] = on ? src[0] : 0.f;
+        x1[i] = on ? src[1] : 0.f;
+    }
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int sidx = w + NW * i;
+        const float wgt = sidx < nsplit ? wsh[sidx] : 0.f;
+        a0 = fmaf(wgt, x0[i], a0);
+        a1 = fmaf(wgt, x1[i], a1);
+    }
+    if (col) {
+        part[w][2 * lane] = a0;
+        part[w][2 * lane + 1] = a1;
+    }
+    __syncthreads();
+    if (w == 0 && col) {
+        const float inv = 1.f / sum;
+        const float r0 = (part[0][2 * lane] + part[1][2 * lane]) + (part[2][2 * lane] + part[3][2 * lane]);
+        const float r1 = (part[0][2 * lane + 1] + part[1][2 * lane + 1]) +
+                         (part[2][2 * lane + 1] + part[3][2 * lane + 1]);
+        store_out1(o + (size_t)row * D + 2 * lane, r0 * inv);
+        store_out1(o + (size_t)row * D + 2 * lane + 1, r1 * inv);
+    }
+    if (tid == 0) lse[row] = (mx + __log2f(sum)) * kLn2;
+}
+
+// ---------------------------------------------------------------- host side
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    DecodePlan p;
+    const int R = (Hq / Hkv) * Nq;
+    p.rm = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
+    p.nrc = (R + p.rm - 1) / p.rm;
+    const long long items0 = (long long)B * Hkv * p.nrc;
+    long long want = (dec::kTargetWaves + items0 - 1) / items0;
+    const long long cap = ((long long)Nk + dec::kMinSplitKeys - 1) / dec::kMinSplitKeys;
+    want = want < 1 ? 1 : want;
+    want = want > cap ? cap : want;
+    want = want > 256 ? 256 : want;
+    p.split_len = (int)((((long long)Nk + want - 1) / want + 63) / 64 * 64);
+    if (p.split_len < 64) p.split_len = 64;
+    p.nsplit = (int)(((long long)Nk + p.split_len - 1) / p.split_len);
+    if (p.nsplit < 1) p.nsplit = 1;
+    (void)d;
+    return p;
+}
+
+size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, d);
+    if (p.nsplit <= 1) return 0;
+    const size_t rows = (size_t)B * Hq * Nq;
+    return ws_round((size_t)p.nsplit * rows * d * sizeof(float)) + ws_round((size_t)p.nsplit * rows * sizeof(float));
+}
+
+template <typename T, typename OT, int D, int RM>
+static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    const int nitems = a.B * a.Hkv * p.nrc * p.nsplit;
+    const int nrows = a.B * a.Hq * a.Nq;
+    float* opart = nullptr;
+    float* lpart = nullptr;
+    if (p.nsplit > 1) {
+        opart = static_cast<float*>(a.workspace);
+        lpart = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                         ws_round((size_t)p.nsplit * nrows * D * sizeof(float)));
+    }
+    const dim3 grid((unsigned)((nitems + dec::kWaves - 1) / dec::kWaves));
+    hipLaunchKernelGGL((decode_split_kernel<T, OT, D, RM>), grid, dim3(64 * dec::kWaves), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, (OT*)a.o, a.lse, opart, lpart, a.Hq,
+                       a.Hkv, a.Nq, a.Nk, a.causal, a.scale, p.nrc, p.nsplit, p.split_len, nitems, nrows);
+    if (p.nsplit > 1)
+        hipLaunchKernelGGL((decode_merge_kernel<OT, D>), dim3((unsigned)nrows), dim3(kMergeThreads), 0, st, opart, lpart,
+                           (OT*)a.o, a.lse, nrows, p.nsplit);
+    return hipGetLastError();
+}
+
+template <typename T, typename OT, int D>
+static hipError_t launch_decode_rm(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    switch (p.rm) {
+        case 1: return launch_decode_t<T, OT, D, 1>(a, p, st);
+        case 2: return launch_decode_t<T, OT, D, 2>(a, p, st);
+        case 4: return launch_decode_t<T, OT, D, 4>(a, p, st);
+        default: return launch_decode_t<T, OT, D, 8>(a, p, st);
+    }
+}
+
+template <typename T, typename OT>
+static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    switch (a.d) {
+        case 16: return launch_decode_rm<T, OT, 16>(a, p, st);
+        case 32: return launch_decode_rm<T, OT, 32>(a, p, st);
+        case 64: return launch_decode_rm<T, OT, 64>(a, p, st);
+        case 128: return launch_decode_rm<T, OT, 128>(a, p, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+    const DecodePlan p = decode_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d);
+    const bool in32 = a.dtype == ATTN_F32, out32 = a.out_dtype == ATTN_F32;
+    if (in32) return out32 ? launch_decode_d<float, float>(a, p, st) : launch_decode_d<float, bf16_t>(a, p, st);
+    return out32 ? launch_decode_d<bf16_t, float>(a, p, st) : launch_decode_d<bf16_t, bf16_t>(a, p, st);
 }
 
 }  // namespace tca

@@ -174,4 +174,47 @@ attn_status attn_bwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, cons
     return run_dkdv(a, st);
 }
 
+size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    (void)dtype;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Nq < 1 || Nk < Nq || !supported_d(d)) return 0;
+    return tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+}
+
+attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                        int Nq, int Nk, int d, int causal, float scale, void* stream) {
+    if (!known_dtype(dtype) || !known_dtype(out_dtype)) return ATTN_EINVAL;
+    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_EINVAL;
+    if (Hq % Hkv != 0 || Nq > Nk) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!isfinite(scale)) return ATTN_EINVAL;
+    if ((int64_t)(Nk + 256) * d * 4 >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // byte offsets in a head's K/V
+    if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;
+    if ((int64_t)B * Hkv * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // work items
+    if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+    if ((int64_t)B * Nq == 0) return ATTN_OK;
+    attn_status s = check_ptrs({q, k, v, o, lse});
+    if (s != ATTN_OK) return s;
+    const size_t need = tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+    if (need > 0 && (workspace_bytes < need || workspace == nullptr || !aligned16(workspace))) return ATTN_EINVAL;
+    tca::DecodeArgs a;
+    a.dtype = dtype;
+    a.out_dtype = out_dtype;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    return from_hip(tca::launch_decode(a, (hipStream_t)stream));
+}
+
 }  // extern "C"

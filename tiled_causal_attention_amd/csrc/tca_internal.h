@@ -73,6 +73,28 @@ hipError_t launch_fwd_generic(const AttnArgs& a, hipStream_t st);
 hipError_t launch_bwd_generic_dq(const AttnArgs& a, hipStream_t st);
 hipError_t launch_bwd_generic_dkdv(const AttnArgs& a, hipStream_t st);
 
+// Few-query attention over a cache (decode): q, o [B, Hq, Nq, d]; k, v [B, Hkv, Nk, d].
+struct DecodeArgs {
+    attn_dtype dtype, out_dtype;
+    const void* q;
+    const void* k;
+    const void* v;
+    void* o;
+    float* lse;
+    void* workspace;
+    int B, Hq, Hkv, Nq, Nk, d, causal;
+    float scale;
+};
+// Launch shape of the decode kernels, a function of the sizes only: RM rows per
+// wave (1, 2, 4 or 8), nrc row chunks of a GQA group's G * Nq rows, nsplit key
+// splits of split_len keys (a multiple of 64).
+struct DecodePlan {
+    int rm, nrc, nsplit, split_len;
+};
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
 // matrix-core path: bf16 inputs, d in {64, 128}; same two backward phases
 bool mfma_path(const AttnArgs& a);
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st);

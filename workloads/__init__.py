@@ -94,3 +94,65 @@ def make_inputs(s: Shape, seed: int | None = None):
         k = k * s.qk_std
     dt = s.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt), do.to(dt)
+
+
+# ---------------------------------------------------------------- decode
+# Few-query attention over a cache: Nq new query rows (the last Nq positions)
+# against Nk cached keys and values. Recipe: one generator seeded with
+# ``seed``; draw Q [B,Hq,Nq,d], K [B,Hkv,Nk,d], V [B,Hkv,Nk,d] in that order,
+# each torch.randn float32; multiply Q and K by qk_std; round to the dtype.
+@dataclasses.dataclass(frozen=True)
+class DecodeShape:
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    seed: int
+    qk_std: float = 1.0
+    causal: int = 1
+
+    @property
+    def scale(self) -> float:
+        return float(torch.tensor(1.0 / math.sqrt(self.d), dtype=torch.float32).item())
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return {"f32": torch.float32, "bf16": torch.bfloat16}[self.dtype]
+
+    def min_bytes(self, out_bytes: int = 4) -> int:
+        """HBM bytes a decode step must move: K and V once, Q, O and LSE."""
+        el = 2 if self.dtype == "bf16" else 4
+        kv = 2 * self.B * self.Hkv * self.Nk * self.d * el
+        qo = self.B * self.Hq * self.Nq * self.d * (el + out_bytes)
+        return kv + qo + self.B * self.Hq * self.Nq * 4
+
+
+# Decode steps of the two model shapes: the GPT-2-small GQA heads at the
+# pages' context length, and the wide-head shape at its full 8192-token context.
+DECODE_CONFIGS: Dict[str, DecodeShape] = {
+    "decode_gpt2_gqa": DecodeShape("decode_gpt2_gqa", 8, 12, 4, 1, 1024, 64, "bf16", 2001),
+    "decode_wide_d128": DecodeShape("decode_wide_d128", 4, 16, 4, 1, 8192, 128, "bf16", 2002),
+}
+
+
+def make_decode_shape(B, Hq, Hkv, Nq, Nk, d, dtype="bf16", seed=7, qk_std=1.0, causal=1,
+                      name="adhoc_decode") -> DecodeShape:
+    return DecodeShape(name, B, Hq, Hkv, Nq, Nk, d, dtype, seed, qk_std, causal)
+
+
+def make_decode_inputs(s: DecodeShape, seed: int | None = None):
+    """Return (q, k, v) as CPU tensors in the shape's dtype."""
+    g = torch.Generator("cpu")
+    g.manual_seed(s.seed if seed is None else seed)
+    q = torch.randn((s.B, s.Hq, s.Nq, s.d), generator=g, dtype=torch.float32)
+    k = torch.randn((s.B, s.Hkv, s.Nk, s.d), generator=g, dtype=torch.float32)
+    v = torch.randn((s.B, s.Hkv, s.Nk, s.d), generator=g, dtype=torch.float32)
+    if s.qk_std != 1.0:
+        q = q * s.qk_std
+        k = k * s.qk_std
+    dt = s.torch_dtype
+    return q.to(dt), k.to(dt), v.to(dt)
