@@ -30,12 +30,14 @@
 //  * kUnroll keys per slot are loaded ahead of their math (128 bytes per lane
 //    in flight for bf16), enough outstanding loads to cover HBM latency at
 //    2-4 waves per SIMD.
+#include <type_traits>
+
 #include "tca_internal.h"
 
 namespace tca {
 
 namespace dec {
-constexpr int kWaves = 4;        // waves per workgroup; each runs its own work item
+constexpr int kWaves = 1;        // waves per workgroup (each wave runs its own work item)
 constexpr int kUnroll = 2;       // keys per slot per batch (two batches in flight)
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 constexpr int kTargetWaves = 4096;   // work items aimed for (4 per SIMD)
@@ -62,6 +64,13 @@ __device__ __forceinline__ float slot_sum(float x) {
     if constexpr (CPR >= 8) x += dpp<kRowHalfMirror>(x);
     if constexpr (CPR >= 16) x += dpp<kRowMirror>(x);
     return x;
+}
+
+// a.lo * b.lo + a.hi * b.hi + acc over packed bf16 pairs, in float32 (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), acc,
+                                           false);
 }
 
 // One 8-element chunk of a K or V row as raw bits (bf16: 16 bytes; float: 32).
@@ -132,8 +141,12 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     Chunk<T> ka[kUnroll], va[kUnroll], kb[kUnroll], vb[kUnroll];
     load_batch(ka, va, k0);
 
-    // this lane's chunk of every row's query, pre-scaled to log2 units
+    // this lane's chunk of every row's query: bf16 inputs keep the raw pairs for
+    // v_dot2_f32_bf16 (the score is scaled to log2 units after the slot sum);
+    // float inputs keep floats pre-scaled to log2 units
+    constexpr bool kBf16 = std::is_same<T, bf16_t>::value;
     float qr[RM][8];
+    u32x4 qp2[RM];
     int lim[RM];          // keys j < lim[r] are visible to row r in this split
     size_t grow[RM];      // global row index (b, hq, i) of row r
     bool ok[RM];
@@ -149,10 +162,14 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
         kend = max(kend, lim[r]);
         Chunk<T> qc;   // 8 consecutive elements: one (bf16) or two (float) 16-byte loads
         qc.load(make_rsrc(q + grow[r] * D, (uint32_t)(D * sizeof(T))), (uint32_t)(8 * c * (int)sizeof(T)));
-        float x[8];
-        qc.unpack(x);
+        if constexpr (kBf16) {
+            qp2[r] = ok[r] ? qc.w : u32x4{0u, 0u, 0u, 0u};
+        } else {
+            float x[8];
+            qc.unpack(x);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qr[r][t] = ok[r] ? x[t] * sl2 : 0.f;
+            for (int t = 0; t < 8; ++t) qr[r][t] = ok[r] ? x[t] * sl2 : 0.f;
+        }
     }
 
     float m[RM], l[RM], acc[RM][8];
@@ -171,15 +188,28 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
             const int j = base + u * KS + slot;
-            float kf[8];
-            kc[u].unpack(kf);
+            if constexpr (kBf16) {
+                const u32x4 kw = kc[u].w;
 #pragma unroll
-            for (int r = 0; r < RM; ++r) {
-                float part = 0.f;
+                for (int r = 0; r < RM; ++r) {
+                    float part = dot2_bf16(qp2[r].x, kw.x, 0.f);
+                    part = dot2_bf16(qp2[r].y, kw.y, part);
+                    part = dot2_bf16(qp2[r].z, kw.z, part);
+                    part = dot2_bf16(qp2[r].w, kw.w, part);
+                    const float s = slot_sum<CPR>(part) * sl2;
+                    sc[u][r] = (j < lim[r]) ? s : -INFINITY;
+                }
+            } else {
+                float kf[8];
+                kc[u].unpack(kf);
 #pragma unroll
-                for (int t = 0; t < 8; ++t) part = fmaf(qr[r][t], kf[t], part);
-                const float s = slot_sum<CPR>(part);
-                sc[u][r] = (j < lim[r]) ? s : -INFINITY;
+                for (int r = 0; r < RM; ++r) {
+                    float part = 0.f;
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) part = fmaf(qr[r][t], kf[t], part);
+                    const float s = slot_sum<CPR>(part);
+                    sc[u][r] = (j < lim[r]) ? s : -INFINITY;
+                }
             }
         }
         bool grow_max = false;
@@ -287,6 +317,18 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     __shared__ float part[NW][D];
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    // every load of the merge goes out first: the partial columns and the LSEs are
+    // independent, so the merge waits for one round of memory latency
+    const bool col = 2 * lane < D;
+    float x0[PER_WAVE], x1[PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+        const int sidx = w + NW * i;
+        const bool on = col && sidx < nsplit;
+        const float* src = opart + ((size_t)(on ? sidx : 0) * nrows + row) * D + (col ? 2 * lane : 0);
+        x0[i] = on ? src[0] : 0.f;
+        x1[i] = on ? src[1] : 0.f;
+    }
     const float ls = tid < nsplit ? lpart[(size_t)tid * nrows + row] : -INFINITY;
     float mx = ls;
 #pragma unroll
@@ -303,16 +345,6 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     if (lane == 0) red[w] = sum;
     __syncthreads();
     sum = (red[0] + red[1]) + (red[2] + red[3]);
-    const bool col = 2 * lane < D;
-    float x0[PER_WAVE], x1[PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-        const int sidx = w + NW * i;
-        const bool on = col && sidx < nsplit;
-        const float* src = opart + ((size_t)(on ? sidx : 0) * nrows + row) * D + (col ? 2 * lane : 0);
-        x0[i] = on ? src[0] : 0.f;
-        x1[i] = on ? src[1] : 0.f;
-    }
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
