@@ -9,6 +9,7 @@ all on torch's current stream, inputs resident in HBM.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2_gqa] [--out-dtype f32|bf16]
     python bench.py --all-configs [--oracle]     # per-workload report, see below
     python bench.py --decode                     # few-query attention over a K/V cache
+    python bench.py --naive                      # tiled forward against the naive materialised-score one
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
 N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
@@ -70,6 +71,8 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="per-workload report (median/p10/p90) instead of the one-line benchmark")
     p.add_argument("--oracle", action="store_true", help="with --all-configs: time the oracle per workload")
+    p.add_argument("--naive", action="store_true",
+                   help="one JSON line: the forward of the workload, tiled against the naive materialised-score one")
     p.add_argument("--decode", action="store_true",
                    help="one JSON line per decode workload (few queries over a K/V cache) instead")
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
@@ -271,6 +274,40 @@ def all_configs(args):
     print(json.dumps({"clocks_after": shader_clocks()}), flush=True)
 
 
+def naive_report(args):
+    """Forward of one workload (default the headline), the tiled kernel against the
+    unoptimised materialised-score path (S = QK^T in HBM, softmax, PV), both timed by
+    HIP events on the launch stream, median of 50 calls after 5 warm-up calls."""
+    import numpy as np
+    s = workloads.CONFIGS[args.workload]
+    q, k, v, _ = (t.cuda() for t in workloads.make_inputs(s))
+    o = torch.empty((s.B, s.Hq, s.N, s.d), device=q.device)
+    lse = torch.empty((s.B, s.Hq, s.N), device=q.device)
+    ws = torch.empty(int(tca.lib().attn_fwd_naive_workspace_bytes(s.B, s.Hq, s.N)), dtype=torch.uint8,
+                     device=q.device)
+    causal, scale = bool(s.causal), s.scale
+    calls = {"tiled": lambda: tca.attn_fwd(q, k, v, causal, scale, out=(o, lse)),
+             "naive": lambda: tca.attn_fwd_naive(q, k, v, causal, scale, out=(o, lse), workspace=ws)}
+    med = {}
+    for name, fn in calls.items():
+        for _ in range(5):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        med[name] = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    ff = s.flops_fwd()
+    print(json.dumps({"workload": s.name, "B": s.B, "Hq": s.Hq, "Hkv": s.Hkv, "N": s.N, "d": s.d,
+                      "tiled_fwd_ms": med["tiled"], "naive_fwd_ms": med["naive"],
+                      "tiled_tflops": ff / (med["tiled"] * 1e-3) / 1e12,
+                      "naive_tflops": ff / (med["naive"] * 1e-3) / 1e12,
+                      "speedup": med["naive"] / med["tiled"], "score_matrix_bytes": ws.numel()}), flush=True)
+
+
 def decode_report(args):
     """Few-query attention over a K/V cache: HBM-bound, so reported as GB/s of the
     minimum traffic (K and V once, Q, O, LSE) against the 8 TB/s HBM peak. Each
@@ -335,6 +372,9 @@ def main():
         return
     if args.decode:
         decode_report(args)
+        return
+    if args.naive:
+        naive_report(args)
         return
 
     s = workloads.CONFIGS[args.workload]

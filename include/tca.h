@@ -162,6 +162,25 @@ attn_status attn_bwd_dkdv(attn_dtype dtype, attn_dtype out_dtype,
                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           void* stream);
 
+/* Workspace bytes attn_fwd_naive needs: the score matrix, B*Hq*N*N floats. */
+size_t attn_fwd_naive_workspace_bytes(int B, int Hq, int N);
+
+/* Unoptimised forward, for teaching and as a baseline (the NanoEuler article
+ * lists a "naive", unoptimised version kept to understand every step): the
+ * same o and lse as attn_fwd, computed the obvious way with the whole score
+ * matrix in `workspace` (at least attn_fwd_naive_workspace_bytes(B, Hq, N)
+ * bytes of device memory, 16-byte aligned): S = scale * Q K^T with masked
+ * entries -inf, a row softmax in place (and lse), then O = P V, each step a
+ * plain kernel reading global memory directly, in float32 for every dtype.
+ * Arguments, layouts, sizes and errors as for attn_fwd; also ATTN_EINVAL when
+ * B*Hq*N*N >= 2^39. */
+attn_status attn_fwd_naive(attn_dtype dtype, attn_dtype out_dtype,
+                           const void* q, const void* k, const void* v,
+                           void* o, float* lse,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                           void* stream);
+
 /* Workspace bytes attn_decode needs for these sizes: the per-split partial
  * outputs and log-sum-exps when the keys are split (nsplit * B*Hq*Nq * (d + 1)
  * floats, each part rounded up to 256 bytes), else 0. A function of the sizes

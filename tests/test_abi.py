@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
                      "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_workspace_bytes",
-                     "attn_abi_version", "attn_decode", "attn_decode_workspace_bytes"):
+                     "attn_abi_version", "attn_decode", "attn_decode_workspace_bytes",
+                     "attn_fwd_naive", "attn_fwd_naive_workspace_bytes"):
         assert required in names
 
 
@@ -240,3 +241,20 @@ def test_decode_noops_and_workspace(L):
     nsplit = round(n / (rows * 64 * 4 + rows * 4))
     assert n == ((nsplit * rows * 64 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
     assert L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 2, 1, 64) == 0   # invalid: Nq > Nk
+
+
+def test_naive_validation(L):
+    assert L.attn_fwd_naive_workspace_bytes(8, 12, 1024) == 8 * 12 * 1024 * 1024 * 4
+    assert L.attn_fwd_naive_workspace_bytes(-1, 12, 1024) == 0
+    args = lambda **kw: dict(dict(dtype=BF16, out=F32, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, ws=FAKE,
+                                  wsb=1 << 30, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125), **kw)
+    call = lambda a: L.attn_fwd_naive(a["dtype"], a["out"], a["q"], a["k"], a["v"], a["o"], a["lse"], a["ws"],
+                                      a["wsb"], a["B"], a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"],
+                                      a["scale"], None)
+    assert call(args(ws=None)) == EINVAL
+    assert call(args(wsb=2 * 4 * 64 * 64 * 4 - 1)) == EINVAL       # one byte short of the score matrix
+    assert call(args(Hq=6, Hkv=4)) == EINVAL
+    assert call(args(out=7)) == EINVAL
+    assert call(args(d=48)) == EUNSUP
+    assert call(args(B=0, q=None, ws=None, wsb=0)) == OK
+    assert call(args(B=64, Hq=64, Hkv=64, N=16384, d=16, wsb=0)) == EINVAL   # B*Hq*N*N >= 2^39

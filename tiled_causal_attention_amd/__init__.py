@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         getattr(L, name).argtypes = bwd_args
         getattr(L, name).restype = i
+    L.attn_fwd_naive_workspace_bytes.argtypes = [i, i, i]
+    L.attn_fwd_naive_workspace_bytes.restype = sz
+    L.attn_fwd_naive.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_naive.restype = i
     L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, i, f, vp]
@@ -212,4 +216,27 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     _check(L.attn_decode(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                          _ptr(workspace), wsn, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
                          _stream(q.device)))
+    return o, lse
+
+
+def attn_fwd_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                   scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                   out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Unoptimised forward through the materialised score matrix (B*Hq*N*N floats
+    of workspace): same results as attn_fwd, for teaching and comparison."""
+    B, Hq, Hkv, N, d = _dims(q, k)
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=out_dtype or torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    L = lib()
+    ws_bytes = int(L.attn_fwd_naive_workspace_bytes(B, Hq, N))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _check(L.attn_fwd_naive(_dtype_code(q), _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), scale,
+                            _stream(q.device)))
     return o, lse

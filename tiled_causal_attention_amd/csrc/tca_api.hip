@@ -174,6 +174,26 @@ attn_status attn_bwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, cons
     return run_dkdv(a, st);
 }
 
+size_t attn_fwd_naive_workspace_bytes(int B, int Hq, int N) {
+    if (B < 0 || Hq < 0 || N < 0) return 0;
+    return tca::naive_workspace_size(B, Hq, N);
+}
+
+attn_status attn_fwd_naive(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                           void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
+                           int N, int d, int causal, float scale, void* stream) {
+    attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
+    if (s != ATTN_OK) return s;
+    if ((int64_t)B * N == 0) return ATTN_OK;
+    if ((int64_t)B * Hq * N * N >= ((int64_t)1 << 39)) return ATTN_EINVAL;   // score count: grid and workspace
+    s = check_ptrs({q, k, v, o, lse, workspace});
+    if (s != ATTN_OK) return s;
+    if (workspace_bytes < tca::naive_workspace_size(B, Hq, N)) return ATTN_EINVAL;
+    const AttnArgs a = make_args(dtype, out_dtype, q, k, v, o, lse, nullptr, nullptr, nullptr, nullptr,
+                                 workspace, workspace_bytes, B, Hq, Hkv, N, d, causal, scale);
+    return from_hip(tca::launch_fwd_naive(a, (hipStream_t)stream));
+}
+
 size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     (void)dtype;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Nq < 1 || Nk < Nq || !supported_d(d)) return 0;

@@ -95,6 +95,10 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
+// Unoptimised forward through a materialised score matrix (B*Hq*N*N floats of workspace).
+size_t naive_workspace_size(int B, int Hq, int N);
+hipError_t launch_fwd_naive(const AttnArgs& a, hipStream_t st);
+
 // matrix-core path: bf16 inputs, d in {64, 128}; same two backward phases
 bool mfma_path(const AttnArgs& a);
 hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st);
