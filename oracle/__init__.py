@@ -55,6 +55,10 @@ def load(path: str = _LIB):
     lib.oracle_attn_sampled.restype = None
     lib.oracle_attn_decode.argtypes = [dp, dp, dp, dp, dp, i, i, i, i, i, i, i, ctypes.c_double]
     lib.oracle_attn_decode.restype = None
+    lib.oracle_attn_fwd_rope.argtypes = [dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_attn_fwd_rope.restype = None
+    lib.oracle_attn_bwd_rope.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, dp, i, i, i, i, i, i, ctypes.c_double]
+    lib.oracle_attn_bwd_rope.restype = None
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     if path == _LIB:
@@ -167,3 +171,38 @@ def attn_sampled(q, k, v, dout, b: int, hkv: int, rows, keys, causal: int = 1,
 def threads(lib=None) -> int:
     """OpenMP threads the oracle will use (before capping by work units)."""
     return int((lib or load()).oracle_threads())
+
+
+def _tables(cos, sin, N, d):
+    cs, sn = _f64(cos), _f64(sin)
+    if cs.shape != (N, d // 2) or sn.shape != (N, d // 2) or d % 2:
+        raise ValueError(f"rope tables must be [N, d/2] = {(N, d // 2)}")
+    return cs, sn
+
+
+def attn_fwd_rope(q, k, v, cos, sin, causal: int = 1, scale: float | None = None, lib=None):
+    """Forward with rotary position embedding (rotate-half pairing) of q and k;
+    cos, sin: [N, d/2] tables. Returns (o, lse) in float64."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    cs, sn = _tables(cos, sin, N, d)
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    o = np.zeros((B, Hq, N, d))
+    lse = np.zeros((B, Hq, N))
+    (lib or load()).oracle_attn_fwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(cs), _ptr(sn), _ptr(o), _ptr(lse),
+                                         B, Hq, Hkv, N, d, int(causal), float(scale))
+    return o, lse
+
+
+def attn_bwd_rope(q, k, v, dout, cos, sin, causal: int = 1, scale: float | None = None, lib=None):
+    """Gradients of the unrotated q, k and of v for the rotary forward above."""
+    q, k, v, dout = _f64(q), _f64(k), _f64(v), _f64(dout)
+    B, Hq, Hkv, N, d = _dims(q, k)
+    cs, sn = _tables(cos, sin, N, d)
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    dq = np.zeros((B, Hq, N, d))
+    dk = np.zeros((B, Hkv, N, d))
+    dv = np.zeros((B, Hkv, N, d))
+    (lib or load()).oracle_attn_bwd_rope(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(cs), _ptr(sn),
+                                         _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, N, d, int(causal), float(scale))
+    return dq, dk, dv

@@ -305,3 +305,70 @@ void oracle_attn_decode(const double* q, const double* k, const double* v,
         free(s);
     }
 }
+
+/*
+ * Rotary position embedding (RoPE; the blog page's FAQ lists RoPE among the
+ * techniques the trainer supports) applied to q and k before the attention.
+ * The pages name RoPE only; the form used is the rotate-half pairing: for a
+ * row at sequence position n and i < d/2, the pair (x_i, x_{i+d/2}) becomes
+ *
+ *     (x_i cos - x_{i+d/2} sin,  x_{i+d/2} cos + x_i sin),   cos, sin = table[n][i]
+ *
+ * with the caller's tables (normally cos/sin of n * base^(-2i/d)). The
+ * attention then runs on the rotated q and k. The rotation is orthogonal per
+ * pair, so the gradients of the unrotated q and k are the rotated-space
+ * gradients turned back by the transpose:
+ *
+ *     (g_i cos + g_{i+d/2} sin,  g_{i+d/2} cos - g_i sin).
+ *
+ * Tables: cs, sn [N][d/2]; tensors as in the forward ([B, H, N, d]).
+ */
+static void rope_apply(double* x, const double* cs, const double* sn, size_t heads, int N, int d, int transpose) {
+    const int h = d / 2;
+    for (size_t r = 0; r < heads * (size_t)N; ++r) {
+        const int n = (int)(r % (size_t)N);
+        double* row = x + r * d;
+        for (int i = 0; i < h; ++i) {
+            const double c = cs[(size_t)n * h + i], s = sn[(size_t)n * h + i];
+            const double a = row[i], b = row[i + h];
+            if (!transpose) {
+                row[i] = a * c - b * s;
+                row[i + h] = b * c + a * s;
+            } else {
+                row[i] = a * c + b * s;
+                row[i + h] = b * c - a * s;
+            }
+        }
+    }
+}
+
+static double* dup(const double* x, size_t n) {
+    double* y = (double*)malloc(sizeof(double) * (n ? n : 1));
+    memcpy(y, x, sizeof(double) * n);
+    return y;
+}
+
+void oracle_attn_fwd_rope(const double* q, const double* k, const double* v, const double* cs, const double* sn,
+                          double* o, double* lse, int B, int Hq, int Hkv, int N, int d, int causal, double scale) {
+    double* qr = dup(q, (size_t)B * Hq * N * d);
+    double* kr = dup(k, (size_t)B * Hkv * N * d);
+    rope_apply(qr, cs, sn, (size_t)B * Hq, N, d, 0);
+    rope_apply(kr, cs, sn, (size_t)B * Hkv, N, d, 0);
+    oracle_attn_fwd(qr, kr, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+    free(qr);
+    free(kr);
+}
+
+void oracle_attn_bwd_rope(const double* q, const double* k, const double* v, const double* dout,
+                          const double* cs, const double* sn, double* dq, double* dk, double* dv,
+                          int B, int Hq, int Hkv, int N, int d, int causal, double scale) {
+    double* qr = dup(q, (size_t)B * Hq * N * d);
+    double* kr = dup(k, (size_t)B * Hkv * N * d);
+    rope_apply(qr, cs, sn, (size_t)B * Hq, N, d, 0);
+    rope_apply(kr, cs, sn, (size_t)B * Hkv, N, d, 0);
+    oracle_attn_bwd(qr, kr, v, dout, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale);
+    rope_apply(dq, cs, sn, (size_t)B * Hq, N, d, 1);
+    rope_apply(dk, cs, sn, (size_t)B * Hkv, N, d, 1);
+    free(qr);
+    free(kr);
+}

@@ -10,6 +10,8 @@ The oracle is checked against things other than itself:
   * invariants of the mathematics (softmax shift invariance, sum of dV, the
     Q/K rescaling identity, GQA equals MHA with repeated K/V);
   * hand-worked examples under tests/golden/;
+  * rotary position embedding: torch autograd through the rotation and SDPA, a
+    hand-worked direction example, position-shift invariance, identity tables;
   * few-query (decode) attention over a cache: torch's SDPA with an explicit
     bottom-right causal mask, the last rows of a full-sequence forward, and
     closed forms;
@@ -99,10 +101,13 @@ def _pin_failures(lib=None, shapes=SHAPES, atol=1e-10):
                     fails.append(f"{nm} vs autograd {B,Hq,Hkv,N,d,causal}: {np.nanmax(np.abs(a - b))}")
     fails += _sampled_failures(lib, atol)
     fails += _decode_failures(lib, atol)
+    fails += _rope_failures(lib, atol)
     for fname in sorted(os.listdir(GOLDEN)):
         if not fname.endswith(".json"):
             continue
         ex = json.load(open(os.path.join(GOLDEN, fname)))
+        if "cos" in ex:   # the rotary example, checked by _rope_failures
+            continue
         arr = {kk: np.array(ex[kk], dtype=np.float64) for kk in ("q", "k", "v", "dO", "o", "lse", "dq", "dk", "dv")}
         o, lse = oracle.attn_fwd(arr["q"], arr["k"], arr["v"], ex["causal"], ex["scale"], lib=lib)
         dq, dk, dv = oracle.attn_bwd(arr["q"], arr["k"], arr["v"], arr["dO"], ex["causal"], ex["scale"], lib=lib)
@@ -197,6 +202,82 @@ def test_decode_closed_forms():
     assert np.allclose(o[0, :, 0], vn[0, [0, 0, 1, 1], 0], atol=1e-14)
     kq = (q[0, :, 0].numpy() * k[0, [0, 0, 1, 1], 0].numpy()).sum(-1)
     assert np.allclose(lse[0, :, 0], 0.7 * kq, atol=1e-14)
+
+
+def rope_tables(N, d, base=10000.0, offset=0):
+    """cos/sin [N, d/2] of (n + offset) * base^(-2i/d), float64."""
+    n = torch.arange(N, dtype=torch.float64)[:, None] + offset
+    inv = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = n * inv[None, :]
+    return torch.cos(ang), torch.sin(ang)
+
+
+def _torch_rotate(x, cos, sin):
+    # rotate-half pairing written with torch ops (x1, x2 the two halves of the head dimension)
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    return torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], dim=-1)
+
+
+def _rope_failures(lib=None, atol=1e-10):
+    """Rotary forward/backward against torch float64: the rotation in torch ops, SDPA,
+    autograd through both (so the backward's transpose rotation is pinned by autograd);
+    plus the hand-worked direction example in tests/golden."""
+    fails = []
+    for (B, Hq, Hkv, N, d) in [(1, 2, 1, 9, 4), (2, 6, 2, 17, 8), (1, 4, 4, 12, 6)]:
+        for causal in (1, 0):
+            q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=N + d + causal)
+            cos, sin = rope_tables(N, d, base=100.0)
+            scale = 1.0 / math.sqrt(d)
+            o, lse = oracle.attn_fwd_rope(q, k, v, cos, sin, causal, scale, lib=lib)
+            dq, dk, dv = oracle.attn_bwd_rope(q, k, v, do, cos, sin, causal, scale, lib=lib)
+            qt, kt, vt = (t.clone().requires_grad_(True) for t in (q, k, v))
+            qr, kr = _torch_rotate(qt, cos, sin), _torch_rotate(kt, cos, sin)
+            ot = _torch_fwd(qr, kr, vt, causal, scale)
+            ot.backward(do)
+            rl = _torch_lse(qr.detach(), kr.detach(), causal, scale).numpy()
+            for nm, a, b in (("o", o, ot.detach().numpy()), ("lse", lse, rl), ("dq", dq, qt.grad.numpy()),
+                             ("dk", dk, kt.grad.numpy()), ("dv", dv, vt.grad.numpy())):
+                if not np.allclose(a, b, atol=atol, rtol=0):
+                    fails.append(f"rope {nm} vs torch {B,Hq,Hkv,N,d,causal}: {np.nanmax(np.abs(a - b))}")
+    ex = json.load(open(os.path.join(GOLDEN, "rope_direction_n2_d2.json")))
+    arr = {kk: np.array(ex[kk], dtype=np.float64) for kk in ("q", "k", "v", "cos", "sin", "o", "lse")}
+    o, lse = oracle.attn_fwd_rope(arr["q"], arr["k"], arr["v"], arr["cos"], arr["sin"], ex["causal"], ex["scale"],
+                                  lib=lib)
+    if not (np.allclose(o, arr["o"], atol=1e-12) and np.allclose(lse, arr["lse"], atol=1e-12)):
+        fails.append(f"rope golden: o {o.ravel()} lse {lse.ravel()}")
+    return fails
+
+
+def test_rope_matches_torch_and_golden():
+    assert _rope_failures() == []
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_rope_depends_on_relative_position_only(causal):
+    # shifting every position by the same amount rotates q and k alike: scores,
+    # hence O and LSE, are unchanged, and so are the gradients
+    B, Hq, Hkv, N, d = 2, 4, 2, 20, 8
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=8)
+    c0, s0 = rope_tables(N, d)
+    c1, s1 = rope_tables(N, d, offset=37)
+    o0, l0 = oracle.attn_fwd_rope(q, k, v, c0, s0, causal, 0.3)
+    o1, l1 = oracle.attn_fwd_rope(q, k, v, c1, s1, causal, 0.3)
+    assert np.allclose(o0, o1, atol=1e-12) and np.allclose(l0, l1, atol=1e-12)
+    # and a real rotation does change the result against no rotation
+    o2, _ = oracle.attn_fwd(q, k, v, causal, 0.3)
+    assert np.abs(o2 - o0).max() > 1e-3
+
+
+def test_rope_identity_tables_equal_plain_attention():
+    B, Hq, Hkv, N, d = 1, 6, 3, 15, 4
+    q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=10)
+    one, zero = torch.ones(N, d // 2, dtype=torch.float64), torch.zeros(N, d // 2, dtype=torch.float64)
+    for causal in (1, 0):
+        a = oracle.attn_fwd_rope(q, k, v, one, zero, causal, 0.5) + oracle.attn_bwd_rope(q, k, v, do, one, zero, causal, 0.5)
+        b = oracle.attn_fwd(q, k, v, causal, 0.5) + oracle.attn_bwd(q, k, v, do, causal, 0.5)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
 
 
 def _sampled_failures(lib=None, atol=1e-10):
@@ -419,6 +500,11 @@ MUTANTS = [
     ("sampled: O row uses K", "oi[c] += s[j] * v[(size_t)j * d + c];", "oi[c] += s[j] * k[(size_t)j * d + c];"),
     ("decode: queries aligned to the start", "const int pos = Nk - Nq + i;", "const int pos = i;"),
     ("decode: position off by one", "const int pos = Nk - Nq + i;", "const int pos = Nk - Nq + i - 1;"),
+    ("rope: opposite rotation direction", "row[i] = a * c - b * s;\n                row[i + h] = b * c + a * s;",
+     "row[i] = a * c + b * s;\n                row[i + h] = b * c - a * s;"),
+    ("rope: gradient rotated forward, not back", "rope_apply(dq, cs, sn, (size_t)B * Hq, N, d, 1);",
+     "rope_apply(dq, cs, sn, (size_t)B * Hq, N, d, 0);"),
+    ("rope: adjacent pairs", "const double a = row[i], b = row[i + h];", "const double a = row[2 * (i % (h / 2 > 0 ? h / 2 : 1))], b = row[i + h];"),
     ("transposed V index", "acc += doi[c] * vh[(size_t)j * d + c];", "acc += doi[c] * vh[(size_t)c * d + j % d];"),
 ]
 
