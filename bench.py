@@ -10,6 +10,7 @@ all on torch's current stream, inputs resident in HBM.
     python bench.py --all-configs [--oracle]     # per-workload report, see below
     python bench.py --decode                     # few-query attention over a K/V cache
     python bench.py --naive                      # tiled forward against the naive materialised-score one
+    python bench.py --rope                       # rotary q/k on fused-QKV views against the plain path
 
 Prints one JSON line. `value` is fwd+bwd TFLOP/s counted with the causal
 N^2/2 convention (forward 4d flops per visible pair, backward 2.5x that).
@@ -71,6 +72,9 @@ def parse():
     p.add_argument("--all-configs", action="store_true",
                    help="per-workload report (median/p10/p90) instead of the one-line benchmark")
     p.add_argument("--oracle", action="store_true", help="with --all-configs: time the oracle per workload")
+    p.add_argument("--rope", action="store_true",
+                   help="one JSON line: fwd+bwd with rotary q/k on views of one fused QKV buffer, "
+                        "against the plain path on contiguous tensors")
     p.add_argument("--naive", action="store_true",
                    help="one JSON line: the forward of the workload, tiled against the naive materialised-score one")
     p.add_argument("--decode", action="store_true",
@@ -308,6 +312,60 @@ def naive_report(args):
                       "speedup": med["naive"] / med["tiled"], "score_matrix_bytes": ws.numel()}), flush=True)
 
 
+def rope_report(args):
+    """fwd+bwd of one workload (default the headline) with rotary q/k read from views of
+    one fused [B, N, Hq + 2 Hkv, d] projection buffer and gradients written back into
+    one such buffer, against the plain path on contiguous tensors; HIP events on the
+    launch stream around each fwd+bwd, median of 50 after 10 warm-up steps."""
+    import numpy as np
+    s = workloads.CONFIGS[args.workload]
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(s))
+    cos, sin = (t.cuda() for t in workloads.rope_tables(s.N, s.d))
+    buf = torch.empty((s.B, s.N, s.Hq + 2 * s.Hkv, s.d), dtype=q.dtype, device=q.device)
+    gbuf = torch.empty((s.B, s.N, s.Hq + 2 * s.Hkv, s.d), device=q.device)
+    views = lambda b: (b[:, :, :s.Hq].permute(0, 2, 1, 3), b[:, :, s.Hq:s.Hq + s.Hkv].permute(0, 2, 1, 3),
+                       b[:, :, s.Hq + s.Hkv:].permute(0, 2, 1, 3))
+    qv, kv, vv = views(buf)
+    qv.copy_(q), kv.copy_(k), vv.copy_(v)
+    gq, gk, gv = views(gbuf)
+    o = torch.empty((s.B, s.Hq, s.N, s.d), device=q.device)
+    lse = torch.empty((s.B, s.Hq, s.N), device=q.device)
+    dq, dk, dv = (torch.empty(t.shape, device=q.device) for t in (q, k, v))
+    L = tca.lib()
+    wsf = torch.empty(int(L.attn_fwd_rope_workspace_bytes(tca.ATTN_BF16, tca.ATTN_F32, s.B, s.Hq, s.Hkv, s.N, s.d)),
+                      dtype=torch.uint8, device=q.device)
+    wsb = torch.empty(int(L.attn_bwd_rope_workspace_bytes(tca.ATTN_BF16, tca.ATTN_F32, s.B, s.Hq, s.Hkv, s.N, s.d)),
+                      dtype=torch.uint8, device=q.device)
+    ws = tca.bwd_workspace(q, k)
+    causal, scale = bool(s.causal), s.scale
+
+    def rope_step():
+        tca.attn_fwd_rope(qv, kv, vv, cos, sin, causal, scale, out=(o, lse), workspace=wsf)
+        tca.attn_bwd_rope(qv, kv, vv, o, lse, do, cos, sin, causal, scale, out=(gq, gk, gv), workspace=wsb)
+
+    def plain_step():
+        tca.attn_fwd(q, k, v, causal, scale, out=(o, lse))
+        tca.attn_bwd(q, k, v, o, lse, do, causal, scale, out=(dq, dk, dv), workspace=ws)
+
+    med = {}
+    for name, fn in (("plain", plain_step), ("rope_fused_qkv", rope_step)):
+        for _ in range(10):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        med[name] = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+    fl = s.flops_fwd() + s.flops_bwd()
+    print(json.dumps({"workload": s.name, "plain_fwd_bwd_ms": med["plain"], "rope_fwd_bwd_ms": med["rope_fused_qkv"],
+                      "plain_tflops": fl / (med["plain"] * 1e-3) / 1e12,
+                      "rope_tflops": fl / (med["rope_fused_qkv"] * 1e-3) / 1e12,
+                      "rope_overhead": med["rope_fused_qkv"] / med["plain"] - 1.0}), flush=True)
+
+
 def decode_report(args):
     """Few-query attention over a K/V cache: HBM-bound, so reported as GB/s of the
     minimum traffic (K and V once, Q, O, LSE) against the 8 TB/s HBM peak. Each
@@ -375,6 +433,9 @@ def main():
         return
     if args.naive:
         naive_report(args)
+        return
+    if args.rope:
+        rope_report(args)
         return
 
     s = workloads.CONFIGS[args.workload]

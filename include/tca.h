@@ -162,6 +162,66 @@ attn_status attn_bwd_dkdv(attn_dtype dtype, attn_dtype out_dtype,
                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           void* stream);
 
+/* Element strides of a [B, H, N, d] tensor whose head dimension is contiguous:
+ * element (b, h, n, c) sits at b*stride_b + h*stride_h + n*stride_n + c. For
+ * q, k, v taken from one fused projection buffer [B, N, (Hq + 2*Hkv)*d]:
+ * stride_b = N*W, stride_h = d, stride_n = W with W = (Hq + 2*Hkv)*d (k and v
+ * start Hq*d and (Hq+Hkv)*d elements in). A NULL layout pointer means the
+ * contiguous [B, H, N, d] layout. */
+typedef struct attn_layout {
+    long long stride_b, stride_h, stride_n;
+} attn_layout;
+
+/* Workspace bytes attn_fwd_rope / attn_bwd_rope need: contiguous copies of q,
+ * k (rotated) and v in `dtype`; for the backward also float32 gradients, a
+ * float32 copy of o for bfloat16 outputs, and attn_bwd's own workspace. Each
+ * part rounded up to 256 bytes. */
+size_t attn_fwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d);
+size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d);
+
+/* Forward with rotary position embedding on q and k and strided inputs (the
+ * blog page's FAQ lists RoPE among the trainer's techniques; q, k, v come from
+ * one fused projection). Row n of every head sits at position n; with
+ * rope_cos/rope_sin ([N, d/2] float32 device tables, normally cos/sin of
+ * n * base^(-2i/d)) the pairs (x_i, x_{i+d/2}) of q and k are rotated to
+ * (x_i cos - x_{i+d/2} sin, x_{i+d/2} cos + x_i sin) before the attention;
+ * both NULL means no rotation (strided input only). d must be even for
+ * tables. q, k, v are read through their layouts (NULL: contiguous); o and lse
+ * are written as by attn_fwd. The rotated q, k (rounded to `dtype`) and a
+ * contiguous v are staged in `workspace` (at least attn_fwd_rope_workspace_bytes)
+ * and attn_fwd's kernels run on them. Pointers to strided tensors need element
+ * alignment only; o and lse as for attn_fwd. Strides must be >= 0 and the
+ * caller's buffers must hold every addressed element. */
+attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype,
+                          const void* q, const attn_layout* q_layout,
+                          const void* k, const attn_layout* k_layout,
+                          const void* v, const attn_layout* v_layout,
+                          const float* rope_cos, const float* rope_sin,
+                          void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          void* stream);
+
+/* Backward of attn_fwd_rope: dq, dk, dv with respect to the UNROTATED q, k and
+ * to v, written through their layouts (NULL: contiguous) in `out_dtype`. o and
+ * lse exactly as attn_fwd_rope wrote them (contiguous), dO contiguous in
+ * `dtype`. The rotated copies are staged again, attn_bwd's kernels write
+ * float32 gradients into `workspace`, and dq, dk are turned back by the
+ * transpose rotation (g_i cos + g_{i+d/2} sin, g_{i+d/2} cos - g_i sin) with a
+ * single rounding to `out_dtype`. */
+attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype,
+                          const void* q, const attn_layout* q_layout,
+                          const void* k, const attn_layout* k_layout,
+                          const void* v, const attn_layout* v_layout,
+                          const float* rope_cos, const float* rope_sin,
+                          const void* o, const float* lse, const void* dO,
+                          void* dq, const attn_layout* dq_layout,
+                          void* dk, const attn_layout* dk_layout,
+                          void* dv, const attn_layout* dv_layout,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          void* stream);
+
 /* Workspace bytes attn_fwd_naive needs: the score matrix, B*Hq*N*N floats. */
 size_t attn_fwd_naive_workspace_bytes(int B, int Hq, int N);
 

@@ -40,7 +40,8 @@ def test_header_declares_the_boundary():
     for required in ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
                      "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_workspace_bytes",
                      "attn_abi_version", "attn_decode", "attn_decode_workspace_bytes",
-                     "attn_fwd_naive", "attn_fwd_naive_workspace_bytes"):
+                     "attn_fwd_naive", "attn_fwd_naive_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope",
+                     "attn_fwd_rope_workspace_bytes", "attn_bwd_rope_workspace_bytes"):
         assert required in names
 
 
@@ -258,3 +259,31 @@ def test_naive_validation(L):
     assert call(args(d=48)) == EUNSUP
     assert call(args(B=0, q=None, ws=None, wsb=0)) == OK
     assert call(args(B=64, Hq=64, Hkv=64, N=16384, d=16, wsb=0)) == EINVAL   # B*Hq*N*N >= 2^39
+
+
+def test_rope_validation(L):
+    import ctypes
+    lay = lambda sb, sh, sn: ctypes.byref(tca.AttnLayout(sb, sh, sn))
+    nq, nk = 2 * 4 * 64 * 64, 2 * 2 * 64 * 64
+    rnd = lambda n: (n + 255) // 256 * 256
+    # forward: q, k, v copies; backward adds float32 gradients (and a float32 o for bf16 outputs)
+    # and attn_bwd's own workspace
+    assert L.attn_fwd_rope_workspace_bytes(BF16, F32, 2, 4, 2, 64, 64) == rnd(nq * 2) + 2 * rnd(nk * 2)
+    bwd = L.attn_bwd_rope_workspace_bytes(BF16, BF16, 2, 4, 2, 64, 64)
+    assert bwd == (rnd(nq * 2) + 2 * rnd(nk * 2) + rnd(nq * 4) + rnd(nq * 4) + 2 * rnd(nk * 4)
+                   + L.attn_bwd_workspace_bytes(BF16, 2, 4, 2, 64, 64))
+
+    def fwd_rope(cos=FAKE, sin=FAKE, ql=None, q=FAKE, d=64, ws=FAKE, wsb=1 << 30, **kw):
+        a = dict(dtype=BF16, out=F32, B=2, Hq=4, Hkv=2, N=64, causal=1, scale=0.125)
+        a.update(kw)
+        return L.attn_fwd_rope(a["dtype"], a["out"], q, ql, FAKE, None, FAKE, None, cos, sin, FAKE, FAKE, ws, wsb,
+                               a["B"], a["Hq"], a["Hkv"], a["N"], d, a["causal"], a["scale"], None)
+    assert fwd_rope(cos=None) == EINVAL                 # one table without the other
+    assert fwd_rope(cos=FAKE + 4) == EINVAL             # tables 16-byte aligned
+    assert fwd_rope(ql=lay(-1, 64, 64)) == EINVAL       # negative stride
+    assert fwd_rope(q=FAKE + 1) == EINVAL               # bf16 needs 2-byte alignment
+    assert fwd_rope(wsb=100) == EINVAL
+    assert fwd_rope(ws=None) == EINVAL
+    assert fwd_rope(d=80) == EUNSUP
+    assert fwd_rope(B=0, q=None, ws=None, wsb=0) == OK
+    assert fwd_rope(causal=4) == EINVAL

@@ -30,6 +30,11 @@ ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
 _lib = None
 
 
+class AttnLayout(ctypes.Structure):
+    """Element strides (batch, head, row) of a [B, H, N, d] tensor with contiguous d."""
+    _fields_ = [("stride_b", ctypes.c_longlong), ("stride_h", ctypes.c_longlong), ("stride_n", ctypes.c_longlong)]
+
+
 class AttnError(RuntimeError):
     """A non-OK status from the C ABI."""
 
@@ -60,6 +65,15 @@ def lib() -> ctypes.CDLL:
     for name in ("attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv"):
         getattr(L, name).argtypes = bwd_args
         getattr(L, name).restype = i
+    lp = ctypes.POINTER(AttnLayout)
+    for nm in ("attn_fwd_rope_workspace_bytes", "attn_bwd_rope_workspace_bytes"):
+        getattr(L, nm).argtypes = [i, i, i, i, i, i, i]
+        getattr(L, nm).restype = sz
+    L.attn_fwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_rope.restype = i
+    L.attn_bwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, fp, vp, vp, lp, vp, lp, vp, lp, vp, sz,
+                                i, i, i, i, i, i, f, vp]
+    L.attn_bwd_rope.restype = i
     L.attn_fwd_naive_workspace_bytes.argtypes = [i, i, i]
     L.attn_fwd_naive_workspace_bytes.restype = sz
     L.attn_fwd_naive.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
@@ -240,3 +254,83 @@ def attn_fwd_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
                             _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), scale,
                             _stream(q.device)))
     return o, lse
+
+
+def _layout(t: torch.Tensor) -> AttnLayout:
+    if t.dim() != 4 or t.stride(-1) != 1:
+        raise ValueError("tensors must be [B, H, N, d] views with a contiguous head dimension")
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    return AttnLayout(t.stride(0), t.stride(1), t.stride(2))
+
+
+def _sptr(t: torch.Tensor) -> Optional[int]:
+    return t.data_ptr() if t.numel() else None
+
+
+def _tables(cos, sin, N, d):
+    if cos is None and sin is None:
+        return None, None
+    for t in (cos, sin):
+        if t is None or t.dtype != torch.float32 or not t.is_cuda or tuple(t.shape) != (N, d // 2) \
+                or not t.is_contiguous():
+            raise ValueError(f"rope tables must be contiguous float32 CUDA tensors of shape {(N, d // 2)}")
+    return cos.data_ptr(), sin.data_ptr()
+
+
+def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optional[float] = None, out=None,
+                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None):
+    """Forward with rotary position embedding of q and k (rotate-half pairing; cos,
+    sin: [N, d/2] float32 tables, or both None) on [B, H, N, d] views with any
+    strides (e.g. slices of one fused QKV projection). Returns (o, lse) like attn_fwd."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = default_scale(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        o = torch.empty((B, Hq, N, d), dtype=out_dtype or torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+    L = lib()
+    cs, sn = _tables(cos, sin, N, d)
+    n = int(L.attn_fwd_rope_workspace_bytes(dt, _code(o.dtype), B, Hq, Hkv, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ql, kl, vl = _layout(q), _layout(k), _layout(v)
+    _check(L.attn_fwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ql), _sptr(k), ctypes.byref(kl), _sptr(v),
+                           ctypes.byref(vl), cs, sn, _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                           B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
+    return o, lse
+
+
+def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, scale: Optional[float] = None,
+                  out=None, workspace: Optional[torch.Tensor] = None):
+    """Backward of attn_fwd_rope: gradients of the unrotated q, k and of v, in o's
+    dtype, written into `out` = (dq, dk, dv) views (any strides) or new contiguous tensors."""
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    scale = default_scale(d) if scale is None else float(scale)
+    dt = _dtype_code(q)
+    if out is None:
+        dq = torch.empty(q.shape, dtype=o.dtype, device=q.device)
+        dk = torch.empty(k.shape, dtype=o.dtype, device=q.device)
+        dv = torch.empty(v.shape, dtype=o.dtype, device=q.device)
+    else:
+        dq, dk, dv = out
+    for t in (dq, dk, dv):
+        if t.dtype != o.dtype:
+            raise TypeError("dq, dk, dv must have o's dtype")
+    L = lib()
+    cs, sn = _tables(cos, sin, N, d)
+    n = int(L.attn_bwd_rope_workspace_bytes(dt, _code(o.dtype), B, Hq, Hkv, N, d))
+    if workspace is None:
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    ls = [_layout(t) for t in (q, k, v, dq, dk, dv)]
+    _check(L.attn_bwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ls[0]), _sptr(k), ctypes.byref(ls[1]),
+                           _sptr(v), ctypes.byref(ls[2]), cs, sn, _ptr(o), _ptr(lse), _ptr(dO),
+                           _sptr(dq), ctypes.byref(ls[3]), _sptr(dk), ctypes.byref(ls[4]), _sptr(dv),
+                           ctypes.byref(ls[5]), _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d,
+                           int(bool(causal)), scale, _stream(q.device)))
+    return dq, dk, dv
+

@@ -82,6 +82,80 @@ AttnArgs make_args(attn_dtype dtype, attn_dtype out_dtype, const void* q, const 
 
 attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_EHIP; }
 
+// ---- rotary / strided path: workspace carving
+size_t elsize(attn_dtype t) { return t == ATTN_F32 ? 4 : 2; }
+attn_layout contiguous_layout(int H, int N, int d) {
+    attn_layout l;
+    l.stride_b = (long long)H * N * d;
+    l.stride_h = (long long)N * d;
+    l.stride_n = d;
+    return l;
+}
+struct RopeWs {
+    char* q;
+    char* k;
+    char* v;
+    float* o32;
+    float* dq;
+    float* dk;
+    float* dv;
+    char* bwd;
+    size_t bwd_bytes;
+    size_t total;
+};
+RopeWs rope_ws(void* base, bool bwd, attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d) {
+    RopeWs w = {};
+    char* p = static_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* r = p ? p + off : nullptr;
+        off += tca::ws_round(bytes);
+        return r;
+    };
+    const size_t nq = (size_t)B * Hq * N * d, nk = (size_t)B * Hkv * N * d;
+    w.q = take(nq * elsize(dtype));
+    w.k = take(nk * elsize(dtype));
+    w.v = take(nk * elsize(dtype));
+    if (bwd) {
+        if (out_dtype == ATTN_BF16) w.o32 = reinterpret_cast<float*>(take(nq * 4));
+        w.dq = reinterpret_cast<float*>(take(nq * 4));
+        w.dk = reinterpret_cast<float*>(take(nk * 4));
+        w.dv = reinterpret_cast<float*>(take(nk * 4));
+        w.bwd_bytes = tca::bwd_workspace_size(dtype, B, Hq, N, d);
+        w.bwd = take(w.bwd_bytes);
+    }
+    w.total = off;
+    return w;
+}
+
+bool layout_ok(const attn_layout* l) {
+    return l == nullptr || (l->stride_b >= 0 && l->stride_h >= 0 && l->stride_n >= 0);
+}
+bool elem_aligned(const void* p, attn_dtype t) { return p != nullptr && ((uintptr_t)p % elsize(t)) == 0; }
+
+attn_status check_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, const attn_layout* ql, const void* k,
+                       const attn_layout* kl, const void* v, const attn_layout* vl, const float* cs, const float* sn,
+                       int d) {
+    if ((cs == nullptr) != (sn == nullptr)) return ATTN_EINVAL;
+    if (cs != nullptr && (d % 2 != 0 || !aligned16(cs) || !aligned16(sn))) return ATTN_EINVAL;
+    if (!layout_ok(ql) || !layout_ok(kl) || !layout_ok(vl)) return ATTN_EINVAL;
+    if (!elem_aligned(q, dtype) || !elem_aligned(k, dtype) || !elem_aligned(v, dtype)) return ATTN_EINVAL;
+    (void)out_dtype;
+    return ATTN_OK;
+}
+
+// q, k (rotated) and v into the contiguous staging copies
+hipError_t stage_qkv(const RopeWs& w, attn_dtype dtype, const void* q, const attn_layout* ql, const void* k,
+                     const attn_layout* kl, const void* v, const attn_layout* vl, const float* cs, const float* sn,
+                     int B, int Hq, int Hkv, int N, int d, hipStream_t st) {
+    const int rot = cs ? 1 : 0;
+    const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
+    hipError_t e = tca::layout_copy(dtype, q, ql ? *ql : cq, dtype, w.q, cq, cs, sn, B, Hq, N, d, rot, st);
+    if (e == hipSuccess) e = tca::layout_copy(dtype, k, kl ? *kl : ck, dtype, w.k, ck, cs, sn, B, Hkv, N, d, rot, st);
+    if (e == hipSuccess) e = tca::layout_copy(dtype, v, vl ? *vl : ck, dtype, w.v, ck, nullptr, nullptr, B, Hkv, N, d, 0, st);
+    return e;
+}
+
 attn_status run_dq(const AttnArgs& a, hipStream_t st) {
     return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma_dq(a, st) : tca::launch_bwd_generic_dq(a, st));
 }
@@ -172,6 +246,84 @@ attn_status attn_bwd(attn_dtype dtype, attn_dtype out_dtype, const void* q, cons
     s = run_dq(a, st);
     if (s != ATTN_OK) return s;
     return run_dkdv(a, st);
+}
+
+size_t attn_fwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return 0;
+    return rope_ws(nullptr, false, dtype, out_dtype, B, Hq, Hkv, N, d).total;
+}
+size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int B, int Hq, int Hkv, int N, int d) {
+    if (B < 0 || Hq < 0 || Hkv < 0 || N < 0 || d < 0) return 0;
+    return rope_ws(nullptr, true, dtype, out_dtype, B, Hq, Hkv, N, d).total;
+}
+
+attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, const attn_layout* q_layout,
+                          const void* k, const attn_layout* k_layout, const void* v, const attn_layout* v_layout,
+                          const float* rope_cos, const float* rope_sin, void* o, float* lse, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          void* stream) {
+    attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
+    if (s != ATTN_OK) return s;
+    if ((int64_t)B * N == 0) return ATTN_OK;
+    s = check_rope(dtype, out_dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, d);
+    if (s != ATTN_OK) return s;
+    s = check_ptrs({o, lse, workspace});
+    if (s != ATTN_OK) return s;
+    const RopeWs w = rope_ws(workspace, false, dtype, out_dtype, B, Hq, Hkv, N, d);
+    if (workspace_bytes < w.total) return ATTN_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
+    if (e != hipSuccess) return ATTN_EHIP;
+    const AttnArgs a = make_args(dtype, out_dtype, w.q, w.k, w.v, o, lse, nullptr, nullptr, nullptr, nullptr,
+                                 nullptr, 0, B, Hq, Hkv, N, d, causal, scale);
+    return from_hip(tca::mfma_path(a) ? tca::launch_fwd_mfma(a, st) : tca::launch_fwd_generic(a, st));
+}
+
+attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, const attn_layout* q_layout,
+                          const void* k, const attn_layout* k_layout, const void* v, const attn_layout* v_layout,
+                          const float* rope_cos, const float* rope_sin, const void* o, const float* lse,
+                          const void* dO, void* dq, const attn_layout* dq_layout, void* dk,
+                          const attn_layout* dk_layout, void* dv, const attn_layout* dv_layout, void* workspace,
+                          size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                          void* stream) {
+    attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
+    if (s != ATTN_OK) return s;
+    if ((int64_t)B * N == 0) return ATTN_OK;
+    s = check_rope(dtype, out_dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, d);
+    if (s != ATTN_OK) return s;
+    if (!layout_ok(dq_layout) || !layout_ok(dk_layout) || !layout_ok(dv_layout)) return ATTN_EINVAL;
+    if (!elem_aligned(dq, out_dtype) || !elem_aligned(dk, out_dtype) || !elem_aligned(dv, out_dtype))
+        return ATTN_EINVAL;
+    s = check_ptrs({o, lse, dO, workspace});
+    if (s != ATTN_OK) return s;
+    const RopeWs w = rope_ws(workspace, true, dtype, out_dtype, B, Hq, Hkv, N, d);
+    if (workspace_bytes < w.total) return ATTN_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
+    if (e != hipSuccess) return ATTN_EHIP;
+    const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
+    const void* o_in = o;
+    if (out_dtype == ATTN_BF16) {   // the backward runs with float32 outputs: widen o exactly
+        e = tca::layout_copy(ATTN_BF16, o, cq, ATTN_F32, w.o32, cq, nullptr, nullptr, B, Hq, N, d, 0, st);
+        if (e != hipSuccess) return ATTN_EHIP;
+        o_in = w.o32;
+    }
+    const AttnArgs a = make_args(dtype, ATTN_F32, w.q, w.k, w.v, o_in, lse, dO, w.dq, w.dk, w.dv, w.bwd, w.bwd_bytes,
+                                 B, Hq, Hkv, N, d, causal, scale);
+    s = run_dq(a, st);
+    if (s != ATTN_OK) return s;
+    s = run_dkdv(a, st);
+    if (s != ATTN_OK) return s;
+    const int rot = rope_cos ? 2 : 0;
+    e = tca::layout_copy(ATTN_F32, w.dq, cq, out_dtype, dq, dq_layout ? *dq_layout : cq, rope_cos, rope_sin, B, Hq,
+                         N, d, rot, st);
+    if (e == hipSuccess)
+        e = tca::layout_copy(ATTN_F32, w.dk, ck, out_dtype, dk, dk_layout ? *dk_layout : ck, rope_cos, rope_sin, B,
+                             Hkv, N, d, rot, st);
+    if (e == hipSuccess)
+        e = tca::layout_copy(ATTN_F32, w.dv, ck, out_dtype, dv, dv_layout ? *dv_layout : ck, nullptr, nullptr, B,
+                             Hkv, N, d, 0, st);
+    return from_hip(e);
 }
 
 size_t attn_fwd_naive_workspace_bytes(int B, int Hq, int N) {

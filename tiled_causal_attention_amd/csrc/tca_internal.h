@@ -95,6 +95,13 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
+// Strided copy of [B, H, N, d] tensors (head dimension contiguous) with an optional
+// rotary rotation of the (i, i + d/2) pairs at each row's position: rot 0 none,
+// 1 forward, 2 transpose; cs, sn [N][d/2].
+hipError_t layout_copy(attn_dtype ti, const void* src, const attn_layout& sl, attn_dtype to, void* dst,
+                       const attn_layout& dl, const float* cs, const float* sn, int B, int H, int N, int d, int rot,
+                       hipStream_t st);
+
 // Unoptimised forward through a materialised score matrix (B*Hq*N*N floats of workspace).
 size_t naive_workspace_size(int B, int Hq, int N);
 hipError_t launch_fwd_naive(const AttnArgs& a, hipStream_t st);

@@ -156,3 +156,14 @@ def make_decode_inputs(s: DecodeShape, seed: int | None = None):
         k = k * s.qk_std
     dt = s.torch_dtype
     return q.to(dt), k.to(dt), v.to(dt)
+
+
+# ---------------------------------------------------------------- rotary tables
+def rope_tables(N: int, d: int, base: float = 10000.0):
+    """Rotary tables cos/sin [N, d/2] of n * base^(-2i/d), computed in float64 and
+    rounded once to float32 (CPU tensors). The GPU path receives them as they are;
+    the oracle receives the same float32 values widened to float64."""
+    n = torch.arange(N, dtype=torch.float64)[:, None]
+    inv = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = n * inv[None, :]
+    return torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
