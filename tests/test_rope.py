@@ -132,3 +132,30 @@ def test_strided_copies_are_exact():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
     for a, b in zip(g1, g2):
         assert torch.equal(a, b)
+
+
+def test_rope_unaligned_views():
+    # rows d+1 elements apart, starting one element in: no 16-byte alignment, so the
+    # copies take their element-wise path
+    s = workloads.make_shape(2, 6, 2, 150, 64, dtype="bf16", seed=81)
+    q, k, v, do = workloads.make_inputs(s)
+    cos, sin = workloads.rope_tables(s.N, s.d, base=500.0)
+
+    def odd_view(t):
+        B, H, N, d = t.shape
+        buf = torch.zeros((B, H, N, d + 1), dtype=t.dtype, device="cuda")
+        view = buf[..., 1:]
+        view.copy_(t.cuda())
+        return view
+
+    qv, kv, vv = odd_view(q), odd_view(k), odd_view(v)
+    assert qv.data_ptr() % 16 != 0
+    cd, sd = cos.cuda(), sin.cuda()
+    outs = tuple(odd_view(torch.zeros(t.shape)) for t in (q, k, v))
+    o, lse = tca.attn_fwd_rope(qv, kv, vv, cd, sd, scale=s.scale)
+    dq, dk, dv = tca.attn_bwd_rope(qv, kv, vv, o, lse, do.cuda(), cd, sd, scale=s.scale, out=outs)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd_rope(q, k, v, cos, sin, 1, s.scale)
+    rq, rk, rv = oracle.attn_bwd_rope(q, k, v, do, cos, sin, 1, s.scale)
+    for name, got, ref in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+        check(name, got, ref, "bf16", False, "unaligned views")

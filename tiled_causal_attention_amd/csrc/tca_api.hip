@@ -144,16 +144,18 @@ attn_status check_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, co
     return ATTN_OK;
 }
 
-// q, k (rotated) and v into the contiguous staging copies
+// q, k (rotated) and v into the contiguous staging copies, one launch
 hipError_t stage_qkv(const RopeWs& w, attn_dtype dtype, const void* q, const attn_layout* ql, const void* k,
                      const attn_layout* kl, const void* v, const attn_layout* vl, const float* cs, const float* sn,
                      int B, int Hq, int Hkv, int N, int d, hipStream_t st) {
     const int rot = cs ? 1 : 0;
     const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
-    hipError_t e = tca::layout_copy(dtype, q, ql ? *ql : cq, dtype, w.q, cq, cs, sn, B, Hq, N, d, rot, st);
-    if (e == hipSuccess) e = tca::layout_copy(dtype, k, kl ? *kl : ck, dtype, w.k, ck, cs, sn, B, Hkv, N, d, rot, st);
-    if (e == hipSuccess) e = tca::layout_copy(dtype, v, vl ? *vl : ck, dtype, w.v, ck, nullptr, nullptr, B, Hkv, N, d, 0, st);
-    return e;
+    tca::CopyJobs jobs;
+    jobs.n = 3;
+    jobs.j[0] = tca::copy_job(q, ql ? *ql : cq, w.q, cq, B, Hq, N, d, rot);
+    jobs.j[1] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, rot);
+    jobs.j[2] = tca::copy_job(v, vl ? *vl : ck, w.v, ck, B, Hkv, N, d, 0);
+    return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
 }
 
 attn_status run_dq(const AttnArgs& a, hipStream_t st) {
@@ -304,7 +306,10 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
     const void* o_in = o;
     if (out_dtype == ATTN_BF16) {   // the backward runs with float32 outputs: widen o exactly
-        e = tca::layout_copy(ATTN_BF16, o, cq, ATTN_F32, w.o32, cq, nullptr, nullptr, B, Hq, N, d, 0, st);
+        tca::CopyJobs jobs;
+        jobs.n = 1;
+        jobs.j[0] = tca::copy_job(o, cq, w.o32, cq, B, Hq, N, d, 0);
+        e = tca::layout_copy(ATTN_BF16, ATTN_F32, jobs, nullptr, nullptr, N, d, st);
         if (e != hipSuccess) return ATTN_EHIP;
         o_in = w.o32;
     }
@@ -314,16 +319,14 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     if (s != ATTN_OK) return s;
     s = run_dkdv(a, st);
     if (s != ATTN_OK) return s;
+    // dq, dk turned back by the transpose rotation, dv copied; one launch
     const int rot = rope_cos ? 2 : 0;
-    e = tca::layout_copy(ATTN_F32, w.dq, cq, out_dtype, dq, dq_layout ? *dq_layout : cq, rope_cos, rope_sin, B, Hq,
-                         N, d, rot, st);
-    if (e == hipSuccess)
-        e = tca::layout_copy(ATTN_F32, w.dk, ck, out_dtype, dk, dk_layout ? *dk_layout : ck, rope_cos, rope_sin, B,
-                             Hkv, N, d, rot, st);
-    if (e == hipSuccess)
-        e = tca::layout_copy(ATTN_F32, w.dv, ck, out_dtype, dv, dv_layout ? *dv_layout : ck, nullptr, nullptr, B,
-                             Hkv, N, d, 0, st);
-    return from_hip(e);
+    tca::CopyJobs jobs;
+    jobs.n = 3;
+    jobs.j[0] = tca::copy_job(w.dq, cq, dq, dq_layout ? *dq_layout : cq, B, Hq, N, d, rot);
+    jobs.j[1] = tca::copy_job(w.dk, ck, dk, dk_layout ? *dk_layout : ck, B, Hkv, N, d, rot);
+    jobs.j[2] = tca::copy_job(w.dv, ck, dv, dv_layout ? *dv_layout : ck, B, Hkv, N, d, 0);
+    return from_hip(tca::layout_copy(ATTN_F32, out_dtype, jobs, rope_cos, rope_sin, N, d, st));
 }
 
 size_t attn_fwd_naive_workspace_bytes(int B, int Hq, int N) {

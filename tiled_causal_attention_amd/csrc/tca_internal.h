@@ -95,12 +95,25 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 
-// Strided copy of [B, H, N, d] tensors (head dimension contiguous) with an optional
-// rotary rotation of the (i, i + d/2) pairs at each row's position: rot 0 none,
-// 1 forward, 2 transpose; cs, sn [N][d/2].
-hipError_t layout_copy(attn_dtype ti, const void* src, const attn_layout& sl, attn_dtype to, void* dst,
-                       const attn_layout& dl, const float* cs, const float* sn, int B, int H, int N, int d, int rot,
-                       hipStream_t st);
+// Strided copies of [B, H, N, d] tensors (head dimension contiguous) with an
+// optional rotary rotation of the (i, i + d/2) pairs at each row's position:
+// rot 0 none, 1 forward, 2 transpose; cs, sn [N][d/2]. Up to three copies of
+// the same element types run in one launch.
+struct CopyJob {
+    const void* src;
+    void* dst;
+    long long sb, sh, sn, db, dh, dn;   // element strides (batch, head, row) of source and destination
+    int H, rot;
+    long long count, begin;             // threads of this job (one per 8 pairs of a row) and its first thread
+};
+struct CopyJobs {
+    CopyJob j[3];
+    int n;
+};
+CopyJob copy_job(const void* src, const attn_layout& sl, void* dst, const attn_layout& dl, int B, int H, int N, int d,
+                 int rot);
+hipError_t layout_copy(attn_dtype ti, attn_dtype to, const CopyJobs& jobs, const float* cs, const float* sn, int N,
+                       int d, hipStream_t st);
 
 // Unoptimised forward through a materialised score matrix (B*Hq*N*N floats of workspace).
 size_t naive_workspace_size(int B, int Hq, int N);
