@@ -107,6 +107,11 @@ def resource_usage_markdown() -> str:
                 args.append(lit.group(1))
                 i += lit.end()
                 continue
+            flag = re.match(r"Lb([01])E", rest[i:])
+            if flag:
+                args.append("true" if flag.group(1) == "1" else "false")
+                i += flag.end()
+                continue
             for code, ty in names.items():
                 if rest.startswith(code, i):
                     args.append(ty)

@@ -75,14 +75,49 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
     }
 }
 
-// OT: element type of o (read) and dq (written): float32 or bfloat16
-template <int D, typename OT>
+// Store one query row's dQ (val[x][a4] holds dims 32x + 8 a4 + 4h .. +3). ROPE: the
+// pairs (dim, dim + D/2) -- blocks x and x + D/64 of the same lane -- are turned
+// back by the transpose rotation at row position qi and written through rq's dq
+// strides; otherwise the row goes to `row` as it is.
+template <int D, typename OT, bool ROPE>
+__device__ __forceinline__ void store_dq_row(OT* row, const f32x4 (&val)[D / 32][4], const QRope& rq, int b, int hq,
+                                             int qi, int h) {
+    constexpr int DB = D / 32;
+    if constexpr (ROPE) {
+        OT* dst = static_cast<OT*>(rq.dq) + b * rq.gb + hq * rq.gh + qi * rq.gn;
+        const float* cr = rq.cs + (size_t)qi * (D / 2);
+        const float* sr = rq.sn + (size_t)qi * (D / 2);
+#pragma unroll
+        for (int x = 0; x < DB / 2; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) {
+                const int i0 = 32 * x + 8 * a4 + 4 * h;
+                const f32x4 c = *reinterpret_cast<const f32x4*>(cr + i0), s = *reinterpret_cast<const f32x4*>(sr + i0);
+                const f32x4 g1 = val[x][a4], g2 = val[x + DB / 2][a4];
+                store_out4(dst + i0, f32x4{g1[0] * c[0] + g2[0] * s[0], g1[1] * c[1] + g2[1] * s[1],
+                                           g1[2] * c[2] + g2[2] * s[2], g1[3] * c[3] + g2[3] * s[3]});
+                store_out4(dst + i0 + D / 2, f32x4{g2[0] * c[0] - g1[0] * s[0], g2[1] * c[1] - g1[1] * s[1],
+                                                   g2[2] * c[2] - g1[2] * s[2], g2[3] * c[3] - g1[3] * s[3]});
+            }
+    } else {
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4) store_out4(row + 32 * x + 8 * a4 + 4 * h, val[x][a4]);
+    }
+}
+
+// OT: element type of o (read) and dq (written): float32 or bfloat16.
+// ROPE: Q is read through rq's strides and rotated in registers (so the fp16 Q copy
+// left for the dK/dV pass is rotated too; K holds the rotated keys), and dQ is
+// turned back by the transpose rotation and stored through rq's dq strides.
+template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 2)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
               const OT* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
               _Float16* __restrict__ q16, _Float16* __restrict__ do16, OT* __restrict__ dq,
-              int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
+              int Hq, int Hkv, int N, int causal, float scale, int nqt, int units, QRope rq) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + kPad<D>;
     constexpr int NKH = kKeyHalves<D>;   // key parts per tile (one wave each)
@@ -131,15 +166,20 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     bf16x8 db[DC];
     float Di;
     {
-        const bf16_t* qrow = q + (bh * N + qc) * D + 8 * h;
+        const bf16_t* qrow = ROPE ? rq.q + tm.b * rq.qb + hq * rq.qh + qc * rq.qn + 8 * h
+                                  : q + (bh * N + qc) * D + 8 * h;
         const bf16_t* drow = dout + (bh * N + qc) * D + 8 * h;
         const OT* orow = o + (bh * N + qc) * D + 8 * h;
-        u32x4 dvr[DC];
+        u32x4 dvr[DC], qraw[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-            const u32x4 qv = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+            qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
             dvr[c] = *reinterpret_cast<const u32x4*>(drow + 16 * c);
-            const u32x4 qh16 = bf16x8_to_f16x8(qv);
+        }
+        if constexpr (ROPE) rope_rotate_q<D>(qraw, rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const u32x4 qh16 = bf16x8_to_f16x8(qraw[c]);
             qb[c] = qok ? __builtin_bit_cast(f16x8, qh16) : f16x8{};
             db[c] = qok ? __builtin_bit_cast(bf16x8, dvr[c]) : bf16x8{};
         }
@@ -263,15 +303,14 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     // query qi); with two key halves, their partial sums are first added through LDS
     if constexpr (NKH == 1) {
         if (qok) {
-            OT* row = dq + (bh * N + qi) * D;
+            f32x4 val[DB][4];
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
-                for (int a4 = 0; a4 < 4; ++a4) {
-                    const f32x4 val = {dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
+                for (int a4 = 0; a4 < 4; ++a4)
+                    val[x][a4] = f32x4{dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
                                        dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
-                    store_out4(row + 32 * x + 8 * a4 + 4 * h, val);
-                }
+            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, tm.b, hq, qi, h);
         }
     } else {
         // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
@@ -288,16 +327,16 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         }
         __syncthreads();
         if (khalf == 0 && qok) {
-            OT* row = dq + (bh * N + qi) * D;
+            f32x4 val[DB][4];
 #pragma unroll
             for (int x = 0; x < DB; ++x)
 #pragma unroll
                 for (int a4 = 0; a4 < 4; ++a4) {
                     const f32x4 o1 = *reinterpret_cast<const f32x4*>(xo + merge_off<D>(r, 8 * x + 2 * a4 + h));
-                    const f32x4 val = {(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
+                    val[x][a4] = f32x4{(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
                                        (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
-                    store_out4(row + 32 * x + 8 * a4 + 4 * h, val);
                 }
+            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, tm.b, hq, qi, h);
         }
     }
 }
@@ -709,15 +748,16 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     }
 }
 
-template <int D, typename OT>
+template <int D, typename OT, bool ROPE>
 static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + bwdq::kRows<D> - 1) / bwdq::kRows<D>;
     const int units = a.B * a.Hkv;
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    hipLaunchKernelGGL((bwd_dq_kernel<D, OT>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
+    const QRope rq = ROPE ? *a.rope : QRope{};
+    hipLaunchKernelGGL((bwd_dq_kernel<D, OT, ROPE>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
                        (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const OT*)a.o,
                        (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, (OT*)a.dq,
-                       a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units);
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units, rq);
     return hipGetLastError();
 }
 
@@ -733,10 +773,15 @@ static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st) {
+template <bool ROPE>
+static hipError_t launch_bwd_dq_rope_or_not(const AttnArgs& a, hipStream_t st) {
     if (a.out_dtype == ATTN_BF16)
-        return (a.d == 64) ? launch_bwd_dq_d<64, bf16_t>(a, st) : launch_bwd_dq_d<128, bf16_t>(a, st);
-    return (a.d == 64) ? launch_bwd_dq_d<64, float>(a, st) : launch_bwd_dq_d<128, float>(a, st);
+        return (a.d == 64) ? launch_bwd_dq_d<64, bf16_t, ROPE>(a, st) : launch_bwd_dq_d<128, bf16_t, ROPE>(a, st);
+    return (a.d == 64) ? launch_bwd_dq_d<64, float, ROPE>(a, st) : launch_bwd_dq_d<128, float, ROPE>(a, st);
+}
+
+hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st) {
+    return a.rope ? launch_bwd_dq_rope_or_not<true>(a, st) : launch_bwd_dq_rope_or_not<false>(a, st);
 }
 hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st) {
     if (a.out_dtype == ATTN_BF16)

@@ -98,12 +98,14 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
     }
 }
 
-// OT: element type of o (float32, or bfloat16 rounded to nearest even at the store)
-template <int D, typename OT>
+// OT: element type of o (float32, or bfloat16 rounded to nearest even at the store).
+// ROPE: Q is read through rq's strides and rotated in registers (rotary embedding);
+// K and V then hold the rotated keys and the values, contiguous.
+template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, OT* __restrict__ o, float* __restrict__ lse,
-                int Hq, int Hkv, int N, int causal, float scale, int nqt, int units) {
+                int Hq, int Hkv, int N, int causal, float scale, int nqt, int units, QRope rq) {
     using namespace fwd;
     constexpr int DC = D / 16;          // 16-deep chunks of the head dimension
     constexpr int DB = D / 32;          // 32-wide blocks of the head dimension
@@ -138,12 +140,15 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]
     bf16x8 qb[DC];
     {
-        const bf16_t* qrow = qh + (size_t)min(qi, N - 1) * D + 8 * h;
+        const int qc = min(qi, N - 1);
+        const bf16_t* qrow = ROPE ? rq.q + tm.b * rq.qb + hq * rq.qh + qc * rq.qn + 8 * h
+                                  : qh + (size_t)qc * D + 8 * h;
+        u32x4 qraw[DC];
 #pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            const bf16x8 val = *reinterpret_cast<const bf16x8*>(qrow + 16 * c);
-            qb[c] = (qi < N) ? val : bf16x8{};
-        }
+        for (int c = 0; c < DC; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+        if constexpr (ROPE) rope_rotate_q<D>(qraw, rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
     }
 
     // K/V tile prefetch registers: thread owns chunks tid + NT u (coalesced rows)
@@ -318,21 +323,27 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
 bool mfma_path(const AttnArgs& a) { return mfma_shape(a.dtype, a.d); }
 
-template <int D, typename OT>
+template <int D, typename OT, bool ROPE>
 static hipError_t launch_fwd_d(const AttnArgs& a, hipStream_t st) {
     const int nqt = (a.N + fwd::kRows<D> - 1) / fwd::kRows<D>;
     const int units = a.B * a.Hkv;
     const dim3 grid((unsigned)(nqt * a.B * a.Hq));
-    hipLaunchKernelGGL((fwd_mfma_kernel<D, OT>), grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
+    const QRope rq = ROPE ? *a.rope : QRope{};
+    hipLaunchKernelGGL((fwd_mfma_kernel<D, OT, ROPE>), grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
                        (const bf16_t*)a.k, (const bf16_t*)a.v, (OT*)a.o, a.lse, a.Hq, a.Hkv, a.N, a.causal,
-                       a.scale, nqt, units);
+                       a.scale, nqt, units, rq);
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
+template <bool ROPE>
+static hipError_t launch_fwd_rope_or_not(const AttnArgs& a, hipStream_t st) {
     if (a.out_dtype == ATTN_BF16)
-        return (a.d == 64) ? launch_fwd_d<64, bf16_t>(a, st) : launch_fwd_d<128, bf16_t>(a, st);
-    return (a.d == 64) ? launch_fwd_d<64, float>(a, st) : launch_fwd_d<128, float>(a, st);
+        return (a.d == 64) ? launch_fwd_d<64, bf16_t, ROPE>(a, st) : launch_fwd_d<128, bf16_t, ROPE>(a, st);
+    return (a.d == 64) ? launch_fwd_d<64, float, ROPE>(a, st) : launch_fwd_d<128, float, ROPE>(a, st);
+}
+
+hipError_t launch_fwd_mfma(const AttnArgs& a, hipStream_t st) {
+    return a.rope ? launch_fwd_rope_or_not<true>(a, st) : launch_fwd_rope_or_not<false>(a, st);
 }
 
 }  // namespace tca

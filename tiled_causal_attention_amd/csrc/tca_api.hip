@@ -158,6 +158,45 @@ hipError_t stage_qkv(const RopeWs& w, attn_dtype dtype, const void* q, const att
     return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
 }
 
+// Q (and dQ) read / written in place by the matrix-core kernels: rows 16-byte aligned
+bool rows_aligned16(const void* p, const attn_layout* l, size_t es) {
+    if (p == nullptr || (uintptr_t)p % 16 != 0) return false;
+    if (l == nullptr) return true;
+    return ((size_t)l->stride_b * es) % 16 == 0 && ((size_t)l->stride_h * es) % 16 == 0 &&
+           ((size_t)l->stride_n * es) % 16 == 0;
+}
+
+// k (rotated) and v into the contiguous staging copies, one launch (q is rotated in
+// the kernels' registers on the fused path)
+hipError_t stage_kv(const RopeWs& w, attn_dtype dtype, const void* k, const attn_layout* kl, const void* v,
+                    const attn_layout* vl, const float* cs, const float* sn, int B, int Hkv, int N, int d,
+                    hipStream_t st) {
+    const attn_layout ck = contiguous_layout(Hkv, N, d);
+    tca::CopyJobs jobs;
+    jobs.n = 2;
+    jobs.j[0] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, 1);
+    jobs.j[1] = tca::copy_job(v, vl ? *vl : ck, w.v, ck, B, Hkv, N, d, 0);
+    return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
+}
+
+tca::QRope make_qrope(const void* q, const attn_layout* ql, const float* cs, const float* sn, void* dq,
+                      const attn_layout* gl, int Hq, int N, int d) {
+    const attn_layout cq = contiguous_layout(Hq, N, d);
+    const attn_layout a = ql ? *ql : cq, g = gl ? *gl : cq;
+    tca::QRope r;
+    r.q = static_cast<const tca::bf16_t*>(q);
+    r.qb = a.stride_b;
+    r.qh = a.stride_h;
+    r.qn = a.stride_n;
+    r.dq = dq;
+    r.gb = g.stride_b;
+    r.gh = g.stride_h;
+    r.gn = g.stride_n;
+    r.cs = cs;
+    r.sn = sn;
+    return r;
+}
+
 attn_status run_dq(const AttnArgs& a, hipStream_t st) {
     return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma_dq(a, st) : tca::launch_bwd_generic_dq(a, st));
 }
@@ -274,6 +313,16 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const RopeWs w = rope_ws(workspace, false, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
+    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2)) {
+        // fused: the forward reads q through its strides and rotates it in registers
+        if (stage_kv(w, dtype, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
+            return ATTN_EHIP;
+        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, nullptr, nullptr, Hq, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, q, w.k, w.v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                               B, Hq, Hkv, N, d, causal, scale);
+        a.rope = &rq;
+        return from_hip(tca::launch_fwd_mfma(a, st));
+    }
     hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
     if (e != hipSuccess) return ATTN_EHIP;
     const AttnArgs a = make_args(dtype, out_dtype, w.q, w.k, w.v, o, lse, nullptr, nullptr, nullptr, nullptr,
@@ -301,6 +350,31 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const RopeWs w = rope_ws(workspace, true, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
+    const attn_layout ckv = contiguous_layout(Hkv, N, d);
+    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
+        rows_aligned16(dq, dq_layout, elsize(out_dtype))) {
+        // fused: the dQ pass reads q through its strides, rotates it in registers (its fp16
+        // copy for the dK/dV pass is rotated too) and stores dq turned back through dq's
+        // strides; k, v are staged and dk, dv scattered as below
+        if (stage_kv(w, dtype, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
+            return ATTN_EHIP;
+        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, Hq, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, q, w.k, w.v, o, lse, dO, dq, w.dk, w.dv, w.bwd, w.bwd_bytes, B, Hq,
+                               Hkv, N, d, causal, scale);
+        a.rope = &rq;
+        s = run_dq(a, st);
+        if (s != ATTN_OK) return s;
+        AttnArgs a2 = a;   // dK/dV into float32 temporaries (one rounding after the rotation)
+        a2.rope = nullptr;
+        a2.out_dtype = ATTN_F32;
+        s = run_dkdv(a2, st);
+        if (s != ATTN_OK) return s;
+        tca::CopyJobs jobs;
+        jobs.n = 2;
+        jobs.j[0] = tca::copy_job(w.dk, ckv, dk, dk_layout ? *dk_layout : ckv, B, Hkv, N, d, 2);
+        jobs.j[1] = tca::copy_job(w.dv, ckv, dv, dv_layout ? *dv_layout : ckv, B, Hkv, N, d, 0);
+        return from_hip(tca::layout_copy(ATTN_F32, out_dtype, jobs, rope_cos, rope_sin, N, d, st));
+    }
     hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
     if (e != hipSuccess) return ATTN_EHIP;
     const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);

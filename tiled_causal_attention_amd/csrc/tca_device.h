@@ -268,6 +268,47 @@ __device__ __forceinline__ void load8_f32(const bf16_t* p, float (&x)[8]) {
     x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
+// Rotary embedding of the query side, for kernels that rotate Q in registers
+// (rotate-half pairing: dims i and i + D/2, cos/sin = table[n][i] at row n) and,
+// in the dQ pass, turn dQ back by the transpose rotation at the store. Q and dQ
+// are read / written through element strides (batch, head, row); the head
+// dimension is contiguous and every row start 16-byte aligned.
+struct QRope {
+    const bf16_t* q;
+    long long qb, qh, qn;    // q strides
+    void* dq;                // dq in the output type
+    long long gb, gh, gn;    // dq strides
+    const float* cs;         // [N][D/2]
+    const float* sn;
+};
+
+// Rotate the Q chunks a lane holds: chunk c (dims 16c + 8h .. +7) pairs with chunk
+// c + D/32 (the same dims + D/2). The rotated values are rounded to bfloat16.
+template <int D>
+__device__ __forceinline__ void rope_rotate_q(u32x4 (&qr)[D / 16], const float* cs_row, const float* sn_row, int h) {
+    constexpr int DC = D / 16;
+#pragma unroll
+    for (int c = 0; c < DC / 2; ++c) {
+        const int i0 = 16 * c + 8 * h;
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs_row + i0), c1 = *reinterpret_cast<const f32x4*>(cs_row + i0 + 4);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sn_row + i0), s1 = *reinterpret_cast<const f32x4*>(sn_row + i0 + 4);
+        const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+        const u32x4 a = qr[c], b = qr[c + DC / 2];
+        const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+        uint32_t ra[4], rbw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float a0 = bf16_lo(aw[t]), a1 = bf16_hi(aw[t]), b0 = bf16_lo(bw[t]), b1 = bf16_hi(bw[t]);
+            const float c_0 = cv[2 * t], c_1 = cv[2 * t + 1], s_0 = sv[2 * t], s_1 = sv[2 * t + 1];
+            ra[t] = pack_bf16(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
+            rbw[t] = pack_bf16(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
+        }
+        qr[c] = u32x4{ra[0], ra[1], ra[2], ra[3]};
+        qr[c + DC / 2] = u32x4{rbw[0], rbw[1], rbw[2], rbw[3]};
+    }
+}
+
 template <typename T>
 __device__ __forceinline__ float load_as_f32(const T* p);
 template <>

@@ -26,6 +26,10 @@ struct AttnArgs {
     size_t workspace_bytes;
     int B, Hq, Hkv, N, d, causal;
     float scale;
+    // matrix-core path only: Q read through these strides and rotated in registers
+    // (k, v hold the rotated keys and the values); the dQ pass stores dQ turned back
+    // by the transpose rotation through rope->dq's strides. nullptr: plain layout.
+    const QRope* rope = nullptr;
 };
 
 // True when the matrix-core kernels serve these inputs: bf16, d in {64, 128}.
