@@ -267,3 +267,35 @@ def test_bwd_workspace_contents(d):
     dref = (do.double().numpy() * ro).sum(-1)
     # D from the kernel's own O (fp32) differs from the oracle's by the forward's rounding
     assert np.abs(neg_d + dref).max() <= 1e-2 * max(1.0, np.abs(dref).max())
+
+
+@pytest.mark.parametrize("Hq,Hkv,d", [(4, 1, 64), (2, 1, 128)])
+def test_longest_sequence_sampled(Hq, Hkv, d):
+    """N = 16384, twice the longest named workload: sampled rows and keys against the
+    oracle (its row statistics run over every row of the unit), plus the full-size
+    properties sum_j dK_j = 0 (softmax shift invariance) and sum_j dV_j = sum_i dO_i."""
+    N = 16384
+    s = workloads.make_shape(1, Hq, Hkv, N, d, dtype="bf16", seed=1600 + d)
+    print(f"[parity] N={N} d={d}", flush=True)
+    q, k, v, do = workloads.make_inputs(s)
+    g = run_gpu(q, k, v, do, 1, s.scale)
+    G = Hq // Hkv
+    rows = [(gg, i) for gg in range(G) for i in (0, 1, 4095, 8192, N - 65, N - 1)]
+    keys = [0, 1, 8191, N - 64, N - 1]
+    ref = oracle.attn_sampled(q, k, v, do, 0, 0, rows, keys, 1, s.scale)
+    hq = [gg for gg, _ in rows]
+    ii = [i for _, i in rows]
+    ctx = f"N={N} d={d}"
+    check("o", g["o"][0, hq, ii], ref["o"], "bf16", ctx)
+    check("lse", g["lse"][0, hq, ii], ref["lse"], "bf16", ctx)
+    check("dq", g["dq"][0, hq, ii], ref["dq"], "bf16", ctx)
+    check("dk", g["dk"][0, 0, keys], ref["dk"], "bf16", ctx)
+    check("dv", g["dv"][0, 0, keys], ref["dv"], "bf16", ctx)
+    # full size: dK sums to zero over the keys (relative to the summed magnitudes: the rounding of
+    # P and dS leaves a residue, no systematic term); dV sums to the group's dO (fp16 P rows sum
+    # to 1 within 2^-11, so within 2^-10 of the summed |dO|)
+    dkf = g["dk"][0, 0].sum(axis=0)
+    assert (np.abs(dkf) <= 1e-2 * np.abs(g["dk"][0, 0]).sum(axis=0)).all()
+    dof = do.double().numpy()[0].sum(axis=(0, 1))
+    bound = 2.0 ** -10 * np.abs(do.double().numpy()[0]).sum(axis=(0, 1))
+    assert (np.abs(g["dv"][0, 0].sum(axis=0) - dof) <= bound + 1e-3).all()
