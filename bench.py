@@ -374,6 +374,11 @@ def decode_report(args):
     import numpy as np
     import oracle
     out_dt = OUT_DTYPES[args.out_dtype]
+    if args.calibrate_copy:   # a plain 256 MiB device copy, the reference for --pmc byte counters
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        torch.empty_like(src).copy_(src)
+        torch.cuda.synchronize()
+        del src
     for name, s in workloads.DECODE_CONFIGS.items():
         inputs = workloads.make_decode_inputs(s)
         q, k, v = (t.cuda() for t in inputs)
