@@ -297,13 +297,13 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 }
 
 // Merge of the splits of one row: LSE = log2 sum_s 2^LSE_s (log2 units in lpart),
-// O = sum_s 2^(LSE_s - LSE) O_s. One workgroup of 4 waves per row, one row's
-// merge being a short reduction whose cost is load latency: thread t takes the
-// maximum and weight sum over splits t, t + 256, ... (workgroup reductions
-// through LDS), then wave w accumulates columns 2 lane, 2 lane + 1 over splits
-// w, w + 4, ..., with all of its loads issued before the adds; the four partial
-// columns are summed through LDS. Split 0 holds key 0, visible to every row, so
-// the maximum is finite.
+// O = sum_s 2^(LSE_s - LSE) O_s. One workgroup of 256 threads per row: thread t
+// takes the maximum and weight sum over splits t, t + 256, ... (workgroup
+// reductions through LDS, the weights kept in LDS), then thread t = (split group
+// g, column pair p) accumulates columns 2p, 2p + 1 over splits g, g + NG, ...
+// (NG = 512 / D groups), with its partial sums added across the groups through
+// LDS. Every thread loads only its own splits. Split 0 holds key 0, visible to
+// every row, so the maximum is finite.
 constexpr int kMergeThreads = 256;
 template <typename OT, int D>
 __global__ void __launch_bounds__(kMergeThreads)
@@ -311,24 +311,14 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
                     float* __restrict__ lse, int nrows, int nsplit) {
     constexpr int NW = kMergeThreads / 64;
     constexpr int MAXS = 256;                 // splits per row at most (decode_plan caps it)
-    constexpr int PER_WAVE = MAXS / NW;       // splits a wave may own
+    constexpr int NP = D / 2;                 // column pairs
+    constexpr int NG = kMergeThreads / NP;    // split groups
     __shared__ float red[NW];
     __shared__ float wsh[MAXS];
-    __shared__ float part[NW][D];
+    __shared__ float2 part[NG][NP];
     const int row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    // every load of the merge goes out first: the partial columns and the LSEs are
-    // independent, so the merge waits for one round of memory latency
-    const bool col = 2 * lane < D;
-    float x0[PER_WAVE], x1[PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-        const int sidx = w + NW * i;
-        const bool on = col && sidx < nsplit;
-        const float* src = opart + ((size_t)(on ? sidx : 0) * nrows + row) * D + (col ? 2 * lane : 0);
-        x0[i] = on ? src[0] : 0.f;
-        x1[i] = on ? src[1] : 0.f;
-    }
+    const int p = tid % NP, g = tid / NP;
     const float ls = tid < nsplit ? lpart[(size_t)tid * nrows + row] : -INFINITY;
     float mx = ls;
 #pragma unroll
@@ -346,25 +336,25 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     __syncthreads();
     sum = (red[0] + red[1]) + (red[2] + red[3]);
     float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < PER_WAVE; ++i) {
-        const int sidx = w + NW * i;
-        const float wgt = sidx < nsplit ? wsh[sidx] : 0.f;
-        a0 = fmaf(wgt, x0[i], a0);
-        a1 = fmaf(wgt, x1[i], a1);
+#pragma unroll 4
+    for (int sidx = g; sidx < nsplit; sidx += NG) {
+        const float2 x = *reinterpret_cast<const float2*>(opart + ((size_t)sidx * nrows + row) * D + 2 * p);
+        const float wgt = wsh[sidx];
+        a0 = fmaf(wgt, x.x, a0);
+        a1 = fmaf(wgt, x.y, a1);
     }
-    if (col) {
-        part[w][2 * lane] = a0;
-        part[w][2 * lane + 1] = a1;
-    }
+    part[g][p] = float2{a0, a1};
     __syncthreads();
-    if (w == 0 && col) {
+    if (g == 0) {
+        float r0 = 0.f, r1 = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < NG; ++gg) {
+            r0 += part[gg][p].x;
+            r1 += part[gg][p].y;
+        }
         const float inv = 1.f / sum;
-        const float r0 = (part[0][2 * lane] + part[1][2 * lane]) + (part[2][2 * lane] + part[3][2 * lane]);
-        const float r1 = (part[0][2 * lane + 1] + part[1][2 * lane + 1]) +
-                         (part[2][2 * lane + 1] + part[3][2 * lane + 1]);
-        store_out1(o + (size_t)row * D + 2 * lane, r0 * inv);
-        store_out1(o + (size_t)row * D + 2 * lane + 1, r1 * inv);
+        store_out1(o + (size_t)row * D + 2 * p, r0 * inv);
+        store_out1(o + (size_t)row * D + 2 * p + 1, r1 * inv);
     }
     if (tid == 0) lse[row] = (mx + __log2f(sum)) * kLn2;
 }
