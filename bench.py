@@ -401,6 +401,36 @@ def decode_report(args):
         t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
         med = float(np.median(t))
         nbytes = s.min_bytes(2 if args.out_dtype == "bf16" else 4)
+        # second, labelled number: 20 calls captured in a HIP graph and replayed, so that no
+        # host work sits between the launches; every replay's output is checked against
+        # the eager result (bitwise: same kernels, same inputs)
+        graph_us = None
+        try:
+            o_ref, l_ref = o.clone(), lse.clone()
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                with torch.cuda.graph(g, stream=side):
+                    for _ in range(20):
+                        tca.attn_decode(q, k, v, causal, scale, out=(o, lse), workspace=ws)
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            gt = []
+            for _ in range(10):
+                o.zero_()
+                g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                g0.record()
+                g.replay()
+                g1.record()
+                torch.cuda.synchronize()
+                if not (torch.equal(o, o_ref) and torch.equal(lse, l_ref)):
+                    raise RuntimeError("graph replay differs from the eager result")
+                gt.append(g0.elapsed_time(g1) / 20)
+            graph_us = float(np.median(gt)) * 1e3
+            del g
+        except Exception as e:  # noqa: BLE001 -- reported, the eager number stands
+            print(f"graph replay not measured: {e}", file=sys.stderr)
         ro, rl = oracle.attn_decode(*inputs, s.causal, s.scale)
         t0 = time.perf_counter()
         oracle.attn_decode(*inputs, s.causal, s.scale)
@@ -410,6 +440,8 @@ def decode_report(args):
                "median_ms": med, "p10_ms": float(np.percentile(t, 10)), "p90_ms": float(np.percentile(t, 90)),
                "min_hbm_bytes": nbytes, "gb_per_s": nbytes / (med * 1e-3) / 1e9,
                "frac_hbm_peak": nbytes / (med * 1e-3) / 8e12,
+               "graph_replay_us_per_call": graph_us,
+               "graph_replay_gb_per_s": (nbytes / (graph_us * 1e-6) / 1e9) if graph_us else None,
                "max_abs_o": float(np.abs(o.float().cpu().double().numpy() - ro).max()),
                "max_abs_lse": float(np.abs(lse.cpu().double().numpy() - rl).max()),
                "oracle": {"seconds": t_or, "threads": oracle.threads(),
