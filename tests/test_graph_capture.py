@@ -1,0 +1,82 @@
+"""The library's calls captured in a HIP graph (they launch kernels only: no
+memsets, no allocation, no host synchronisation) and replayed several times, with
+eager work and synchronisations between the replays; every replay must equal the
+eager result bit for bit (the same kernels on the same inputs)."""
+import pytest
+import torch
+
+import tiled_causal_attention_amd as tca
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tca.lib()
+    yield
+
+
+def capture(fn):
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("name", ["gpt2_gqa", "tiny_f32"])
+def test_fwd_bwd_graph_replays_match_eager(name):
+    s = workloads.CONFIGS[name]
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(s))
+    o = torch.empty((s.B, s.Hq, s.N, s.d), device="cuda")
+    lse = torch.empty((s.B, s.Hq, s.N), device="cuda")
+    dq, dk, dv = (torch.empty(t.shape, device="cuda") for t in (q, k, v))
+    ws = tca.bwd_workspace(q, k)
+
+    def step():
+        tca.attn_fwd(q, k, v, True, s.scale, out=(o, lse))
+        tca.attn_bwd(q, k, v, o, lse, do, True, s.scale, out=(dq, dk, dv), workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse, dq, dk, dv)]
+    g = capture(step)
+    for rep in range(4):
+        for t in (o, lse, dq, dk, dv):
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((o, lse, dq, dk, dv), ref):
+            assert torch.equal(a, b), f"replay {rep}"
+        step()   # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_decode_graph_replays_match_eager():
+    s = workloads.DECODE_CONFIGS["decode_wide_d128"]
+    q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
+    o = torch.empty((s.B, s.Hq, s.Nq, s.d), device="cuda")
+    lse = torch.empty((s.B, s.Hq, s.Nq), device="cuda")
+    n = int(tca.lib().attn_decode_workspace_bytes(tca.ATTN_BF16, s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d))
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    call = lambda: tca.attn_decode(q, k, v, True, s.scale, out=(o, lse), workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    ref = (o.clone(), lse.clone())
+    g = capture(call)
+    for rep in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"replay {rep}"
+        call()
+        torch.cuda.synchronize()
