@@ -158,6 +158,8 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     u32x4 kreg[KCH], vreg[KCH];
     bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
     const float lse_i = lse[bh * N + qc];
+    QRopeRow<D> qtab;   // ROPE: the row's table values, issued with the first loads
+    if constexpr (ROPE) qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
 
     // Q (fp16) and dO (bf16) rows of this lane's query as B operands, and D_i:
     // key half 0 loads the O rows and computes D, key half 1 takes it from LDS
@@ -176,7 +178,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
             dvr[c] = *reinterpret_cast<const u32x4*>(drow + 16 * c);
         }
-        if constexpr (ROPE) rope_rotate_q<D>(qraw, rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
+        if constexpr (ROPE) rope_rotate_q<D>(qraw, qtab);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
             const u32x4 qh16 = bf16x8_to_f16x8(qraw[c]);

@@ -137,18 +137,24 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* qh = q + bh * N * D;
     const float sl2 = scale * kLog2e;      // scores in log2 units
 
-    // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]
+    // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]. With ROPE
+    // the row's table values are loaded next to it and the rotation waits until the
+    // first K/V tile is staged, so both loads' latency overlaps the tile loads.
     bf16x8 qb[DC];
+    u32x4 qraw[DC];
+    QRopeRow<D> qtab;
     {
         const int qc = min(qi, N - 1);
         const bf16_t* qrow = ROPE ? rq.q + tm.b * rq.qb + hq * rq.qh + qc * rq.qn + 8 * h
                                   : qh + (size_t)qc * D + 8 * h;
-        u32x4 qraw[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-        if constexpr (ROPE) rope_rotate_q<D>(qraw, rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
+        if constexpr (ROPE) {
+            qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
+        } else {
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
+            for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
+        }
     }
 
     // K/V tile prefetch registers: thread owns chunks tid + NT u (coalesced rows)
@@ -183,6 +189,11 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     store_kv_tile<D, KCH>(kreg, vreg, kst0, vst0);
     if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
     __syncthreads();
+    if constexpr (ROPE) {
+        rope_rotate_q<D>(qraw, qtab);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
+    }
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;

@@ -282,16 +282,32 @@ struct QRope {
     const float* sn;
 };
 
+// The cos/sin values a lane needs to rotate its Q chunks: frequencies 16c + 8h .. +7
+// for chunks c < D/32 of the row's table entries. Loaded on their own so that a
+// kernel can issue them early and rotate later.
+template <int D>
+struct QRopeRow {
+    f32x4 c[D / 32][2], s[D / 32][2];
+    __device__ __forceinline__ void load(const float* cs_row, const float* sn_row, int h) {
+#pragma unroll
+        for (int k = 0; k < D / 32; ++k) {
+            const int i0 = 16 * k + 8 * h;
+            c[k][0] = *reinterpret_cast<const f32x4*>(cs_row + i0);
+            c[k][1] = *reinterpret_cast<const f32x4*>(cs_row + i0 + 4);
+            s[k][0] = *reinterpret_cast<const f32x4*>(sn_row + i0);
+            s[k][1] = *reinterpret_cast<const f32x4*>(sn_row + i0 + 4);
+        }
+    }
+};
+
 // Rotate the Q chunks a lane holds: chunk c (dims 16c + 8h .. +7) pairs with chunk
 // c + D/32 (the same dims + D/2). The rotated values are rounded to bfloat16.
 template <int D>
-__device__ __forceinline__ void rope_rotate_q(u32x4 (&qr)[D / 16], const float* cs_row, const float* sn_row, int h) {
+__device__ __forceinline__ void rope_rotate_q(u32x4 (&qr)[D / 16], const QRopeRow<D>& tab) {
     constexpr int DC = D / 16;
 #pragma unroll
     for (int c = 0; c < DC / 2; ++c) {
-        const int i0 = 16 * c + 8 * h;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs_row + i0), c1 = *reinterpret_cast<const f32x4*>(cs_row + i0 + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(sn_row + i0), s1 = *reinterpret_cast<const f32x4*>(sn_row + i0 + 4);
+        const f32x4 c0 = tab.c[c][0], c1 = tab.c[c][1], s0 = tab.s[c][0], s1 = tab.s[c][1];
         const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
         const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
         const u32x4 a = qr[c], b = qr[c + DC / 2];
