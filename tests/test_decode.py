@@ -79,6 +79,8 @@ SHAPES = [
     (1, 6, 2, 3, 150, 64, "f32"),
     (2, 4, 1, 2, 1000, 128, "f32"),
     (1, 2, 1, 17, 17, 32, "f32"),
+    (1, 4, 2, 1, 4000, 32, "bf16"),    # 63 splits: the merge splits each row's columns
+    (1, 4, 1, 1, 5000, 128, "f32"),    # 79 splits, float32 inputs
 ]
 
 

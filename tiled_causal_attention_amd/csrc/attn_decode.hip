@@ -297,26 +297,33 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 }
 
 // Merge of the splits of one row: LSE = log2 sum_s 2^LSE_s (log2 units in lpart),
-// O = sum_s 2^(LSE_s - LSE) O_s. One workgroup of 256 threads per row: thread t
-// takes the maximum and weight sum over splits t, t + 256, ... (workgroup
-// reductions through LDS, the weights kept in LDS), then thread t = (split group
-// g, column pair p) accumulates columns 2p, 2p + 1 over splits g, g + NG, ...
-// (NG = 512 / D groups), with its partial sums added across the groups through
-// LDS. Every thread loads only its own splits. Split 0 holds key 0, visible to
-// every row, so the maximum is finite.
+// O = sum_s 2^(LSE_s - LSE) O_s. CB = D / (2 NP) workgroups of 256 threads per
+// row, each owning NP column pairs: with many splits NP = 16 (4 workgroups per
+// row at d = 128, so a few dozen rows still spread over the CUs), with few one
+// workgroup takes the whole row (NP = D / 2). In each, thread t takes the
+// maximum and weight sum over split t (workgroup reductions through LDS, the
+// weights kept in LDS; every workgroup of a row computes the same values), then
+// thread t = (split group g, column pair p) accumulates its two columns over
+// splits g, g + NG, ... (NG = 256 / NP groups), with the partial sums added
+// across the groups through LDS in a fixed order. Every thread loads only its
+// own splits. Split 0 holds key 0, visible to every row, so the maximum is
+// finite.
 constexpr int kMergeThreads = 256;
-template <typename OT, int D>
+constexpr int kMergeColSplits = 32;   // more splits per row than this: column blocks of 16 pairs
+template <typename OT, int D, int NP>
 __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ lpart, OT* __restrict__ o,
                     float* __restrict__ lse, int nrows, int nsplit) {
     constexpr int NW = kMergeThreads / 64;
     constexpr int MAXS = 256;                 // splits per row at most (decode_plan caps it)
-    constexpr int NP = D / 2;                 // column pairs
+    constexpr int CB = D / (2 * NP);          // workgroups per row
     constexpr int NG = kMergeThreads / NP;    // split groups
+    static_assert(kMergeThreads % NP == 0 && NP * CB * 2 == D, "merge tiling");
     __shared__ float red[NW];
     __shared__ float wsh[MAXS];
     __shared__ float2 part[NG][NP];
-    const int row = blockIdx.x;
+    const int row = blockIdx.x / CB;
+    const int c0 = 2 * NP * (blockIdx.x % CB);   // first column of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int p = tid % NP, g = tid / NP;
     const float ls = tid < nsplit ? lpart[(size_t)tid * nrows + row] : -INFINITY;
@@ -338,7 +345,7 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     float a0 = 0.f, a1 = 0.f;
 #pragma unroll 4
     for (int sidx = g; sidx < nsplit; sidx += NG) {
-        const float2 x = *reinterpret_cast<const float2*>(opart + ((size_t)sidx * nrows + row) * D + 2 * p);
+        const float2 x = *reinterpret_cast<const float2*>(opart + ((size_t)sidx * nrows + row) * D + c0 + 2 * p);
         const float wgt = wsh[sidx];
         a0 = fmaf(wgt, x.x, a0);
         a1 = fmaf(wgt, x.y, a1);
@@ -353,10 +360,10 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
             r1 += part[gg][p].y;
         }
         const float inv = 1.f / sum;
-        store_out1(o + (size_t)row * D + 2 * p, r0 * inv);
-        store_out1(o + (size_t)row * D + 2 * p + 1, r1 * inv);
+        store_out1(o + (size_t)row * D + c0 + 2 * p, r0 * inv);
+        store_out1(o + (size_t)row * D + c0 + 2 * p + 1, r1 * inv);
     }
-    if (tid == 0) lse[row] = (mx + __log2f(sum)) * kLn2;
+    if (c0 == 0 && tid == 0) lse[row] = (mx + __log2f(sum)) * kLn2;
 }
 
 // ---------------------------------------------------------------- host side
@@ -401,9 +408,14 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     hipLaunchKernelGGL((decode_split_kernel<T, OT, D, RM>), grid, dim3(64 * dec::kWaves), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (OT*)a.o, a.lse, opart, lpart, a.Hq,
                        a.Hkv, a.Nq, a.Nk, a.causal, a.scale, p.nrc, p.nsplit, p.split_len, nitems, nrows);
-    if (p.nsplit > 1)
-        hipLaunchKernelGGL((decode_merge_kernel<OT, D>), dim3((unsigned)nrows), dim3(kMergeThreads), 0, st, opart, lpart,
-                           (OT*)a.o, a.lse, nrows, p.nsplit);
+    if (p.nsplit > kMergeColSplits && D >= 32) {
+        constexpr int NP = D >= 32 ? 16 : D / 2;
+        hipLaunchKernelGGL((decode_merge_kernel<OT, D, NP>), dim3((unsigned)((long long)nrows * (D / (2 * NP)))),
+                           dim3(kMergeThreads), 0, st, opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
+    } else if (p.nsplit > 1) {
+        hipLaunchKernelGGL((decode_merge_kernel<OT, D, D / 2>), dim3((unsigned)nrows), dim3(kMergeThreads), 0, st,
+                           opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
+    }
     return hipGetLastError();
 }
 
