@@ -81,6 +81,7 @@ SHAPES = [
     (1, 2, 1, 17, 17, 32, "f32"),
     (1, 4, 2, 1, 4000, 32, "bf16"),    # 63 splits: the merge splits each row's columns
     (1, 4, 1, 1, 5000, 128, "f32"),    # 79 splits, float32 inputs
+    (1, 4, 1, 1, 16384, 64, "bf16"),   # 256 splits of 64 keys: the most a row can have
 ]
 
 
