@@ -67,7 +67,10 @@
  * Supported shapes: B >= 0, N >= 0 (B*N == 0 is a no-op that returns ATTN_OK
  * and ignores every pointer), Hq >= 1, Hkv >= 1, Hq % Hkv == 0,
  * d in {16, 32, 64, 128}, (N+64)*d < 2^31, B*Hq*N < 2^31, causal in {0, 1},
- * scale finite.
+ * scale finite. Any finite scale follows the definitions above, including 0
+ * (every visible key gets the same weight; dq = dk = 0) and negative values
+ * (masked keys stay excluded: the matrix-core kernels form the scores as
+ * |scale| * <sgn(scale) q_i, k_j>, exactly equal to scale * <q_i, k_j>).
  */
 #ifndef TCA_H
 #define TCA_H

@@ -187,6 +187,46 @@ def test_python_binding_checks_output_dtypes():
         tca.attn_bwd(q, q, q, obf, lse, q, out=(obf, o32, obf), workspace=torch.zeros(1))
 
 
+def test_python_binding_checks_every_shape():
+    """Each tensor is checked against q's and k's sizes before any pointer reaches the
+    C ABI (the kernels size their walks from B, Hq, Hkv, N, d alone). The checks come
+    before the device check, so they are visible here on CPU tensors."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(2, 6, 40, 64, dtype=bf)
+    k = torch.zeros(2, 2, 40, 64, dtype=bf)
+    o, lse = torch.zeros(2, 6, 40, 64), torch.zeros(2, 6, 40)
+    dq, dk = torch.zeros(2, 6, 40, 64), torch.zeros(2, 2, 40, 64)
+    ws = torch.zeros(16, dtype=torch.uint8)
+    cases = [
+        (lambda: tca.attn_fwd(q, k[:, :, :39], k), "k has shape"),
+        (lambda: tca.attn_fwd(q, k, k[:, :, :39]), "v has shape"),
+        (lambda: tca.attn_fwd(q, k[:1], k[:1]), "k has shape"),
+        (lambda: tca.attn_fwd(q, k[..., :32], k[..., :32]), "k has shape"),
+        (lambda: tca.attn_fwd(q, k, k, out=(o[:, :, :39], lse)), "o has shape"),
+        (lambda: tca.attn_fwd(q, k, k, out=(o, lse[:1])), "lse has shape"),
+        (lambda: tca.attn_bwd(q, k, k, o, lse, q[:, :, :20], workspace=ws), "dO has shape"),
+        (lambda: tca.attn_bwd(q, k, k, o[:1], lse, q, workspace=ws), "o has shape"),
+        (lambda: tca.attn_bwd(q, k, k, o, lse, q, out=(dq[:, :3], dk, dk), workspace=ws), "dq has shape"),
+        (lambda: tca.attn_bwd(q, k, k, o, lse, q, out=(dq, dk[:, :1], dk), workspace=ws), "dk has shape"),
+        (lambda: tca.attn_bwd(q, k, k, o, lse, q, out=(dq, dk, dk[:, :, :8]), workspace=ws), "dv has shape"),
+        (lambda: tca.attn_decode(q[:, :, :1], k, k[:, :, :20]), "v has shape"),
+        (lambda: tca.attn_decode(q[:, :, :1], k, k, out=(o[:, :, :2], lse[:, :, :1])), "o has shape"),
+        (lambda: tca.attn_fwd_naive(q, k, k[:, :1]), "v has shape"),
+        (lambda: tca.attn_fwd_rope(q, k, k[:, :, :5]), "v has shape"),
+        (lambda: tca.attn_bwd_rope(q, k, k, o, lse, q, out=(dq, dk, dk[:1]), workspace=ws), "dv has shape"),
+    ]
+    for fn, msg in cases:
+        with pytest.raises(ValueError, match=msg):
+            fn()
+    with pytest.raises(TypeError, match="k is"):
+        tca.attn_fwd(q, k.float(), k.float())
+    with pytest.raises(TypeError, match="dO is"):
+        tca.attn_bwd(q, k, k, o, lse, q.float(), workspace=ws)
+    with pytest.raises(TypeError, match="dq, dk, dv"):
+        tca.attn_bwd(q, k, k, o, lse, q, out=(dq.bfloat16(), dk, dk), workspace=ws)
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 8, 16)

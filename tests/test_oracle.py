@@ -335,6 +335,34 @@ def test_headline_shape_slice_vs_sdpa():
     assert np.allclose(lse, _torch_lse(q, k, 1, s.scale).numpy(), atol=1e-12, rtol=0)
 
 
+def _torch_explicit(q, k, v, causal, scale):
+    # softmax(scale Q K^T, masked keys at -inf after scaling) V, built from plain torch ops
+    # (torch's fused causal attention masks before it scales, which a negative scale breaks)
+    g = q.shape[1] // k.shape[1]
+    kr, vr = k.repeat_interleave(g, dim=1), v.repeat_interleave(g, dim=1)
+    s = scale * torch.matmul(q, kr.transpose(-1, -2).contiguous())
+    if causal:
+        N = q.shape[2]
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    return torch.matmul(torch.softmax(s, dim=-1), vr), torch.logsumexp(s, dim=-1)
+
+
+@pytest.mark.parametrize("causal", [1, 0])
+def test_negative_scale_vs_explicit_softmax(causal):
+    # a negative scale flips which keys dominate; the definition holds for any finite scale
+    for (B, Hq, Hkv, N, d), scale in (((2, 6, 2, 40, 12), -0.7), ((1, 4, 1, 33, 5), -2.0)):
+        q, k, v, do = _inputs(B, Hq, Hkv, N, d, seed=N + 11)
+        o, lse = oracle.attn_fwd(q, k, v, causal, scale)
+        qq, kk, vv = (t.clone().requires_grad_(True) for t in (q, k, v))
+        ro, rl = _torch_explicit(qq, kk, vv, causal, scale)
+        assert np.allclose(o, ro.detach().numpy(), atol=1e-10, rtol=0)
+        assert np.allclose(lse, rl.detach().numpy(), atol=1e-10, rtol=0)
+        ro.backward(do)
+        dq, dk, dv = oracle.attn_bwd(q, k, v, do, causal, scale)
+        for a, t in zip((dq, dk, dv), (qq, kk, vv)):
+            assert np.allclose(a, t.grad.numpy(), atol=1e-10, rtol=0)
+
+
 # ---------------------------------------------------------------- finite differences
 def _fd_grads(q, k, v, G, causal, scale, eps=1e-5):
     """Central differences of L = sum(O * G) with respect to every input element."""

@@ -128,6 +128,62 @@ def _dims(q: torch.Tensor, k: torch.Tensor):
     return B, Hq, k.shape[1], N, d
 
 
+# Every tensor is checked against q's and k's sizes before a pointer reaches the
+# C ABI: the kernels size their buffer walks from (B, Hq, Hkv, N, d) alone, so a
+# short tensor would otherwise be read or written past its end.
+def _expect(t: torch.Tensor, name: str, shape, dtypes=None):
+    if t is None:
+        raise ValueError(f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} is {t.dtype}, expected one of {tuple(dtypes)}")
+
+
+def _same_device(ref: torch.Tensor, **named):
+    for name, t in named.items():
+        if t is not None and t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, q on {ref.device}: all tensors must share one device")
+
+
+_IN_DTYPES = (torch.float32, torch.bfloat16)
+
+
+def _check_qkv(q, k, v, kv_rows=None):
+    """(B, Hq, Hkv, Nq, d) after checking that k and v are [B, Hkv, Nk, d] with q's
+    dtype (Nk = kv_rows, or q's N when None)."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    _expect(q, "q", q.shape, _IN_DTYPES)
+    Nk = N if kv_rows is None else kv_rows
+    _expect(k, "k", (B, k.shape[1], Nk, d), (q.dtype,))
+    _expect(v, "v", k.shape, (q.dtype,))
+    _same_device(q, k=k, v=v)
+    return B, Hq, k.shape[1], N, d
+
+
+def _check_outputs(q, o, lse, B, Hq, N, d):
+    _expect(o, "o", (B, Hq, N, d), _IN_DTYPES)
+    _expect(lse, "lse", (B, Hq, N), (torch.float32,))
+    _same_device(q, o=o, lse=lse)
+
+
+def _check_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws):
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    _check_outputs(q, o, lse, B, Hq, N, d)
+    _expect(dO, "dO", q.shape, (q.dtype,))
+    _expect(dq, "dq", q.shape, (o.dtype,))
+    _expect(dk, "dk", k.shape, (o.dtype,))
+    _expect(dv, "dv", k.shape, (o.dtype,))
+    _same_device(q, dO=dO, dq=dq, dk=dk, dv=dv, workspace=ws)
+    return B, Hq, Hkv, N, d
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
@@ -137,7 +193,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
              out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward: returns (o [B,Hq,N,d] in out_dtype (float32 unless given, or
     the dtype of out[0]), lse float32 [B,Hq,N])."""
-    B, Hq, Hkv, N, d = _dims(q, k)
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     if out is None:
@@ -149,6 +205,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = T
             raise TypeError(f"out[0] is {o.dtype}, out_dtype is {out_dtype}")
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
+    _check_outputs(q, o, lse, B, Hq, N, d)
     L = lib()
     ws_bytes = L.attn_fwd_workspace_bytes(dt, B, Hq, Hkv, N, d)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
@@ -164,15 +221,15 @@ def bwd_workspace(q: torch.Tensor, k: torch.Tensor) -> torch.Tensor:
 
 
 def _bwd_call(name, q, k, v, o, lse, dO, dq, dk, dv, ws, causal, scale):
-    B, Hq, Hkv, N, d = _dims(q, k)
-    scale = default_scale(d) if scale is None else float(scale)
     for t in (dq, dk, dv):
-        if t.dtype != o.dtype:
+        if t is not None and o is not None and t.dtype != o.dtype:
             raise TypeError(f"dq, dk, dv must have o's dtype {o.dtype}, got {t.dtype}")
-    if lse.dtype != torch.float32:
+    if lse is not None and lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
+    B, Hq, Hkv, N, d = _check_bwd(q, k, v, o, lse, dO, dq, dk, dv, ws)
+    scale = default_scale(d) if scale is None else float(scale)
     _check(getattr(lib(), name)(_dtype_code(q), _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                                _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), _nbytes(ws),
                                 B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
 
 
@@ -207,10 +264,10 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     """Few-query attention over a cache: q [B,Hq,Nq,d] are the last Nq positions of
     the sequence whose keys/values k, v [B,Hkv,Nk,d] hold. Returns (o [B,Hq,Nq,d]
     in out_dtype (float32 unless given, or out[0]'s dtype), lse float32 [B,Hq,Nq])."""
-    if q.dim() != 4 or k.dim() != 4 or v.shape != k.shape:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]")
-    B, Hq, Nq, d = q.shape
-    Hkv, Nk = k.shape[1], k.shape[2]
+    B, Hq, Hkv, Nq, d = _check_qkv(q, k, v, kv_rows=k.shape[2])
+    Nk = k.shape[2]
     scale = default_scale(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     if out is None:
@@ -222,11 +279,13 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
             raise TypeError(f"out[0] is {o.dtype}, out_dtype is {out_dtype}")
     if lse.dtype != torch.float32:
         raise TypeError("lse must be float32")
+    _check_outputs(q, o, lse, B, Hq, Nq, d)
     L = lib()
     ws_bytes = int(L.attn_decode_workspace_bytes(dt, B, Hq, Hkv, Nq, Nk, d))
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    wsn = workspace.numel() if workspace is not None else 0
+    _same_device(q, workspace=workspace)
+    wsn = _nbytes(workspace)
     _check(L.attn_decode(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                          _ptr(workspace), wsn, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
                          _stream(q.device)))
@@ -239,19 +298,21 @@ def attn_fwd_naive(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bo
                    ) -> Tuple[torch.Tensor, torch.Tensor]:
     """Unoptimised forward through the materialised score matrix (B*Hq*N*N floats
     of workspace): same results as attn_fwd, for teaching and comparison."""
-    B, Hq, Hkv, N, d = _dims(q, k)
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
     if out is None:
         o = torch.empty((B, Hq, N, d), dtype=out_dtype or torch.float32, device=q.device)
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+    _check_outputs(q, o, lse, B, Hq, N, d)
     L = lib()
     ws_bytes = int(L.attn_fwd_naive_workspace_bytes(B, Hq, N))
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=q.device)
+    _same_device(q, workspace=workspace)
     _check(L.attn_fwd_naive(_dtype_code(q), _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                            _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d, int(bool(causal)), scale,
+                            _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, d, int(bool(causal)), scale,
                             _stream(q.device)))
     return o, lse
 
@@ -283,8 +344,7 @@ def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optio
     """Forward with rotary position embedding of q and k (rotate-half pairing; cos,
     sin: [N, d/2] float32 tables, or both None) on [B, H, N, d] views with any
     strides (e.g. slices of one fused QKV projection). Returns (o, lse) like attn_fwd."""
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    B, Hq, Hkv, N, d = _check_qkv(q, k, v)
     scale = default_scale(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     if out is None:
@@ -292,14 +352,16 @@ def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optio
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
+    _check_outputs(q, o, lse, B, Hq, N, d)
     L = lib()
     cs, sn = _tables(cos, sin, N, d)
     n = int(L.attn_fwd_rope_workspace_bytes(dt, _code(o.dtype), B, Hq, Hkv, N, d))
     if workspace is None:
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+    _same_device(q, workspace=workspace)
     ql, kl, vl = _layout(q), _layout(k), _layout(v)
     _check(L.attn_fwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ql), _sptr(k), ctypes.byref(kl), _sptr(v),
-                           ctypes.byref(vl), cs, sn, _ptr(o), _ptr(lse), _ptr(workspace), workspace.numel(),
+                           ctypes.byref(vl), cs, sn, _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
                            B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
     return o, lse
 
@@ -308,9 +370,8 @@ def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, 
                   out=None, workspace: Optional[torch.Tensor] = None):
     """Backward of attn_fwd_rope: gradients of the unrotated q, k and of v, in o's
     dtype, written into `out` = (dq, dk, dv) views (any strides) or new contiguous tensors."""
-    B, Hq, N, d = q.shape
-    Hkv = k.shape[1]
-    scale = default_scale(d) if scale is None else float(scale)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
+        raise ValueError("q, k, v, o must be 4-D [B, H, N, d]")
     dt = _dtype_code(q)
     if out is None:
         dq = torch.empty(q.shape, dtype=o.dtype, device=q.device)
@@ -321,6 +382,8 @@ def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, 
     for t in (dq, dk, dv):
         if t.dtype != o.dtype:
             raise TypeError("dq, dk, dv must have o's dtype")
+    B, Hq, Hkv, N, d = _check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace)
+    scale = default_scale(d) if scale is None else float(scale)
     L = lib()
     cs, sn = _tables(cos, sin, N, d)
     n = int(L.attn_bwd_rope_workspace_bytes(dt, _code(o.dtype), B, Hq, Hkv, N, d))
@@ -330,7 +393,7 @@ def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, 
     _check(L.attn_bwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ls[0]), _sptr(k), ctypes.byref(ls[1]),
                            _sptr(v), ctypes.byref(ls[2]), cs, sn, _ptr(o), _ptr(lse), _ptr(dO),
                            _sptr(dq), ctypes.byref(ls[3]), _sptr(dk), ctypes.byref(ls[4]), _sptr(dv),
-                           ctypes.byref(ls[5]), _ptr(workspace), workspace.numel(), B, Hq, Hkv, N, d,
+                           ctypes.byref(ls[5]), _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, d,
                            int(bool(causal)), scale, _stream(q.device)))
     return dq, dk, dv
 

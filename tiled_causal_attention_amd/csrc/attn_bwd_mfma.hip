@@ -117,7 +117,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
               const OT* __restrict__ o, const float* __restrict__ lse,
               const bf16_t* __restrict__ dout, float* __restrict__ delta, float* __restrict__ l2,
               _Float16* __restrict__ q16, _Float16* __restrict__ do16, OT* __restrict__ dq,
-              int Hq, int Hkv, int N, int causal, float scale, int nqt, int units, QRope rq) {
+              int Hq, int Hkv, int N, int causal, float scale, ScoreScale sc, int nqt, int units, QRope rq) {
     using namespace bwdq;
     constexpr int DC = D / 16, DB = D / 32, LD = D + kPad<D>;
     constexpr int NKH = kKeyHalves<D>;   // key parts per tile (one wave each)
@@ -147,7 +147,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const bool qok = qi < N;
     const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
-    const float sl2 = scale * kLog2e;
+    const float sl2 = sc.sl2;   // positive multiplier of Q' K^T (scale is dQ's factor)
     __shared__ float dsh[NKH == 2 ? BQ : 1];   // D of each row, from key half 0
 
     // The first K/V tile's loads and this row's LSE go out before the Q, dO and O
@@ -181,7 +181,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         if constexpr (ROPE) rope_rotate_q<D>(qraw, qtab);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-            const u32x4 qh16 = bf16x8_to_f16x8(qraw[c]);
+            const u32x4 qh16 = bf16x8_to_f16x8(apply_qsign(qraw[c], sc));
             qb[c] = qok ? __builtin_bit_cast(f16x8, qh16) : f16x8{};
             db[c] = qok ? __builtin_bit_cast(bf16x8, dvr[c]) : bf16x8{};
         }
@@ -382,7 +382,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
                 const float* __restrict__ l2, const float* __restrict__ delta,
                 OT* __restrict__ dk, OT* __restrict__ dv,
-                int Hq, int Hkv, int N, int causal, float scale, int ntiles, int wg_per_unit) {
+                int Hq, int Hkv, int N, int causal, ScoreScale sc, int ntiles, int wg_per_unit) {
     using namespace bwdkv;
     constexpr int NQW = Cfg<D>::NQW;
     constexpr int NW = 2 * NQW;               // waves
@@ -426,7 +426,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, scalar
     const int kh_ = w & 1, qw = w >> 1;       // key half, query sub-block
     const size_t kvoff = ((size_t)b * Hkv + hkv) * N * D;
-    const float sl2 = scale * kLog2e;
+    const float sl2 = sc.sl2;         // positive multiplier of Q' K^T (Q' is the stored copy)
+    const float scale = sc.kscale;    // dK = s' dS^T Q'
     const int nqt = (N + BQ - 1) / BQ;
 
     // K/V tiles of this workgroup: causal -> {slot, ntiles-1-slot} (one if they coincide)
@@ -759,7 +760,7 @@ static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, OT, ROPE>), dim3((unsigned)(nqt * a.B * a.Hq)), dim3(bwdq::kThreads<D>), 0, st,
                        (const bf16_t*)a.q, (const bf16_t*)a.k, (const bf16_t*)a.v, (const OT*)a.o,
                        (const float*)a.lse, (const bf16_t*)a.dout, ws.delta, ws.l2, ws.q16, ws.do16, (OT*)a.dq,
-                       a.Hq, a.Hkv, a.N, a.causal, a.scale, nqt, units, rq);
+                       a.Hq, a.Hkv, a.N, a.causal, a.scale, score_scale(a.scale), nqt, units, rq);
     return hipGetLastError();
 }
 
@@ -771,7 +772,7 @@ static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
                        (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, (OT*)a.dk,
-                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, a.scale, ntiles, per_unit);
+                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, score_scale(a.scale), ntiles, per_unit);
     return hipGetLastError();
 }
 

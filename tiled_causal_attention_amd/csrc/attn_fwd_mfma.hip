@@ -105,7 +105,7 @@ template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 const bf16_t* __restrict__ v, OT* __restrict__ o, float* __restrict__ lse,
-                int Hq, int Hkv, int N, int causal, float scale, int nqt, int units, QRope rq) {
+                int Hq, int Hkv, int N, int causal, ScoreScale sc, int nqt, int units, QRope rq) {
     using namespace fwd;
     constexpr int DC = D / 16;          // 16-deep chunks of the head dimension
     constexpr int DB = D / 32;          // 32-wide blocks of the head dimension
@@ -135,7 +135,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const int q0w = tm.qt * BR + 32 * rb;  // first query row of this wave
     const int qi = q0w + r;                // this lane's query row
     const bf16_t* qh = q + bh * N * D;
-    const float sl2 = scale * kLog2e;      // scores in log2 units
+    const float sl2 = sc.sl2;              // scores in log2 units (positive multiplier)
 
     // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]. With ROPE
     // the row's table values are loaded next to it and the rotation waits until the
@@ -153,7 +153,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
         } else {
 #pragma unroll
-            for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
+            for (int c = 0; c < DC; ++c)
+                qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
         }
     }
 
@@ -192,7 +193,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     if constexpr (ROPE) {
         rope_rotate_q<D>(qraw, qtab);
 #pragma unroll
-        for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, qraw[c]) : bf16x8{};
+        for (int c = 0; c < DC; ++c)
+            qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
     }
 
     for (int j = 0; j < ntile; ++j) {
@@ -342,7 +344,7 @@ static hipError_t launch_fwd_d(const AttnArgs& a, hipStream_t st) {
     const QRope rq = ROPE ? *a.rope : QRope{};
     hipLaunchKernelGGL((fwd_mfma_kernel<D, OT, ROPE>), grid, dim3(fwd::kThreads<D>), 0, st, (const bf16_t*)a.q,
                        (const bf16_t*)a.k, (const bf16_t*)a.v, (OT*)a.o, a.lse, a.Hq, a.Hkv, a.N, a.causal,
-                       a.scale, nqt, units, rq);
+                       score_scale(a.scale), nqt, units, rq);
     return hipGetLastError();
 }
 

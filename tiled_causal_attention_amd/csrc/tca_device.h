@@ -268,6 +268,31 @@ __device__ __forceinline__ void load8_f32(const bf16_t* p, float (&x)[8]) {
     x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
 }
 
+// Scores for the matrix-core kernels, for any finite scale. They form
+// s' (Q' K^T) with Q' = sgn(scale) Q and s' = |scale| (1 when scale is 0), which
+// equals scale (Q K^T) exactly (a sign flip or a zero is exact in any format). The
+// exponent's multiplier s' log2(e) is then always positive, so a key masked with
+// -inf before the multiply stays -inf and the running max of the raw products is
+// the max of the scaled ones. Gradients: dQ = scale dS K (the true scale),
+// dK = s' dS^T Q' (the stored Q' copy carries the sign). Scale 0 zeroes Q', so every
+// visible key gets the same weight and dK is zero.
+struct ScoreScale {
+    float sl2;        // s' log2(e)
+    float kscale;     // s', the dK multiplier against Q'
+    uint32_t qand;    // Q' bits = (Q bits & qand) ^ qxor on each 32-bit pair of 16-bit values
+    uint32_t qxor;    // (bf16 and fp16 keep the sign in bit 15 of each half)
+};
+inline ScoreScale score_scale(float scale) {
+    ScoreScale s;
+    const float sp = (scale == 0.f) ? 1.f : fabsf(scale);
+    s.sl2 = sp * kLog2e;
+    s.kscale = sp;
+    s.qand = (scale == 0.f) ? 0u : 0xffffffffu;
+    s.qxor = (scale < 0.f) ? 0x80008000u : 0u;
+    return s;
+}
+__device__ __forceinline__ u32x4 apply_qsign(u32x4 x, const ScoreScale& s) { return (x & s.qand) ^ s.qxor; }
+
 // Rotary embedding of the query side, for kernels that rotate Q in registers
 // (rotate-half pairing: dims i and i + D/2, cos/sin = table[n][i] at row n) and,
 // in the dQ pass, turn dQ back by the transpose rotation at the store. Q and dQ
