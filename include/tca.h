@@ -90,11 +90,12 @@ typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_EINVAL = 1,        /* invalid argument: null or misaligned pointer, bad size, bad flag */
     ATTN_EUNSUPPORTED = 2,  /* valid but not supported (head dimension) */
-    ATTN_EHIP = 3           /* the HIP runtime reported an error while enqueueing */
+    ATTN_EHIP = 3,          /* the HIP runtime reported an error while enqueueing */
+    ATTN_ESCRATCH = 4       /* attn_decode_noalloc: the call needs more than its fixed scratch array */
 } attn_status;
 
-/* Version of this interface; bumped on any incompatible change (2: the
- * out_dtype argument). */
+/* Version of this interface; bumped on any change (2: the out_dtype argument;
+ * 3: attn_decode_noalloc and ATTN_ESCRATCH). */
 int attn_abi_version(void);
 
 /* Static, human-readable name of a status code (never NULL). */
@@ -275,6 +276,26 @@ attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype,
                         void* workspace, size_t workspace_bytes,
                         int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                         void* stream);
+
+/* Bytes of the fixed device array that attn_decode_noalloc uses as scratch. */
+#define ATTN_DECODE_SCRATCH_BYTES (16u << 20)
+
+/* attn_decode without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation). Arguments, results and errors are attn_decode's; the results
+ * are bitwise those of attn_decode. The split partials go to a file-scope device
+ * array of ATTN_DECODE_SCRATCH_BYTES bytes that each GPU the library runs on holds
+ * until the process ends (its address is looked up on the first call on a device,
+ * with that device current; `stream` must belong to the current device). A call
+ * whose attn_decode_workspace_bytes(...) exceeds ATTN_DECODE_SCRATCH_BYTES returns
+ * ATTN_ESCRATCH and enqueues nothing. The call itself allocates nothing. Every call
+ * on one GPU shares that GPU's array: calls that may overlap on one GPU (different
+ * streams, or host threads) race and must be serialised by the caller. */
+attn_status attn_decode_noalloc(attn_dtype dtype, attn_dtype out_dtype,
+                                const void* q, const void* k, const void* v,
+                                void* o, float* lse,
+                                int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                void* stream);
 
 #ifdef __cplusplus
 }

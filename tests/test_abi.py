@@ -41,7 +41,7 @@ def test_header_declares_the_boundary():
                      "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_workspace_bytes",
                      "attn_abi_version", "attn_decode", "attn_decode_workspace_bytes",
                      "attn_fwd_naive", "attn_fwd_naive_workspace_bytes", "attn_fwd_rope", "attn_bwd_rope",
-                     "attn_fwd_rope_workspace_bytes", "attn_bwd_rope_workspace_bytes"):
+                     "attn_fwd_rope_workspace_bytes", "attn_bwd_rope_workspace_bytes", "attn_decode_noalloc"):
         assert required in names
 
 
@@ -57,8 +57,8 @@ def test_exports_are_c_symbols():
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 2
-    for s in (OK, EINVAL, EUNSUP, tca.ATTN_EHIP):
+    assert L.attn_abi_version() == 3
+    for s in (OK, EINVAL, EUNSUP, tca.ATTN_EHIP, tca.ATTN_ESCRATCH):
         assert L.attn_status_str(s)
     assert b"unknown" in L.attn_status_str(99)
 
@@ -267,6 +267,27 @@ def dec(L, dtype=BF16, out_dtype=F32, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=64, causa
 ])
 def test_decode_rejects(L, kw, want):
     assert dec(L, **kw) == want
+
+
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode checks its arguments like attn_decode and refuses,
+    before any HIP call, sizes whose split partials exceed its fixed array."""
+    def nd(dtype=BF16, out_dtype=F32, B=2, Hq=4, Hkv=2, Nq=1, Nk=64, d=64, causal=1, scale=0.125,
+           q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE):
+        return L.attn_decode_noalloc(dtype, out_dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                                     None)
+    assert nd(dtype=4) == EINVAL and nd(Nq=65) == EINVAL and nd(Hq=6, Hkv=4) == EINVAL
+    assert nd(causal=2) == EINVAL and nd(scale=float("inf")) == EINVAL and nd(d=80) == EUNSUP
+    assert nd(q=None) == EINVAL and nd(k=FAKE + 8) == EINVAL
+    nul = dict(q=None, k=None, v=None, o=None, lse=None)
+    assert nd(B=0, **nul) == OK and nd(Nq=0, **nul) == OK
+    big = dict(B=1, Hq=16, Hkv=2, Nq=8, Nk=16384, d=128)
+    need = L.attn_decode_workspace_bytes(BF16, *big.values())
+    assert need > tca.DECODE_SCRATCH_BYTES
+    assert nd(**big) == tca.ATTN_ESCRATCH
+    assert b"ESCRATCH" in L.attn_status_str(tca.ATTN_ESCRATCH)
+    header = open(HEADER).read()
+    assert re.search(r"#define ATTN_DECODE_SCRATCH_BYTES \(16u << 20\)", header)
 
 
 def test_decode_noops_and_workspace(L):

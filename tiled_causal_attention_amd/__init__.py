@@ -25,7 +25,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtca.so")
 
 ATTN_F32, ATTN_BF16 = 0, 1
-ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ESCRATCH = 0, 1, 2, 3, 4
+DECODE_SCRATCH_BYTES = 16 << 20   # the fixed array behind attn_decode_noalloc (ATTN_DECODE_SCRATCH_BYTES)
 
 _lib = None
 
@@ -82,6 +83,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [i, i, vp, vp, vp, vp, fp, vp, sz, i, i, i, i, i, i, i, f, vp]
     L.attn_decode.restype = i
+    L.attn_decode_noalloc.argtypes = [i, i, vp, vp, vp, vp, fp, i, i, i, i, i, i, i, f, vp]
+    L.attn_decode_noalloc.restype = i
     _lib = L
     return L
 
@@ -289,6 +292,32 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     _check(L.attn_decode(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                          _ptr(workspace), wsn, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
                          _stream(q.device)))
+    return o, lse
+
+
+def attn_decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
+                        scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
+                        out_dtype: Optional[torch.dtype] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """attn_decode without a workspace: the library's fixed device array holds the
+    split partials (calls that overlap on one GPU race on it). With `out` given the
+    call allocates nothing. Raises AttnError (ATTN_ESCRATCH) when the sizes need more
+    than DECODE_SCRATCH_BYTES of partials."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q [B,Hq,Nq,d], k and v [B,Hkv,Nk,d]")
+    B, Hq, Hkv, Nq, d = _check_qkv(q, k, v, kv_rows=k.shape[2])
+    Nk = k.shape[2]
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=out_dtype or torch.float32, device=q.device)
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        if out_dtype is not None and o.dtype != out_dtype:
+            raise TypeError(f"out[0] is {o.dtype}, out_dtype is {out_dtype}")
+    _check_outputs(q, o, lse, B, Hq, Nq, d)
+    _check(lib().attn_decode_noalloc(_dtype_code(q), _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(lse), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+                                     _stream(q.device)))
     return o, lse
 
 

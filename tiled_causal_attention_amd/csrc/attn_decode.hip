@@ -30,6 +30,7 @@
 //  * kUnroll keys per slot are loaded ahead of their math (128 bytes per lane
 //    in flight for bf16), enough outstanding loads to cover HBM latency at
 //    2-4 waves per SIMD.
+#include <mutex>
 #include <type_traits>
 
 #include "tca_internal.h"
@@ -438,6 +439,36 @@ static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipS
         case 128: return launch_decode_rm<T, OT, 128>(a, p, st);
         default: return hipErrorInvalidValue;
     }
+}
+
+// ---------------------------------------------------------------- fixed scratch
+// The split partials of attn_decode_noalloc live in this file-scope device array
+// instead of a caller workspace, for callers that cannot allocate. Each GPU holds
+// its own copy, at its own address, until the process ends. In host code the
+// array's name is only a host-side stand-in: kernels and copies get the device
+// address that hipGetSymbolAddress returns, taken once per device with that
+// device current, kept below and used everywhere instead of the name. Nothing in
+// it needs clearing: every partial the merge reads is written by the split
+// kernel of the same call. Calls that overlap on one GPU share it and race.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* ptrs[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ptrs[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {

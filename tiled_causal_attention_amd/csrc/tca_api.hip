@@ -10,7 +10,7 @@ using tca::AttnArgs;
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -205,7 +205,51 @@ attn_status run_dkdv(const AttnArgs& a, hipStream_t st) {
     return from_hip(tca::mfma_path(a) ? tca::launch_bwd_mfma_dkdv(a, st) : tca::launch_bwd_generic_dkdv(a, st));
 }
 
+// Size, flag and pointer checks of the decode entry points (not the workspace)
+attn_status check_decode(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                         void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+                         float scale, bool* noop) {
+    *noop = false;
+    if (!known_dtype(dtype) || !known_dtype(out_dtype)) return ATTN_EINVAL;
+    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_EINVAL;
+    if (Hq % Hkv != 0 || Nq > Nk) return ATTN_EINVAL;
+    if (causal != 0 && causal != 1) return ATTN_EINVAL;
+    if (!isfinite(scale)) return ATTN_EINVAL;
+    if ((int64_t)(Nk + 256) * d * 4 >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // byte offsets in a head's K/V
+    if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;
+    if ((int64_t)B * Hkv * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // work items
+    if (!supported_d(d)) return ATTN_EUNSUPPORTED;
+    if ((int64_t)B * Nq == 0) {
+        *noop = true;
+        return ATTN_OK;
+    }
+    return check_ptrs({q, k, v, o, lse});
+}
+
+tca::DecodeArgs decode_args(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
+                            void* o, float* lse, void* workspace, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                            int causal, float scale) {
+    tca::DecodeArgs a;
+    a.dtype = dtype;
+    a.out_dtype = out_dtype;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.workspace = workspace;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Nq = Nq;
+    a.Nk = Nk;
+    a.d = d;
+    a.causal = causal;
+    a.scale = scale;
+    return a;
+}
 }  // namespace
+
 
 extern "C" {
 
@@ -217,6 +261,8 @@ const char* attn_status_str(attn_status s) {
         case ATTN_EINVAL: return "ATTN_EINVAL: invalid argument";
         case ATTN_EUNSUPPORTED: return "ATTN_EUNSUPPORTED: unsupported head dimension";
         case ATTN_EHIP: return "ATTN_EHIP: HIP runtime error while enqueueing";
+        case ATTN_ESCRATCH:
+            return "ATTN_ESCRATCH: the decode needs more split-partial memory than the fixed scratch array holds";
         default: return "unknown attn_status";
     }
 }
@@ -432,37 +478,27 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
 attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
                         void* o, float* lse, void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv,
                         int Nq, int Nk, int d, int causal, float scale, void* stream) {
-    if (!known_dtype(dtype) || !known_dtype(out_dtype)) return ATTN_EINVAL;
-    if (B < 0 || Nq < 0 || Nk < 0 || Hq < 1 || Hkv < 1 || d < 1) return ATTN_EINVAL;
-    if (Hq % Hkv != 0 || Nq > Nk) return ATTN_EINVAL;
-    if (causal != 0 && causal != 1) return ATTN_EINVAL;
-    if (!isfinite(scale)) return ATTN_EINVAL;
-    if ((int64_t)(Nk + 256) * d * 4 >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // byte offsets in a head's K/V
-    if ((int64_t)B * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;
-    if ((int64_t)B * Hkv * Hq * Nq >= ((int64_t)1 << 31)) return ATTN_EINVAL;   // work items
-    if (!supported_d(d)) return ATTN_EUNSUPPORTED;
-    if ((int64_t)B * Nq == 0) return ATTN_OK;
-    attn_status s = check_ptrs({q, k, v, o, lse});
-    if (s != ATTN_OK) return s;
+    bool noop = false;
+    attn_status s = check_decode(dtype, out_dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, &noop);
+    if (s != ATTN_OK || noop) return s;
     const size_t need = tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
     if (need > 0 && (workspace_bytes < need || workspace == nullptr || !aligned16(workspace))) return ATTN_EINVAL;
-    tca::DecodeArgs a;
-    a.dtype = dtype;
-    a.out_dtype = out_dtype;
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.o = o;
-    a.lse = lse;
-    a.workspace = workspace;
-    a.B = B;
-    a.Hq = Hq;
-    a.Hkv = Hkv;
-    a.Nq = Nq;
-    a.Nk = Nk;
-    a.d = d;
-    a.causal = causal;
-    a.scale = scale;
+    const tca::DecodeArgs a =
+        decode_args(dtype, out_dtype, q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal, scale);
+    return from_hip(tca::launch_decode(a, (hipStream_t)stream));
+}
+
+attn_status attn_decode_noalloc(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k,
+                                const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                                int causal, float scale, void* stream) {
+    bool noop = false;
+    attn_status s = check_decode(dtype, out_dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, &noop);
+    if (s != ATTN_OK || noop) return s;
+    const size_t need = tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+    if (need > tca::kDecodeScratchBytes) return ATTN_ESCRATCH;
+    void* ws = nullptr;
+    if (need > 0 && tca::decode_scratch(&ws) != hipSuccess) return ATTN_EHIP;
+    const tca::DecodeArgs a = decode_args(dtype, out_dtype, q, k, v, o, lse, ws, B, Hq, Hkv, Nq, Nk, d, causal, scale);
     return from_hip(tca::launch_decode(a, (hipStream_t)stream));
 }
 

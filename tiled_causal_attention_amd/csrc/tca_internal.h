@@ -98,6 +98,10 @@ struct DecodePlan {
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+// Size of the fixed device array behind attn_decode_noalloc, and its address on
+// the current device (looked up on the first call per device, then cached).
+constexpr size_t kDecodeScratchBytes = (size_t)ATTN_DECODE_SCRATCH_BYTES;
+hipError_t decode_scratch(void** out);
 
 // Strided copies of [B, H, N, d] tensors (head dimension contiguous) with an
 // optional rotary rotation of the (i, i + d/2) pairs at each row's position:
