@@ -79,6 +79,9 @@ def parse():
                    help="one JSON line: the forward of the workload, tiled against the naive materialised-score one")
     p.add_argument("--decode", action="store_true",
                    help="one JSON line per decode workload (few queries over a K/V cache) instead")
+    p.add_argument("--ceiling", action="store_true",
+                   help="one JSON line per instruction mix: the per-block mixes of the three kernels "
+                        "run register/LDS-only at 1-4 waves per SIMD (what the mix itself can reach)")
     p.add_argument("--out-dtype", default="f32", choices=["f32", "bf16"],
                    help="element type of o, dq, dk, dv (lse is always float32)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -209,6 +212,73 @@ def measured_mfma_peak():
     e1.record()
     torch.cuda.synchronize()
     return L.tca_mfma_peak_flops(blocks, iters) / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e12
+
+
+MIX_NAMES = ["mfma_only", "exp_only", "fma_only", "cvt_only", "fwd", "fwd_reg", "fwd_staged", "dq", "dkdv",
+             "fwd_w8", "fwd_pingpong", "fwd_2q"]
+MIX_VALU_PER_BLOCK = {"exp_only": 16, "fma_only": 16, "cvt_only": 8}
+
+
+def ceiling_report(args):
+    """Per instruction mix and waves per SIMD: SIMD cycles per 32x32 block (each wave loops
+    over one block per iteration, no global memory traffic), the matrix-core busy fraction
+    that implies (32 cycles per 32x32x16 product), and the rate the mix would sustain at the
+    measured shader clock, in its own products' TFLOP/s."""
+    import ctypes
+
+    import numpy as np
+    from tiled_causal_attention_amd import build as tca_build
+    L = ctypes.CDLL(tca_build.MEASURE_LIB)
+    L.tca_mix_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.tca_mix_launch.restype = ctypes.c_int
+    L.tca_mix_mfma_per_block.argtypes = [ctypes.c_int]
+    L.tca_mix_mfma_per_block.restype = ctypes.c_int
+    L.tca_mix_max_blocks_per_cu.argtypes = [ctypes.c_int]
+    L.tca_mix_max_blocks_per_cu.restype = ctypes.c_int
+    L.tca_mix_waves_per_block.argtypes = [ctypes.c_int]
+    L.tca_mix_waves_per_block.restype = ctypes.c_int
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    iters = 4096
+    peak = measured_mfma_peak()
+    for mid, name in enumerate(MIX_NAMES):
+        fit = L.tca_mix_max_blocks_per_cu(mid)
+        wpb = L.tca_mix_waves_per_block(mid)
+        for w in (1, 2, 3, 4):
+            if w * wpb // 4 > 4 or w > fit:
+                continue
+            blocks = n_cu * w
+            out = torch.empty(blocks * 512, dtype=torch.float32, device="cuda")
+            cyc = torch.zeros(blocks * 16, dtype=torch.int64, device="cuda")
+            for _ in range(2):
+                rc = L.tca_mix_launch(mid, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cyc.data_ptr()),
+                                      blocks, iters, st)
+                if rc != 0:
+                    raise RuntimeError(f"mix {name} launch failed: {rc}")
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            L.tca_mix_launch(mid, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cyc.data_ptr()), blocks, iters, st)
+            e1.record()
+            torch.cuda.synchronize()
+            wall_s = e0.elapsed_time(e1) * 1e-3
+            c = cyc.cpu().numpy().astype(np.float64).reshape(blocks, 8, 2)[:, :wpb].reshape(-1, 2)
+            wps = w * wpb // 4                                 # waves per SIMD
+            ns_wave = float(np.median(c[:, 1])) * 10.0 / iters  # 100 MHz counter: ns per block, per wave
+            ns_simd = ns_wave / wps                            # per SIMD (wps waves share it)
+            tick_ghz = float(np.median(c[:, 0] / c[:, 1])) * 0.1   # s_memtime rate
+            nm = L.tca_mix_mfma_per_block(mid)
+            row = {"mix": name, "waves_per_simd": wps, "ns_per_block_per_simd": round(ns_simd, 2),
+                   "memtime_ghz": round(tick_ghz, 3), "wall_us": round(wall_s * 1e6, 1), "mfma_per_block": nm}
+            if nm > 0:
+                # every SIMD of the chip at this rate (the steady state of one resident set)
+                flops = 4 * n_cu * nm * 32768.0 / (ns_simd * 1e-9)
+                row["tflops"] = round(flops / 1e12, 1)
+                row["pct_of_2500"] = round(100 * flops / 1e12 / PEAK_MFMA_BF16_TFLOPS, 1)
+            if name in MIX_VALU_PER_BLOCK:
+                row["ns_per_instruction_per_simd"] = round(ns_simd / MIX_VALU_PER_BLOCK[name], 3)
+            row["measured_mfma_peak_tflops"] = round(peak, 1)
+            print(json.dumps(row), flush=True)
 
 
 def all_configs(args):
@@ -467,6 +537,9 @@ def main():
         return
     if args.decode:
         decode_report(args)
+        return
+    if args.ceiling:
+        ceiling_report(args)
         return
     if args.naive:
         naive_report(args)

@@ -17,8 +17,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtca.so")
-# the benchmark report's matrix-core throughput probe (not the attention library)
-MEASURE_SRC = os.path.join(HERE, "measure", "mfma_peak.hip")
+# the benchmark report's probes (not the attention library): the matrix-core
+# throughput loop and the per-block instruction-mix ceilings
+MEASURE_SRCS = sorted(glob.glob(os.path.join(HERE, "measure", "*.hip")))
 MEASURE_LIB = os.path.join(HERE, "libtca_measure.so")
 
 HIPCC_FLAGS = [
@@ -62,7 +63,7 @@ def build(out: str = LIB, extra=(), verbose: bool = False) -> str:
     """The attention library (and, for the default output, the measurement probe)."""
     _compile(sources(), out, extra, verbose)
     if out == LIB:
-        _compile([MEASURE_SRC], MEASURE_LIB, extra, verbose)
+        _compile(MEASURE_SRCS, MEASURE_LIB, extra, verbose)
     return out
 
 

@@ -150,8 +150,15 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const float sl2 = sc.sl2;   // positive multiplier of Q' K^T (scale is dQ's factor)
     __shared__ float dsh[NKH == 2 ? BQ : 1];   // D of each row, from key half 0
 
-    // The first K/V tile's loads and this row's LSE go out before the Q, dO and O
-    // rows, so their latency overlaps the D computation instead of following it.
+    // Key half 0 computes D = rowsum(dO o O). Its O rows are the first loads, and the
+    // first K/V tile's and this row's LSE follow before the Q and dO rows: every
+    // prologue load is in flight before any of them is waited for.
+    Row8<OT> orw[D / 16];
+    if (khalf == 0) {
+        const OT* orow = o + (bh * N + qc) * D + 8 * h;
+#pragma unroll
+        for (int c = 0; c < D / 16; ++c) orw[c].load(orow + 16 * c);
+    }
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (uint32_t)N * D * 2);
     const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)N * D * 2);
     const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a tile
@@ -171,7 +178,6 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         const bf16_t* qrow = ROPE ? rq.q + tm.b * rq.qb + hq * rq.qh + qc * rq.qn + 8 * h
                                   : q + (bh * N + qc) * D + 8 * h;
         const bf16_t* drow = dout + (bh * N + qc) * D + 8 * h;
-        const OT* orow = o + (bh * N + qc) * D + 8 * h;
         u32x4 dvr[DC], qraw[DC];
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
@@ -192,7 +198,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             for (int c = 0; c < DC; ++c) {
                 const u32x4 dv = dvr[c];
                 float ov[8];
-                load8_f32(orow + 16 * c, ov);
+                orw[c].get(ov);
                 part = fmaf(bf16_lo(dv.x), ov[0], part);
                 part = fmaf(bf16_hi(dv.x), ov[1], part);
                 part = fmaf(bf16_lo(dv.y), ov[2], part);

@@ -256,6 +256,29 @@ __device__ __forceinline__ void store_out1(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_out1(bf16_t* p, float v) {
     *p = (bf16_t)(pack_bf16(v, 0.f) & 0xffffu);
 }
+// Eight consecutive output-type elements held as raw registers, so a load can be
+// issued early and converted later (float32: 32 bytes, bfloat16: 16 bytes).
+template <typename T> struct Row8;
+template <> struct Row8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const f32x4*>(p);
+        b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+        x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+        x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+    }
+};
+template <> struct Row8<bf16_t> {
+    u32x4 w;
+    __device__ __forceinline__ void load(const bf16_t* p) { w = *reinterpret_cast<const u32x4*>(p); }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+        x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+        x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+    }
+};
+
 // Eight consecutive elements (float32 or bfloat16) at p -> float32.
 __device__ __forceinline__ void load8_f32(const float* p, float (&x)[8]) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
