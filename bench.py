@@ -456,7 +456,7 @@ def decode_report(args):
         lse = torch.empty((s.B, s.Hq, s.Nq), dtype=torch.float32, device=q.device)
         nws = int(tca.lib().attn_decode_workspace_bytes(tca.ATTN_BF16 if s.dtype == "bf16" else tca.ATTN_F32,
                                                         s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d))
-        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=q.device)
+        ws = tca.decode_workspace(nws, q.device)
         causal, scale = bool(s.causal), s.scale
         for _ in range(20):
             tca.attn_decode(q, k, v, causal, scale, out=(o, lse), workspace=ws)

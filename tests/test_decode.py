@@ -136,3 +136,20 @@ def test_decode_empty():
     k = torch.zeros(2, 2, 10, 64, dtype=torch.bfloat16, device="cuda")
     o, lse = tca.attn_decode(q, k, k)
     assert o.shape == (2, 4, 0, 64) and lse.shape == (2, 4, 0)
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace through calls of different shapes (16, 128 and 32 key splits per row):
+    every call matches a call on a fresh workspace (the partials of one call never leak
+    into the next)."""
+    shapes = [workloads.DECODE_CONFIGS["decode_gpt2_gqa"], workloads.DECODE_CONFIGS["decode_wide_d128"],
+              workloads.make_decode_shape(2, 8, 2, 3, 2000, 64, seed=41), workloads.DECODE_CONFIGS["decode_gpt2_gqa"]]
+    L = tca.lib()
+    sizes = [int(L.attn_decode_workspace_bytes(tca.ATTN_BF16, s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d)) for s in shapes]
+    shared = tca.decode_workspace(max(sizes), "cuda")
+    for s, n in zip(shapes, sizes):
+        q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
+        o1, l1 = tca.attn_decode(q, k, v, causal=True, scale=s.scale, workspace=shared)
+        o2, l2 = tca.attn_decode(q, k, v, causal=True, scale=s.scale, workspace=tca.decode_workspace(n, "cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), (s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d)

@@ -60,13 +60,15 @@ def test_fwd_bwd_graph_replays_match_eager(name):
         torch.cuda.synchronize()
 
 
-def test_decode_graph_replays_match_eager():
-    s = workloads.DECODE_CONFIGS["decode_wide_d128"]
+@pytest.mark.parametrize("name", ["decode_wide_d128", "decode_gpt2_gqa"])
+def test_decode_graph_replays_match_eager(name):
+    # wide: 128 key splits per row (column-block merge); GPT-2-small: 16 (whole-row merge)
+    s = workloads.DECODE_CONFIGS[name]
     q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
     o = torch.empty((s.B, s.Hq, s.Nq, s.d), device="cuda")
     lse = torch.empty((s.B, s.Hq, s.Nq), device="cuda")
     n = int(tca.lib().attn_decode_workspace_bytes(tca.ATTN_BF16, s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d))
-    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    ws = tca.decode_workspace(n, "cuda")
     call = lambda: tca.attn_decode(q, k, v, True, s.scale, out=(o, lse), workspace=ws)
     call()
     torch.cuda.synchronize()

@@ -260,6 +260,11 @@ def attn_bwd_dkdv(q, k, v, o, lse, dO, dq, dk, dv, workspace, causal=True, scale
     _bwd_call("attn_bwd_dkdv", q, k, v, o, lse, dO, dq, dk, dv, workspace, causal, scale)
 
 
+def decode_workspace(nbytes: int, device) -> torch.Tensor:
+    """A workspace of `nbytes` (attn_decode_workspace_bytes) for attn_decode."""
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
 def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = True,
                 scale: Optional[float] = None, out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None,
                 out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None
@@ -286,7 +291,7 @@ def attn_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool 
     L = lib()
     ws_bytes = int(L.attn_decode_workspace_bytes(dt, B, Hq, Hkv, Nq, Nk, d))
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(ws_bytes, q.device)
     _same_device(q, workspace=workspace)
     wsn = _nbytes(workspace)
     _check(L.attn_decode(dt, _code(o.dtype), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
