@@ -48,16 +48,18 @@ template <int D> constexpr int kPad = (D == 128) ? 24 : 8;   // K/V tile row pad
 }  // namespace bwdq
 
 // Global -> registers: the K and V chunks of one tile through buffer resources
-// over the head's N rows; voff is this thread's byte offset of chunk 0 in the
-// tile's first row. Thread tid owns chunks tid + T u, T threads (a wave reads
+// over the head's N rows; koff / voff are this thread's byte offsets of its first
+// chunk (row tid / (D/8), chunk tid % (D/8) of the tile), K rows contiguous, V
+// rows vrow bytes apart. Thread tid owns chunks tid + T u, T threads (a wave reads
 // whole rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
 __device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
-                                            __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
+                                            uint32_t koff, __amdgpu_buffer_rsrc_t vr, uint32_t voff, uint32_t vrow) {
+    constexpr int ROWS_PER_U = bwdq::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        kreg[u] = buf_load16(kr, voff + u * bwdq::kThreads<D> * 16);
-        vreg[u] = buf_load16(vr, voff + u * bwdq::kThreads<D> * 16);
+        kreg[u] = buf_load16(kr, koff + u * bwdq::kThreads<D> * 16);
+        vreg[u] = buf_load16(vr, voff + u * ROWS_PER_U * vrow);
     }
 }
 
@@ -146,7 +148,6 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const int qc = min(qi, N - 1);
     const bool qok = qi < N;
     const bf16_t* kh = k + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
-    const bf16_t* vh = v + ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const float sl2 = sc.sl2;   // positive multiplier of Q' K^T (scale is dQ's factor)
     __shared__ float dsh[NKH == 2 ? BQ : 1];   // D of each row, from key half 0
 
@@ -160,10 +161,12 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         for (int c = 0; c < D / 16; ++c) orw[c].load(orow + 16 * c);
     }
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(kh, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vh, (uint32_t)N * D * 2);
-    const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a tile
+    const VRows<D, ROPE> vrows(v, rq, tm.b, Hkv, tm.hkv, N);
+    const uint32_t ld_off = (uint32_t)tid * 16;                      // byte offset of chunk 0 in a K tile
+    const uint32_t vld_off = (uint32_t)(tid / CPR) * vrows.row_bytes + (uint32_t)(tid % CPR) * 16;
+    const uint32_t vtile = BC * vrows.row_bytes;                       // bytes per V tile
     u32x4 kreg[KCH], vreg[KCH];
-    bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off);
+    bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off, vrows.rs, vld_off, vrows.row_bytes);
     const float lse_i = lse[bh * N + qc];
     QRopeRow<D> qtab;   // ROPE: the row's table values, issued with the first loads
     if constexpr (ROPE) qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
@@ -231,7 +234,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     constexpr int TBUF = BC * LD;                                      // elements per LDS tile buffer
 
     bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
-    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
+    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off + BC * D * 2, vrows.rs, vld_off + vtile, vrows.row_bytes);
     __syncthreads();
     if constexpr (NKH == 2) {
         if (khalf == 1) Di = dsh[32 * rb + r];
@@ -290,7 +293,8 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + (buf ^ 1) * TBUF + st_off,
                                  &Vs[0][0][0] + (buf ^ 1) * TBUF + st_off);
             if (j + 2 < ntile)
-                bwd_load_kv<D, KCH>(kreg, vreg, krs, vrs, ld_off + (uint32_t)(j + 2) * (BC * D * 2));
+                bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows.rs,
+                                    vld_off + (uint32_t)(j + 2) * vtile, vrows.row_bytes);
         }
         __syncthreads();
     }
@@ -381,14 +385,17 @@ template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-r
 
 }  // namespace bwdkv
 
-// OT: element type of dk and dv (float32, or bfloat16 rounded to nearest even)
-template <int D, typename OT>
+// OT: element type of dk and dv (float32, or bfloat16 rounded to nearest even).
+// ROPE: V is read in place through rv's strides, K holds the rotated keys
+// (contiguous), and dK is turned back by the transpose rotation at the store; dK and
+// dV go through rv's strides.
+template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, (D == 128) ? 2 : 1)
 bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
                 const float* __restrict__ l2, const float* __restrict__ delta,
                 OT* __restrict__ dk, OT* __restrict__ dv,
-                int Hq, int Hkv, int N, int causal, ScoreScale sc, int ntiles, int wg_per_unit) {
+                int Hq, int Hkv, int N, int causal, ScoreScale sc, int ntiles, int wg_per_unit, KVRope rv) {
     using namespace bwdkv;
     constexpr int NQW = Cfg<D>::NQW;
     constexpr int NW = 2 * NQW;               // waves
@@ -520,7 +527,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // new K/V tile: this lane's K, V rows as fp16 B operands; clear partials
             cur_tile = tile;
             const bf16_t* krow = k + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
-            const bf16_t* vrow = v + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
+            const bf16_t* vrow = ROPE ? rv.v + b * rv.vb + hkv * rv.vh + (long long)min(kw, N - 1) * rv.vn + 8 * h
+                                      : v + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
                 kb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(krow + 16 * c)));
@@ -648,15 +656,42 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // ---- end of a K/V tile: each wave holds its tensor's final values for its 32 keys
             // (accumulator e of dim block x: key 32kh + 8(e/4) + 4h + e%4, dim 32x + r)
             if (it + 1 == nitems || tile_of(cur) != tile) {
-                OT* const dst = qw ? dk : dv;
                 const float f = qw ? scale : 1.0f;
-#pragma unroll
-                for (int x = 0; x < DB; ++x)
+                if constexpr (ROPE) {
+                    // dims 32x + r and 32x + r + D/2 (blocks x and x + DB/2 of this lane) form a
+                    // rotation pair: dK is turned back with the key row's table entries
+                    OT* const dst = static_cast<OT*>(qw ? rv.dk : rv.dv);
+                    const long long sb = qw ? rv.kb : rv.db, sh = qw ? rv.kh : rv.dh, srow = qw ? rv.kn : rv.dn;
+                    OT* const base = dst + b * sb + hkv * sh;
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
                         const int key = kw0 + 8 * (e >> 2) + 4 * h + (e & 3);
-                        if (key < N) store_out1(dst + kvoff + (size_t)key * D + 32 * x + r, dka[x][e] * f);
+                        if (key >= N) continue;
+                        OT* const row = base + (long long)key * srow;
+#pragma unroll
+                        for (int x = 0; x < DB / 2; ++x) {
+                            const int f0 = 32 * x + r;
+                            const float g1 = dka[x][e] * f, g2 = dka[x + DB / 2][e] * f;
+                            if (qw) {
+                                const float c = rv.cs[(size_t)key * (D / 2) + f0], si = rv.sn[(size_t)key * (D / 2) + f0];
+                                store_out1(row + f0, g1 * c + g2 * si);
+                                store_out1(row + f0 + D / 2, g2 * c - g1 * si);
+                            } else {
+                                store_out1(row + f0, g1);
+                                store_out1(row + f0 + D / 2, g2);
+                            }
+                        }
                     }
+                } else {
+                    OT* const dst = qw ? dk : dv;
+#pragma unroll
+                    for (int x = 0; x < DB; ++x)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const int key = kw0 + 8 * (e >> 2) + 4 * h + (e & 3);
+                            if (key < N) store_out1(dst + kvoff + (size_t)key * D + 32 * x + r, dka[x][e] * f);
+                        }
+                }
             }
         }
         // ---- end of a K/V tile: combine the NQW query sub-blocks' partial dK, dV
@@ -735,18 +770,43 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                         }
                     }
             }
-#pragma unroll
-            for (int x = 0; x < DB; ++x)
+            if constexpr (ROPE) {
+                // dims 32x + r and 32x + r + D/2 (blocks x and x + DB/2 of this lane) form a
+                // rotation pair: dK is turned back with the key row's table entries
+                OT* const dkb = static_cast<OT*>(rv.dk) + b * rv.kb + hkv * rv.kh;
+                OT* const dvb = static_cast<OT*>(rv.dv) + b * rv.db + hkv * rv.dh;
 #pragma unroll
                 for (int i = 0; i < E; ++i) {
                     const int e = E * qw + i;
                     const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
-                    if (key < N) {
-                        const size_t off = kvoff + (size_t)key * D + 32 * x + r;
-                        store_out1(dk + off, sk[x][i] * scale);
-                        store_out1(dv + off, sv[x][i]);
+                    if (key >= N) continue;
+                    OT* const krow_o = dkb + (long long)key * rv.kn;
+                    OT* const vrow_o = dvb + (long long)key * rv.dn;
+#pragma unroll
+                    for (int x = 0; x < DB / 2; ++x) {
+                        const int f0 = 32 * x + r;
+                        const float c = rv.cs[(size_t)key * (D / 2) + f0], si = rv.sn[(size_t)key * (D / 2) + f0];
+                        const float g1 = sk[x][i] * scale, g2 = sk[x + DB / 2][i] * scale;
+                        store_out1(krow_o + f0, g1 * c + g2 * si);
+                        store_out1(krow_o + f0 + D / 2, g2 * c - g1 * si);
+                        store_out1(vrow_o + f0, sv[x][i]);
+                        store_out1(vrow_o + f0 + D / 2, sv[x + DB / 2][i]);
                     }
                 }
+            } else {
+#pragma unroll
+                for (int x = 0; x < DB; ++x)
+#pragma unroll
+                    for (int i = 0; i < E; ++i) {
+                        const int e = E * qw + i;
+                        const int key = tile * BC + 32 * kh_ + 8 * (e >> 2) + 4 * h + (e & 3);
+                        if (key < N) {
+                            const size_t off = kvoff + (size_t)key * D + 32 * x + r;
+                            store_out1(dk + off, sk[x][i] * scale);
+                            store_out1(dv + off, sv[x][i]);
+                        }
+                    }
+            }
         }
         wait_vmem_all();   // the copies land before the barrier that publishes them
         __syncthreads();
@@ -770,15 +830,16 @@ static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int D, typename OT>
+template <int D, typename OT, bool ROPE>
 static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     const int ntiles = (a.N + bwdkv::BC - 1) / bwdkv::BC;
     const int per_unit = a.causal ? (ntiles + 1) / 2 : ntiles;
     const int threads = 64 * 2 * bwdkv::Cfg<D>::NQW;
     const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
+    const KVRope rv = ROPE ? *a.kvrope : KVRope{};
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT, ROPE>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
                        (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, (OT*)a.dk,
-                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, score_scale(a.scale), ntiles, per_unit);
+                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, score_scale(a.scale), ntiles, per_unit, rv);
     return hipGetLastError();
 }
 
@@ -792,10 +853,15 @@ static hipError_t launch_bwd_dq_rope_or_not(const AttnArgs& a, hipStream_t st) {
 hipError_t launch_bwd_mfma_dq(const AttnArgs& a, hipStream_t st) {
     return a.rope ? launch_bwd_dq_rope_or_not<true>(a, st) : launch_bwd_dq_rope_or_not<false>(a, st);
 }
-hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st) {
+template <bool ROPE>
+static hipError_t launch_bwd_dkdv_rope_or_not(const AttnArgs& a, hipStream_t st) {
     if (a.out_dtype == ATTN_BF16)
-        return (a.d == 64) ? launch_bwd_dkdv_d<64, bf16_t>(a, st) : launch_bwd_dkdv_d<128, bf16_t>(a, st);
-    return (a.d == 64) ? launch_bwd_dkdv_d<64, float>(a, st) : launch_bwd_dkdv_d<128, float>(a, st);
+        return (a.d == 64) ? launch_bwd_dkdv_d<64, bf16_t, ROPE>(a, st) : launch_bwd_dkdv_d<128, bf16_t, ROPE>(a, st);
+    return (a.d == 64) ? launch_bwd_dkdv_d<64, float, ROPE>(a, st) : launch_bwd_dkdv_d<128, float, ROPE>(a, st);
+}
+
+hipError_t launch_bwd_mfma_dkdv(const AttnArgs& a, hipStream_t st) {
+    return a.kvrope ? launch_bwd_dkdv_rope_or_not<true>(a, st) : launch_bwd_dkdv_rope_or_not<false>(a, st);
 }
 
 }  // namespace tca

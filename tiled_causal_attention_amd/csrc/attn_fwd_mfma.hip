@@ -71,16 +71,18 @@ constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 }  // namespace fwd
 
 // Global -> registers: the K and V chunks of one tile through buffer
-// resources over the head's N rows; voff is this thread's byte offset of chunk
-// 0 in the tile's first row. Thread tid owns chunks tid + T u, T threads (a wave reads
-// whole rows); rows past the end of the sequence read as zero.
+// resources over the head's N rows; koff / voff are this thread's byte offsets
+// of its first chunk (row tid / (D/8), chunk tid % (D/8) of the tile), K rows
+// contiguous, V rows vrow bytes apart. Thread tid owns chunks tid + T u, T threads
+// (a wave reads whole rows); rows past the end of the sequence read as zero.
 template <int D, int KCH>
 __device__ __forceinline__ void load_kv_tile(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
-                                             __amdgpu_buffer_rsrc_t vr, uint32_t voff) {
+                                             uint32_t koff, __amdgpu_buffer_rsrc_t vr, uint32_t voff, uint32_t vrow) {
+    constexpr int ROWS_PER_U = fwd::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        kreg[u] = buf_load16(kr, voff + u * fwd::kThreads<D> * 16);
-        vreg[u] = buf_load16(vr, voff + u * fwd::kThreads<D> * 16);
+        kreg[u] = buf_load16(kr, koff + u * fwd::kThreads<D> * 16);
+        vreg[u] = buf_load16(vr, voff + u * ROWS_PER_U * vrow);
     }
 }
 
@@ -99,8 +101,8 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
 }
 
 // OT: element type of o (float32, or bfloat16 rounded to nearest even at the store).
-// ROPE: Q is read through rq's strides and rotated in registers (rotary embedding);
-// K and V then hold the rotated keys and the values, contiguous.
+// ROPE: Q is read through rq's strides and rotated in registers (rotary embedding),
+// V is read in place through rq's V strides, and K holds the rotated keys, contiguous.
 template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -179,16 +181,18 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 
     const size_t kvoff = ((size_t)tm.b * Hkv + tm.hkv) * N * D;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)N * D * 2);
-    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff, (uint32_t)N * D * 2);
-    const uint32_t ld_off = (uint32_t)tid * 16;                     // byte offset of chunk 0 in a tile
+    const VRows<D, ROPE> vrows(v, rq, tm.b, Hkv, tm.hkv, N);
+    const uint32_t ld_off = (uint32_t)tid * 16;                     // byte offset of chunk 0 in a K tile
+    const uint32_t vld_off = (uint32_t)(tid / CPR) * vrows.row_bytes + (uint32_t)(tid % CPR) * 16;
+    const uint32_t vtile = BC * vrows.row_bytes;                      // bytes per V tile
     const int st_row = tid / CPR, st_col = (tid % CPR) * 8;           // LDS slot of chunk 0
     bf16_t* const kst0 = &Ks[0][st_row][st_col];
     _Float16* const vst0 = &Vs[0][st_row][st_col];
     constexpr int KBUF = BC * LD;                                     // elements per LDS buffer
 
-    load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off);
+    load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off, vrows.rs, vld_off, vrows.row_bytes);
     store_kv_tile<D, KCH>(kreg, vreg, kst0, vst0);
-    if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off + BC * D * 2);
+    if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off + BC * D * 2, vrows.rs, vld_off + vtile, vrows.row_bytes);
     __syncthreads();
     if constexpr (ROPE) {
         rope_rotate_q<D>(qraw, qtab);
@@ -272,7 +276,9 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
         if (j + 1 < ntile) {
             store_kv_tile<D, KCH>(kreg, vreg, kst0 + (buf ^ 1) * KBUF, vst0 + (buf ^ 1) * KBUF);
-            if (j + 2 < ntile) load_kv_tile<D, KCH>(kreg, vreg, krs, vrs, ld_off + (uint32_t)(j + 2) * (BC * D * 2));
+            if (j + 2 < ntile)
+                load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows.rs,
+                                     vld_off + (uint32_t)(j + 2) * vtile, vrows.row_bytes);
         }
         __syncthreads();
     }

@@ -13,7 +13,11 @@
 // into the caller's layouts, rounding once to the output type.
 //
 // Each step is one HBM-bound pass (a thread per 8 pairs of a row, consecutive
-// threads on consecutive pairs).
+// threads on consecutive pairs). On the matrix-core path the kernels take over all
+// of it except the rotation of k: they read q and v through their strides, rotate
+// q in registers and store dq, dk, dv through their strides (dq, dk turned back),
+// and only k is rotated into a contiguous copy here, once per call, for the tiles
+// of every query block to read.
 #include "tca_internal.h"
 
 namespace tca {

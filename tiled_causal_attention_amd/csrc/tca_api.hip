@@ -166,23 +166,30 @@ bool rows_aligned16(const void* p, const attn_layout* l, size_t es) {
            ((size_t)l->stride_n * es) % 16 == 0;
 }
 
-// k (rotated) and v into the contiguous staging copies, one launch (q is rotated in
-// the kernels' registers on the fused path)
-hipError_t stage_kv(const RopeWs& w, attn_dtype dtype, const void* k, const attn_layout* kl, const void* v,
-                    const attn_layout* vl, const float* cs, const float* sn, int B, int Hkv, int N, int d,
-                    hipStream_t st) {
+// k, rotated, into its contiguous staging copy, one launch (on the fused path q is
+// rotated in the kernels' registers and v is read in place)
+hipError_t stage_k(const RopeWs& w, attn_dtype dtype, const void* k, const attn_layout* kl, const float* cs,
+                   const float* sn, int B, int Hkv, int N, int d, hipStream_t st) {
     const attn_layout ck = contiguous_layout(Hkv, N, d);
     tca::CopyJobs jobs;
-    jobs.n = 2;
+    jobs.n = 1;
     jobs.j[0] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, 1);
-    jobs.j[1] = tca::copy_job(v, vl ? *vl : ck, w.v, ck, B, Hkv, N, d, 0);
     return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
 }
 
+// V read in place by the matrix-core kernels: 16-byte aligned rows at least d apart, and
+// every byte offset within a head's rows (past the last row included) fits 32 bits
+bool v_in_place(const void* v, const attn_layout* vl, int Hkv, int N, int d) {
+    if (!rows_aligned16(v, vl, 2)) return false;
+    const attn_layout l = vl ? *vl : contiguous_layout(Hkv, N, d);
+    return l.stride_n >= d && (int64_t)(N + 64) * l.stride_n * 2 < ((int64_t)1 << 32);
+}
+
 tca::QRope make_qrope(const void* q, const attn_layout* ql, const float* cs, const float* sn, void* dq,
-                      const attn_layout* gl, int Hq, int N, int d) {
+                      const attn_layout* gl, const void* v, const attn_layout* vl, int Hq, int Hkv, int N, int d) {
     const attn_layout cq = contiguous_layout(Hq, N, d);
     const attn_layout a = ql ? *ql : cq, g = gl ? *gl : cq;
+    const attn_layout vv = vl ? *vl : contiguous_layout(Hkv, N, d);
     tca::QRope r;
     r.q = static_cast<const tca::bf16_t*>(q);
     r.qb = a.stride_b;
@@ -192,6 +199,32 @@ tca::QRope make_qrope(const void* q, const attn_layout* ql, const float* cs, con
     r.gb = g.stride_b;
     r.gh = g.stride_h;
     r.gn = g.stride_n;
+    r.cs = cs;
+    r.sn = sn;
+    r.v = static_cast<const tca::bf16_t*>(v);
+    r.vb = vv.stride_b;
+    r.vh = vv.stride_h;
+    r.vn = vv.stride_n;
+    return r;
+}
+
+tca::KVRope make_kvrope(const void* v, const attn_layout* vl, void* dk, const attn_layout* kl, void* dv,
+                        const attn_layout* dl, const float* cs, const float* sn, int Hkv, int N, int d) {
+    const attn_layout ck = contiguous_layout(Hkv, N, d);
+    const attn_layout vv = vl ? *vl : ck, gk = kl ? *kl : ck, gv = dl ? *dl : ck;
+    tca::KVRope r;
+    r.v = static_cast<const tca::bf16_t*>(v);
+    r.vb = vv.stride_b;
+    r.vh = vv.stride_h;
+    r.vn = vv.stride_n;
+    r.dk = dk;
+    r.kb = gk.stride_b;
+    r.kh = gk.stride_h;
+    r.kn = gk.stride_n;
+    r.dv = dv;
+    r.db = gv.stride_b;
+    r.dh = gv.stride_h;
+    r.dn = gv.stride_n;
     r.cs = cs;
     r.sn = sn;
     return r;
@@ -359,12 +392,14 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const RopeWs w = rope_ws(workspace, false, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
-    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2)) {
-        // fused: the forward reads q through its strides and rotates it in registers
-        if (stage_kv(w, dtype, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
-            return ATTN_EHIP;
-        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, nullptr, nullptr, Hq, N, d);
-        AttnArgs a = make_args(dtype, out_dtype, q, w.k, w.v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
+        v_in_place(v, v_layout, Hkv, N, d)) {
+        // fused: the forward reads q through its strides and rotates it in registers, and
+        // reads v in place; only k is staged (rotated once, read by every query tile)
+        if (stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
+        const tca::QRope rq =
+            make_qrope(q, q_layout, rope_cos, rope_sin, nullptr, nullptr, v, v_layout, Hq, Hkv, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                                B, Hq, Hkv, N, d, causal, scale);
         a.rope = &rq;
         return from_hip(tca::launch_fwd_mfma(a, st));
@@ -396,30 +431,24 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const RopeWs w = rope_ws(workspace, true, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
     hipStream_t st = (hipStream_t)stream;
-    const attn_layout ckv = contiguous_layout(Hkv, N, d);
     if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
-        rows_aligned16(dq, dq_layout, elsize(out_dtype))) {
-        // fused: the dQ pass reads q through its strides, rotates it in registers (its fp16
-        // copy for the dK/dV pass is rotated too) and stores dq turned back through dq's
-        // strides; k, v are staged and dk, dv scattered as below
-        if (stage_kv(w, dtype, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
-            return ATTN_EHIP;
-        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, Hq, N, d);
-        AttnArgs a = make_args(dtype, out_dtype, q, w.k, w.v, o, lse, dO, dq, w.dk, w.dv, w.bwd, w.bwd_bytes, B, Hq,
-                               Hkv, N, d, causal, scale);
+        rows_aligned16(dq, dq_layout, elsize(out_dtype)) && v_in_place(v, v_layout, Hkv, N, d)) {
+        // fused: only k is staged (rotated). The dQ pass reads q through its strides,
+        // rotates it in registers (its fp16 copy for the dK/dV pass is rotated too), reads
+        // v in place and stores dq turned back through dq's strides; the dK/dV pass reads v
+        // in place and stores dk turned back, and dv, through their strides
+        if (stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
+        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, v, v_layout, Hq, Hkv, N, d);
+        const tca::KVRope rv = make_kvrope(v, v_layout, dk, dk_layout, dv, dv_layout, rope_cos, rope_sin, Hkv, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, dO, dq, dk, dv, w.bwd, w.bwd_bytes, B, Hq, Hkv,
+                               N, d, causal, scale);
         a.rope = &rq;
         s = run_dq(a, st);
         if (s != ATTN_OK) return s;
-        AttnArgs a2 = a;   // dK/dV into float32 temporaries (one rounding after the rotation)
+        AttnArgs a2 = a;
         a2.rope = nullptr;
-        a2.out_dtype = ATTN_F32;
-        s = run_dkdv(a2, st);
-        if (s != ATTN_OK) return s;
-        tca::CopyJobs jobs;
-        jobs.n = 2;
-        jobs.j[0] = tca::copy_job(w.dk, ckv, dk, dk_layout ? *dk_layout : ckv, B, Hkv, N, d, 2);
-        jobs.j[1] = tca::copy_job(w.dv, ckv, dv, dv_layout ? *dv_layout : ckv, B, Hkv, N, d, 0);
-        return from_hip(tca::layout_copy(ATTN_F32, out_dtype, jobs, rope_cos, rope_sin, N, d, st));
+        a2.kvrope = &rv;
+        return run_dkdv(a2, st);
     }
     hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
     if (e != hipSuccess) return ATTN_EHIP;

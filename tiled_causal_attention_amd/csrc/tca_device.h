@@ -328,6 +328,41 @@ struct QRope {
     long long gb, gh, gn;    // dq strides
     const float* cs;         // [N][D/2]
     const float* sn;
+    const bf16_t* v;         // V read in place through its strides (row starts 16-byte aligned, vn >= D)
+    long long vb, vh, vn;
+};
+
+// The dK/dV pass of the rotary path: V read in place through its strides, dK
+// turned back by the transpose rotation and dK, dV written through their strides
+// in the output type (one rounding).
+struct KVRope {
+    const bf16_t* v;
+    long long vb, vh, vn;    // V strides (row starts 16-byte aligned)
+    void* dk;
+    long long kb, kh, kn;    // dk strides
+    void* dv;
+    long long db, dh, dn;    // dv strides
+    const float* cs;         // [N][D/2]
+    const float* sn;
+};
+
+// Buffer resource and per-row byte stride of one KV head's V rows: in place through
+// rq's strides (ROPE), else contiguous [N][D]. Rows at or past N lie outside the
+// range (the row stride is at least D) and read as zero.
+template <int D, bool ROPE>
+struct VRows {
+    __amdgpu_buffer_rsrc_t rs;
+    uint32_t row_bytes;
+    __device__ __forceinline__ VRows(const bf16_t* v, const QRope& rq, int b, int Hkv, int hkv, int N) {
+        if constexpr (ROPE) {
+            const bf16_t* base = rq.v + b * rq.vb + hkv * rq.vh;
+            row_bytes = (uint32_t)(rq.vn * 2);
+            rs = make_rsrc(base, (uint32_t)(((long long)(N - 1) * rq.vn + D) * 2));
+        } else {
+            row_bytes = (uint32_t)(D * 2);
+            rs = make_rsrc(v + ((size_t)b * Hkv + hkv) * N * D, (uint32_t)N * D * 2);
+        }
+    }
 };
 
 // The cos/sin values a lane needs to rotate its Q chunks: frequencies 16c + 8h .. +7

@@ -30,6 +30,10 @@ struct AttnArgs {
     // (k, v hold the rotated keys and the values); the dQ pass stores dQ turned back
     // by the transpose rotation through rope->dq's strides. nullptr: plain layout.
     const QRope* rope = nullptr;
+    // matrix-core dK/dV pass only: V read through these strides (k holds the rotated
+    // keys), dK turned back by the transpose rotation, dK and dV stored through these
+    // strides. nullptr: plain layout.
+    const KVRope* kvrope = nullptr;
 };
 
 // True when the matrix-core kernels serve these inputs: bf16, d in {64, 128}.
