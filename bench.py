@@ -122,6 +122,35 @@ def counted_traffic(kernel: str, workload: str, out_dtype: str = "f32"):
     return ent["hbm_bytes_per_launch"]
 
 
+def host_cpu() -> dict:
+    """The host CPU: model name, physical cores and logical CPUs of the machine, and
+    the logical CPUs this process may run on."""
+    model, cores, logical = None, set(), 0
+    phys = core = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "processor":
+                    logical += 1
+                elif key == "model name" and model is None:
+                    model = val
+                elif key == "physical id":
+                    phys = val
+                elif key == "core id":
+                    core = val
+                    cores.add((phys, core))
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cpu_model": model, "physical_cores": len(cores) or None, "logical_cpus": logical or os.cpu_count(),
+            "usable_cpus": usable}
+
+
 def cpu_baseline(s: workloads.Shape, inputs):
     """The float64 oracle, as it stands, on this host's cores."""
     import oracle
@@ -145,8 +174,9 @@ def cpu_baseline(s: workloads.Shape, inputs):
     return {
         "value": flops / (t2 - t0) / 1e12,
         "unit": "TFLOP/s",
-        "cores": min(oracle.threads(), nb * nh),
+        "cores": min(oracle.threads(), nb * nh),   # OpenMP threads that had a (b, kv-head) unit to run
         "kind": "oracle",
+        **host_cpu(),
         "sample": f"{nb} of {s.B} batch rows x {nh} of {s.Hkv} KV heads (all {g} query heads each) "
                   f"= {frac:.3f} of the workload; fwd {t1 - t0:.2f} s + bwd {t2 - t1:.2f} s, float64",
     }
