@@ -47,19 +47,21 @@ constexpr int BC = 64;           // keys per K/V tile
 template <int D> constexpr int kPad = (D == 128) ? 24 : 8;   // K/V tile row padding, as the forward's
 }  // namespace bwdq
 
-// Global -> registers: the K and V chunks of one tile through buffer resources
-// over the head's N rows; koff / voff are this thread's byte offsets of its first
-// chunk (row tid / (D/8), chunk tid % (D/8) of the tile), K rows contiguous, V
-// rows vrow bytes apart. Thread tid owns chunks tid + T u, T threads (a wave reads
-// whole rows); rows past the end of the sequence read as zero.
-template <int D, int KCH>
+// Global -> registers: the K and V chunks of one tile. K through a buffer resource
+// over the head's N contiguous rows, koff this thread's byte offset of its first
+// chunk (row tid / (D/8), chunk tid % (D/8) of the tile); V through vr, at this
+// thread's in-tile offset vlane plus the tile's byte offset vtile_off. Thread tid
+// owns chunks tid + T u, T threads (a wave reads whole rows); rows past the end
+// of the sequence read as zero.
+template <int D, int KCH, bool ROPE>
 __device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
-                                            uint32_t koff, __amdgpu_buffer_rsrc_t vr, uint32_t voff, uint32_t vrow) {
+                                            uint32_t koff, const VRows<D, ROPE>& vr, uint32_t vlane,
+                                            uint32_t vtile_off) {
     constexpr int ROWS_PER_U = bwdq::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         kreg[u] = buf_load16(kr, koff + u * bwdq::kThreads<D> * 16);
-        vreg[u] = buf_load16(vr, voff + u * ROWS_PER_U * vrow);
+        vreg[u] = vr.load16(vlane, vtile_off + u * ROWS_PER_U * vr.row_bytes);
     }
 }
 
@@ -166,7 +168,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const uint32_t vld_off = (uint32_t)(tid / CPR) * vrows.row_bytes + (uint32_t)(tid % CPR) * 16;
     const uint32_t vtile = BC * vrows.row_bytes;                       // bytes per V tile
     u32x4 kreg[KCH], vreg[KCH];
-    bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off, vrows.rs, vld_off, vrows.row_bytes);
+    bwd_load_kv<D, KCH, ROPE>(kreg, vreg, krs, ld_off, vrows, vld_off, 0);
     const float lse_i = lse[bh * N + qc];
     QRopeRow<D> qtab;   // ROPE: the row's table values, issued with the first loads
     if constexpr (ROPE) qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
@@ -234,7 +236,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     constexpr int TBUF = BC * LD;                                      // elements per LDS tile buffer
 
     bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
-    if (ntile > 1) bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off + BC * D * 2, vrows.rs, vld_off + vtile, vrows.row_bytes);
+    if (ntile > 1) bwd_load_kv<D, KCH, ROPE>(kreg, vreg, krs, ld_off + BC * D * 2, vrows, vld_off, vtile);
     __syncthreads();
     if constexpr (NKH == 2) {
         if (khalf == 1) Di = dsh[32 * rb + r];
@@ -293,8 +295,8 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + (buf ^ 1) * TBUF + st_off,
                                  &Vs[0][0][0] + (buf ^ 1) * TBUF + st_off);
             if (j + 2 < ntile)
-                bwd_load_kv<D, KCH>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows.rs,
-                                    vld_off + (uint32_t)(j + 2) * vtile, vrows.row_bytes);
+                bwd_load_kv<D, KCH, ROPE>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows,
+                                          vld_off, (uint32_t)(j + 2) * vtile);
         }
         __syncthreads();
     }

@@ -70,19 +70,21 @@ template <int D> constexpr int kPad = (D == 128) ? 24 : 8;
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 }  // namespace fwd
 
-// Global -> registers: the K and V chunks of one tile through buffer
-// resources over the head's N rows; koff / voff are this thread's byte offsets
-// of its first chunk (row tid / (D/8), chunk tid % (D/8) of the tile), K rows
-// contiguous, V rows vrow bytes apart. Thread tid owns chunks tid + T u, T threads
-// (a wave reads whole rows); rows past the end of the sequence read as zero.
-template <int D, int KCH>
+// Global -> registers: the K and V chunks of one tile. K through a buffer
+// resource over the head's N contiguous rows, koff this thread's byte offset of
+// its first chunk (row tid / (D/8), chunk tid % (D/8) of the tile); V through vr,
+// at this thread's in-tile offset vlane plus the tile's byte offset vtile_off.
+// Thread tid owns chunks tid + T u, T threads (a wave reads whole rows); rows
+// past the end of the sequence read as zero.
+template <int D, int KCH, bool ROPE>
 __device__ __forceinline__ void load_kv_tile(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KCH], __amdgpu_buffer_rsrc_t kr,
-                                             uint32_t koff, __amdgpu_buffer_rsrc_t vr, uint32_t voff, uint32_t vrow) {
+                                             uint32_t koff, const VRows<D, ROPE>& vr, uint32_t vlane,
+                                             uint32_t vtile_off) {
     constexpr int ROWS_PER_U = fwd::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
         kreg[u] = buf_load16(kr, koff + u * fwd::kThreads<D> * 16);
-        vreg[u] = buf_load16(vr, voff + u * ROWS_PER_U * vrow);
+        vreg[u] = vr.load16(vlane, vtile_off + u * ROWS_PER_U * vr.row_bytes);
     }
 }
 
@@ -190,9 +192,9 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     _Float16* const vst0 = &Vs[0][st_row][st_col];
     constexpr int KBUF = BC * LD;                                     // elements per LDS buffer
 
-    load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off, vrows.rs, vld_off, vrows.row_bytes);
+    load_kv_tile<D, KCH, ROPE>(kreg, vreg, krs, ld_off, vrows, vld_off, 0);
     store_kv_tile<D, KCH>(kreg, vreg, kst0, vst0);
-    if (ntile > 1) load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off + BC * D * 2, vrows.rs, vld_off + vtile, vrows.row_bytes);
+    if (ntile > 1) load_kv_tile<D, KCH, ROPE>(kreg, vreg, krs, ld_off + BC * D * 2, vrows, vld_off, vtile);
     __syncthreads();
     if constexpr (ROPE) {
         rope_rotate_q<D>(qraw, qtab);
@@ -277,8 +279,8 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         if (j + 1 < ntile) {
             store_kv_tile<D, KCH>(kreg, vreg, kst0 + (buf ^ 1) * KBUF, vst0 + (buf ^ 1) * KBUF);
             if (j + 2 < ntile)
-                load_kv_tile<D, KCH>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows.rs,
-                                     vld_off + (uint32_t)(j + 2) * vtile, vrows.row_bytes);
+                load_kv_tile<D, KCH, ROPE>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows,
+                                           vld_off, (uint32_t)(j + 2) * vtile);
         }
         __syncthreads();
     }

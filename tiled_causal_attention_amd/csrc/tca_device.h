@@ -346,22 +346,38 @@ struct KVRope {
     const float* sn;
 };
 
-// Buffer resource and per-row byte stride of one KV head's V rows: in place through
-// rq's strides (ROPE), else contiguous [N][D]. Rows at or past N lie outside the
-// range (the row stride is at least D) and read as zero.
+// One KV head's V rows: in place through rq's strides (ROPE), else contiguous
+// [N][D]. Rows at or past N lie outside the range (the row stride is at least D)
+// and read as zero.
 template <int D, bool ROPE>
 struct VRows {
-    __amdgpu_buffer_rsrc_t rs;
-    uint32_t row_bytes;
+    const unsigned char* base;
+    uint32_t bytes;       // readable bytes from base
+    uint32_t row_bytes;   // byte stride of consecutive rows
     __device__ __forceinline__ VRows(const bf16_t* v, const QRope& rq, int b, int Hkv, int hkv, int N) {
         if constexpr (ROPE) {
-            const bf16_t* base = rq.v + b * rq.vb + hkv * rq.vh;
+            base = reinterpret_cast<const unsigned char*>(rq.v + b * rq.vb + hkv * rq.vh);
             row_bytes = (uint32_t)(rq.vn * 2);
-            rs = make_rsrc(base, (uint32_t)(((long long)(N - 1) * rq.vn + D) * 2));
+            bytes = (uint32_t)(((long long)(N - 1) * rq.vn + D) * 2);
         } else {
+            base = reinterpret_cast<const unsigned char*>(v + ((size_t)b * Hkv + hkv) * N * D);
             row_bytes = (uint32_t)(D * 2);
-            rs = make_rsrc(v + ((size_t)b * Hkv + hkv) * N * D, (uint32_t)N * D * 2);
+            bytes = (uint32_t)N * D * 2;
         }
+    }
+    // 16 bytes at byte offset lane_off + off (off the same in every lane), zero
+    // past the range. With a runtime row stride the uniform part moves the
+    // resource's base instead of adding to the lane's offset, so that one
+    // register per lane serves every chunk and tile.
+    __device__ __forceinline__ u32x4 load16(uint32_t lane_off, uint32_t off) const {
+        if constexpr (ROPE) {
+            // the clamped difference is a vector instruction: read back as a scalar
+            // so that the resource stays in scalar registers
+            const uint32_t left = __builtin_amdgcn_readfirstlane(bytes > off ? bytes - off : 0u);
+            return buf_load16(make_rsrc(base + off, left), lane_off);
+        }
+        else
+            return buf_load16(make_rsrc(base, bytes), lane_off + off);
     }
 };
 
