@@ -416,7 +416,10 @@ def rope_report(args):
     """fwd+bwd of one workload (default the headline) with rotary q/k read from views of
     one fused [B, N, Hq + 2 Hkv, d] projection buffer and gradients written back into
     one such buffer, against the plain path on contiguous tensors; HIP events on the
-    launch stream around each fwd+bwd, median of 50 after 10 warm-up steps."""
+    launch stream around each fwd+bwd, median over three interleaved rounds of 50 steps
+    (10 warm-up steps before each). The rotary step keeps the forward's rotated keys
+    (k_rot) for the backward, as a training step does; the variant in which each call
+    rotates k itself is reported beside it."""
     import numpy as np
     s = workloads.CONFIGS[args.workload]
     q, k, v, do = (t.cuda() for t in workloads.make_inputs(s))
@@ -439,7 +442,14 @@ def rope_report(args):
     ws = tca.bwd_workspace(q, k)
     causal, scale = bool(s.causal), s.scale
 
-    def rope_step():
+    kr = torch.empty((s.B, s.Hkv, s.N, s.d), dtype=q.dtype, device=q.device)
+
+    def rope_step():   # training pattern: the forward's rotated keys kept for the backward
+        tca.attn_fwd_rope(qv, kv, vv, cos, sin, causal, scale, out=(o, lse), workspace=wsf, k_rot=kr)
+        tca.attn_bwd_rope(qv, kv, vv, o, lse, do, cos, sin, causal, scale, out=(gq, gk, gv), workspace=wsb,
+                          k_rot=kr)
+
+    def rope_rotate_twice_step():   # each call rotates k itself
         tca.attn_fwd_rope(qv, kv, vv, cos, sin, causal, scale, out=(o, lse), workspace=wsf)
         tca.attn_bwd_rope(qv, kv, vv, o, lse, do, cos, sin, causal, scale, out=(gq, gk, gv), workspace=wsb)
 
@@ -447,23 +457,63 @@ def rope_report(args):
         tca.attn_fwd(q, k, v, causal, scale, out=(o, lse))
         tca.attn_bwd(q, k, v, o, lse, do, causal, scale, out=(dq, dk, dv), workspace=ws)
 
-    med = {}
-    for name, fn in (("plain", plain_step), ("rope_fused_qkv", rope_step)):
+    # three rounds, the variants interleaved within each, 50 timed steps per variant and round
+    times = {"plain": [], "rope_fused_qkv": [], "rope_rotate_k_twice": []}
+    steps = (("plain", plain_step), ("rope_fused_qkv", rope_step), ("rope_rotate_k_twice", rope_rotate_twice_step))
+    for _ in range(3):
+        for name, fn in steps:
+            for _ in range(10):
+                fn()
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                e0.record()
+                fn()
+                e1.record()
+            torch.cuda.synchronize()
+            times[name] += [e0.elapsed_time(e1) for e0, e1 in evs]
+    med = {name: float(np.median(t)) for name, t in times.items()}
+    # the host's own time per step (argument checks and launches, no waiting), and each
+    # step captured in a HIP graph and replayed (events around every replay), which
+    # removes the host's share: labelled figures beside the eager ones
+    host, graph = {}, {}
+    for name, fn in steps:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            fn()
+        host[name] = (time.perf_counter() - t0) / 20 * 1e6
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
         for _ in range(10):
-            fn()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
-        torch.cuda.synchronize()
-        for e0, e1 in evs:
-            e0.record()
-            fn()
-            e1.record()
-        torch.cuda.synchronize()
-        med[name] = float(np.median([e0.elapsed_time(e1) for e0, e1 in evs]))
+            g.replay()
+        reps = []
+        for _ in range(3):
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+            torch.cuda.synchronize()
+            for e0, e1 in evs:
+                e0.record()
+                g.replay()
+                e1.record()
+            torch.cuda.synchronize()
+            reps += [e0.elapsed_time(e1) for e0, e1 in evs]
+        graph[name] = float(np.median(reps))
     fl = s.flops_fwd() + s.flops_bwd()
     print(json.dumps({"workload": s.name, "plain_fwd_bwd_ms": med["plain"], "rope_fwd_bwd_ms": med["rope_fused_qkv"],
                       "plain_tflops": fl / (med["plain"] * 1e-3) / 1e12,
                       "rope_tflops": fl / (med["rope_fused_qkv"] * 1e-3) / 1e12,
-                      "rope_overhead": med["rope_fused_qkv"] / med["plain"] - 1.0}), flush=True)
+                      "rope_overhead": med["rope_fused_qkv"] / med["plain"] - 1.0,
+                      "rope_rotate_k_twice_ms": med["rope_rotate_k_twice"],
+                      "rope_rotate_k_twice_overhead": med["rope_rotate_k_twice"] / med["plain"] - 1.0,
+                      "host_us_per_step": host, "graph_replay_ms": graph,
+                      "graph_replay_rope_overhead": graph["rope_fused_qkv"] / graph["plain"] - 1.0}), flush=True)
 
 
 def decode_report(args):

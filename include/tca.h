@@ -95,7 +95,8 @@ typedef enum attn_status {
 } attn_status;
 
 /* Version of this interface; bumped on any change (2: the out_dtype argument;
- * 3: attn_decode_noalloc and ATTN_ESCRATCH). */
+ * 3: attn_decode_noalloc and ATTN_ESCRATCH; 4: the k_rot argument of
+ * attn_fwd_rope and attn_bwd_rope). */
 int attn_abi_version(void);
 
 /* Static, human-readable name of a status code (never NULL). */
@@ -200,12 +201,18 @@ size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int
  * contiguous v are staged there and attn_fwd's kernels run on them. Pointers to
  * strided tensors need element alignment only; o and lse as for attn_fwd.
  * Strides must be >= 0 and the caller's buffers must hold every addressed
- * element. */
+ * element.
+ * k_rot: NULL, or device memory for B*Hkv*N*d elements of `dtype`, 16-byte
+ * aligned. The rotated keys (k itself without tables), contiguous [B, Hkv, N, d]
+ * and rounded to `dtype`, are then written there instead of into `workspace`,
+ * on every path, so that a training step can keep them as a saved activation and
+ * hand them to attn_bwd_rope, which then skips its own rotation of k. The
+ * workspace size does not change. */
 attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype,
                           const void* q, const attn_layout* q_layout,
                           const void* k, const attn_layout* k_layout,
                           const void* v, const attn_layout* v_layout,
-                          const float* rope_cos, const float* rope_sin,
+                          const float* rope_cos, const float* rope_sin, void* k_rot,
                           void* o, float* lse,
                           void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -221,12 +228,17 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype,
  * strides and stores dq turned back through dq's, and the dK/dV pass reads v in
  * place and stores dk turned back, and dv, through their layouts. Otherwise the
  * rotated copies are staged, attn_bwd's kernels write float32 gradients into
- * `workspace`, and one launch turns dq, dk back and scatters all three. */
+ * `workspace`, and one launch turns dq, dk back and scatters all three.
+ * k_rot: NULL, or the k_rot that attn_fwd_rope filled for the same k, tables
+ * and sizes, unchanged since (16-byte aligned). The backward then reads the
+ * rotated keys from it instead of rotating k again, and does not read k (which
+ * must still be a valid pointer). Given anything else the results are
+ * undefined. */
 attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype,
                           const void* q, const attn_layout* q_layout,
                           const void* k, const attn_layout* k_layout,
                           const void* v, const attn_layout* v_layout,
-                          const float* rope_cos, const float* rope_sin,
+                          const float* rope_cos, const float* rope_sin, const void* k_rot,
                           const void* o, const float* lse, const void* dO,
                           void* dq, const attn_layout* dq_layout,
                           void* dk, const attn_layout* dk_layout,

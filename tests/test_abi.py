@@ -57,7 +57,7 @@ def test_exports_are_c_symbols():
 
 
 def test_version_and_status_strings(L):
-    assert L.attn_abi_version() == 3
+    assert L.attn_abi_version() == 4 == tca.ABI_VERSION
     for s in (OK, EINVAL, EUNSUP, tca.ATTN_EHIP, tca.ATTN_ESCRATCH):
         assert L.attn_status_str(s)
     assert b"unknown" in L.attn_status_str(99)
@@ -334,11 +334,23 @@ def test_rope_validation(L):
     assert bwd == (rnd(nq * 2) + 2 * rnd(nk * 2) + rnd(nq * 4) + rnd(nq * 4) + 2 * rnd(nk * 4)
                    + L.attn_bwd_workspace_bytes(BF16, 2, 4, 2, 64, 64))
 
-    def fwd_rope(cos=FAKE, sin=FAKE, ql=None, q=FAKE, d=64, ws=FAKE, wsb=1 << 30, **kw):
+    def fwd_rope(cos=FAKE, sin=FAKE, ql=None, q=FAKE, d=64, ws=FAKE, wsb=1 << 30, kr=None, **kw):
         a = dict(dtype=BF16, out=F32, B=2, Hq=4, Hkv=2, N=64, causal=1, scale=0.125)
         a.update(kw)
-        return L.attn_fwd_rope(a["dtype"], a["out"], q, ql, FAKE, None, FAKE, None, cos, sin, FAKE, FAKE, ws, wsb,
-                               a["B"], a["Hq"], a["Hkv"], a["N"], d, a["causal"], a["scale"], None)
+        return L.attn_fwd_rope(a["dtype"], a["out"], q, ql, FAKE, None, FAKE, None, cos, sin, kr, FAKE, FAKE, ws,
+                               wsb, a["B"], a["Hq"], a["Hkv"], a["N"], d, a["causal"], a["scale"], None)
+
+    def bwd_rope(kr=None, dq=FAKE, ws=FAKE, wsb=1 << 30, **kw):
+        a = dict(dtype=BF16, out=F32, B=2, Hq=4, Hkv=2, N=64, d=64, causal=1, scale=0.125)
+        a.update(kw)
+        return L.attn_bwd_rope(a["dtype"], a["out"], FAKE, None, FAKE, None, FAKE, None, FAKE, FAKE, kr, FAKE, FAKE,
+                               FAKE, dq, None, FAKE, None, FAKE, None, ws, wsb, a["B"], a["Hq"], a["Hkv"], a["N"],
+                               a["d"], a["causal"], a["scale"], None)
+    assert fwd_rope(kr=FAKE + 8) == EINVAL              # the rotated-key buffer is 16-byte aligned
+    assert bwd_rope(kr=FAKE + 8) == EINVAL
+    assert bwd_rope(kr=FAKE, wsb=100) == EINVAL         # the workspace size does not shrink with k_rot
+    assert bwd_rope(kr=FAKE, dq=FAKE + 2) == EINVAL     # float32 gradients need 4-byte alignment
+    assert bwd_rope(kr=FAKE, B=0, ws=None, wsb=0) == OK
     assert fwd_rope(cos=None) == EINVAL                 # one table without the other
     assert fwd_rope(cos=FAKE + 4) == EINVAL             # tables 16-byte aligned
     assert fwd_rope(ql=lay(-1, 64, 64)) == EINVAL       # negative stride

@@ -82,3 +82,47 @@ def test_decode_graph_replays_match_eager(name):
         assert torch.equal(o, ref[0]) and torch.equal(lse, ref[1]), f"replay {rep}"
         call()
         torch.cuda.synchronize()
+
+
+def test_rope_fused_qkv_graph_replays_match_eager():
+    # rotary fwd + bwd on fused-QKV views, the forward's rotated keys kept for the backward:
+    # one K rotation launch and the six matrix-core kernels, no allocation or memset
+    s = workloads.CONFIGS["gpt2_gqa"]
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(s))
+    cos, sin = (t.cuda() for t in workloads.rope_tables(s.N, s.d))
+    H = s.Hq + 2 * s.Hkv
+    buf = torch.empty((s.B, s.N, H, s.d), dtype=q.dtype, device="cuda")
+    gbuf = torch.empty((s.B, s.N, H, s.d), device="cuda")
+    views = lambda b: (b[:, :, :s.Hq].permute(0, 2, 1, 3), b[:, :, s.Hq:s.Hq + s.Hkv].permute(0, 2, 1, 3),
+                       b[:, :, s.Hq + s.Hkv:].permute(0, 2, 1, 3))
+    qv, kv, vv = views(buf)
+    qv.copy_(q), kv.copy_(k), vv.copy_(v)
+    grads = views(gbuf)
+    o = torch.empty((s.B, s.Hq, s.N, s.d), device="cuda")
+    lse = torch.empty((s.B, s.Hq, s.N), device="cuda")
+    kr = torch.empty((s.B, s.Hkv, s.N, s.d), dtype=q.dtype, device="cuda")
+    L = tca.lib()
+    wsf = torch.empty(int(L.attn_fwd_rope_workspace_bytes(tca.ATTN_BF16, tca.ATTN_F32, s.B, s.Hq, s.Hkv, s.N, s.d)),
+                      dtype=torch.uint8, device="cuda")
+    wsb = torch.empty(int(L.attn_bwd_rope_workspace_bytes(tca.ATTN_BF16, tca.ATTN_F32, s.B, s.Hq, s.Hkv, s.N, s.d)),
+                      dtype=torch.uint8, device="cuda")
+
+    def step():
+        tca.attn_fwd_rope(qv, kv, vv, cos, sin, True, s.scale, out=(o, lse), workspace=wsf, k_rot=kr)
+        tca.attn_bwd_rope(qv, kv, vv, o, lse, do, cos, sin, True, s.scale, out=grads, workspace=wsb, k_rot=kr)
+
+    step()
+    torch.cuda.synchronize()
+    outs = (o, lse, kr, gbuf)
+    ref = [t.clone() for t in outs]
+    g = capture(step)
+    for rep in range(4):
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, ref):
+            assert torch.equal(a, b), f"replay {rep}"
+        step()
+        torch.cuda.synchronize()

@@ -159,3 +159,42 @@ def test_rope_unaligned_views():
     rq, rk, rv = oracle.attn_bwd_rope(q, k, v, do, cos, sin, 1, s.scale)
     for name, got, ref in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         check(name, got, ref, "bf16", False, "unaligned views")
+
+
+@pytest.mark.parametrize("case", ["fused_d64", "fused_d128", "f32_staged", "unaligned_staged"])
+def test_saved_rotated_keys(case):
+    # attn_fwd_rope's k_rot receives the rotated keys; attn_bwd_rope given them reads them
+    # back instead of rotating k: every output bitwise equal to the calls without k_rot
+    B, Hq, Hkv, N, d, dtype = {"fused_d64": (2, 6, 2, 200, 64, "bf16"), "fused_d128": (1, 4, 2, 161, 128, "bf16"),
+                               "f32_staged": (1, 3, 1, 100, 64, "f32"),
+                               "unaligned_staged": (2, 6, 2, 150, 64, "bf16")}[case]
+    print(f"[rope k_rot] {case}", flush=True)
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype=dtype, seed=90 + N)
+    q, k, v, do = workloads.make_inputs(s)
+    cos, sin = workloads.rope_tables(s.N, s.d, base=500.0)
+    if case == "unaligned_staged":
+        def view(t):
+            buf = torch.zeros(t.shape[:3] + (d + 1,), dtype=t.dtype, device="cuda")
+            buf[..., 1:].copy_(t.cuda())
+            return buf[..., 1:]
+        qv, kv, vv = view(q), view(k), view(v)
+    else:
+        _, qv, kv, vv = fused_views(q.cuda(), k.cuda(), v.cuda())
+    cd, sd, dod = cos.cuda(), sin.cuda(), do.cuda()
+    o1, l1 = tca.attn_fwd_rope(qv, kv, vv, cd, sd, scale=s.scale)
+    g1 = tca.attn_bwd_rope(qv, kv, vv, o1, l1, dod, cd, sd, scale=s.scale)
+    kr = torch.full((B, Hkv, N, d), float("nan"), dtype=q.dtype, device="cuda")
+    o2, l2 = tca.attn_fwd_rope(qv, kv, vv, cd, sd, scale=s.scale, k_rot=kr)
+    g2 = tca.attn_bwd_rope(qv, kv, vv, o2, l2, dod, cd, sd, scale=s.scale, k_rot=kr)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), case
+    for name, a, b in zip(("dq", "dk", "dv"), g1, g2):
+        assert torch.equal(a, b), f"{case} {name}"
+    # the saved keys: k rotated pairwise (i, i + d/2) by the table's angle, one rounding
+    kf = k.double().numpy()
+    c, sn = cos.double().numpy()[None, None], sin.double().numpy()[None, None]
+    x1, x2 = kf[..., :d // 2], kf[..., d // 2:]
+    ref = np.concatenate([x1 * c - x2 * sn, x2 * c + x1 * sn], axis=-1)
+    got = kr.float().cpu().double().numpy()
+    ulp = 2.0 ** -8 if dtype == "bf16" else 2.0 ** -23
+    assert (np.abs(got - ref) <= ulp * np.abs(ref) + 1e-6).all(), case

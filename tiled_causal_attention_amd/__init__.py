@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libtca.so")
 ATTN_F32, ATTN_BF16 = 0, 1
 ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP, ATTN_ESCRATCH = 0, 1, 2, 3, 4
 DECODE_SCRATCH_BYTES = 16 << 20   # the fixed array behind attn_decode_noalloc (ATTN_DECODE_SCRATCH_BYTES)
+ABI_VERSION = 4                   # the interface these argument lists follow (attn_abi_version)
 
 _lib = None
 
@@ -55,6 +56,9 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     vp, fp, i, f, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.attn_abi_version.argtypes, L.attn_abi_version.restype = [], i
+    if L.attn_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} implements interface version {L.attn_abi_version()}, this binding "
+                           f"version {ABI_VERSION}: rebuild the library")
     L.attn_status_str.argtypes, L.attn_status_str.restype = [i], ctypes.c_char_p
     L.attn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     L.attn_fwd_workspace_bytes.restype = sz
@@ -70,10 +74,10 @@ def lib() -> ctypes.CDLL:
     for nm in ("attn_fwd_rope_workspace_bytes", "attn_bwd_rope_workspace_bytes"):
         getattr(L, nm).argtypes = [i, i, i, i, i, i, i]
         getattr(L, nm).restype = sz
-    L.attn_fwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
+    L.attn_fwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, vp, fp, vp, sz, i, i, i, i, i, i, f, vp]
     L.attn_fwd_rope.restype = i
-    L.attn_bwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, fp, vp, vp, lp, vp, lp, vp, lp, vp, sz,
-                                i, i, i, i, i, i, f, vp]
+    L.attn_bwd_rope.argtypes = [i, i, vp, lp, vp, lp, vp, lp, fp, fp, vp, vp, fp, vp, vp, lp, vp, lp, vp, lp, vp,
+                                sz, i, i, i, i, i, i, f, vp]
     L.attn_bwd_rope.restype = i
     L.attn_fwd_naive_workspace_bytes.argtypes = [i, i, i]
     L.attn_fwd_naive_workspace_bytes.restype = sz
@@ -373,12 +377,25 @@ def _tables(cos, sin, N, d):
     return cos.data_ptr(), sin.data_ptr()
 
 
+def _check_k_rot(k_rot, q, B, Hkv, N, d):
+    """k_rot: None or a contiguous tensor of q's dtype and device holding [B, Hkv, N, d]."""
+    if k_rot is None:
+        return None
+    _expect(k_rot, "k_rot", (B, Hkv, N, d), (q.dtype,))
+    _same_device(q, k_rot=k_rot)
+    return _ptr(k_rot)
+
+
 def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optional[float] = None, out=None,
-                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None):
+                  out_dtype: Optional[torch.dtype] = None, workspace: Optional[torch.Tensor] = None,
+                  k_rot: Optional[torch.Tensor] = None):
     """Forward with rotary position embedding of q and k (rotate-half pairing; cos,
     sin: [N, d/2] float32 tables, or both None) on [B, H, N, d] views with any
-    strides (e.g. slices of one fused QKV projection). Returns (o, lse) like attn_fwd."""
+    strides (e.g. slices of one fused QKV projection). Returns (o, lse) like attn_fwd.
+    k_rot: optional contiguous [B, Hkv, N, d] tensor of q's dtype that receives the
+    rotated keys, to be passed to attn_bwd_rope (which then does not rotate k again)."""
     B, Hq, Hkv, N, d = _check_qkv(q, k, v)
+    kr = _check_k_rot(k_rot, q, B, Hkv, N, d)
     scale = default_scale(d) if scale is None else float(scale)
     dt = _dtype_code(q)
     if out is None:
@@ -395,15 +412,17 @@ def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optio
     _same_device(q, workspace=workspace)
     ql, kl, vl = _layout(q), _layout(k), _layout(v)
     _check(L.attn_fwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ql), _sptr(k), ctypes.byref(kl), _sptr(v),
-                           ctypes.byref(vl), cs, sn, _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
+                           ctypes.byref(vl), cs, sn, kr, _ptr(o), _ptr(lse), _ptr(workspace), _nbytes(workspace),
                            B, Hq, Hkv, N, d, int(bool(causal)), scale, _stream(q.device)))
     return o, lse
 
 
 def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, scale: Optional[float] = None,
-                  out=None, workspace: Optional[torch.Tensor] = None):
+                  out=None, workspace: Optional[torch.Tensor] = None, k_rot: Optional[torch.Tensor] = None):
     """Backward of attn_fwd_rope: gradients of the unrotated q, k and of v, in o's
-    dtype, written into `out` = (dq, dk, dv) views (any strides) or new contiguous tensors."""
+    dtype, written into `out` = (dq, dk, dv) views (any strides) or new contiguous tensors.
+    k_rot: the tensor attn_fwd_rope filled for the same k and tables, unchanged since
+    (the rotated keys are then read from it, not recomputed), or None."""
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or o.dim() != 4:
         raise ValueError("q, k, v, o must be 4-D [B, H, N, d]")
     dt = _dtype_code(q)
@@ -417,6 +436,7 @@ def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, 
         if t.dtype != o.dtype:
             raise TypeError("dq, dk, dv must have o's dtype")
     B, Hq, Hkv, N, d = _check_bwd(q, k, v, o, lse, dO, dq, dk, dv, workspace)
+    kr = _check_k_rot(k_rot, q, B, Hkv, N, d)
     scale = default_scale(d) if scale is None else float(scale)
     L = lib()
     cs, sn = _tables(cos, sin, N, d)
@@ -425,7 +445,7 @@ def attn_bwd_rope(q, k, v, o, lse, dO, cos=None, sin=None, causal: bool = True, 
         workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
     ls = [_layout(t) for t in (q, k, v, dq, dk, dv)]
     _check(L.attn_bwd_rope(dt, _code(o.dtype), _sptr(q), ctypes.byref(ls[0]), _sptr(k), ctypes.byref(ls[1]),
-                           _sptr(v), ctypes.byref(ls[2]), cs, sn, _ptr(o), _ptr(lse), _ptr(dO),
+                           _sptr(v), ctypes.byref(ls[2]), cs, sn, kr, _ptr(o), _ptr(lse), _ptr(dO),
                            _sptr(dq), ctypes.byref(ls[3]), _sptr(dk), ctypes.byref(ls[4]), _sptr(dv),
                            ctypes.byref(ls[5]), _ptr(workspace), _nbytes(workspace), B, Hq, Hkv, N, d,
                            int(bool(causal)), scale, _stream(q.device)))

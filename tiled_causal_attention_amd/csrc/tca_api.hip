@@ -10,7 +10,7 @@ using tca::AttnArgs;
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -144,17 +144,18 @@ attn_status check_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, co
     return ATTN_OK;
 }
 
-// q, k (rotated) and v into the contiguous staging copies, one launch
+// q, k (rotated; unless the rotated keys are already there) and v into the
+// contiguous staging copies, one launch
 hipError_t stage_qkv(const RopeWs& w, attn_dtype dtype, const void* q, const attn_layout* ql, const void* k,
                      const attn_layout* kl, const void* v, const attn_layout* vl, const float* cs, const float* sn,
-                     int B, int Hq, int Hkv, int N, int d, hipStream_t st) {
+                     int B, int Hq, int Hkv, int N, int d, bool with_k, hipStream_t st) {
     const int rot = cs ? 1 : 0;
     const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
     tca::CopyJobs jobs;
-    jobs.n = 3;
-    jobs.j[0] = tca::copy_job(q, ql ? *ql : cq, w.q, cq, B, Hq, N, d, rot);
-    jobs.j[1] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, rot);
-    jobs.j[2] = tca::copy_job(v, vl ? *vl : ck, w.v, ck, B, Hkv, N, d, 0);
+    jobs.n = 0;
+    jobs.j[jobs.n++] = tca::copy_job(q, ql ? *ql : cq, w.q, cq, B, Hq, N, d, rot);
+    if (with_k) jobs.j[jobs.n++] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, rot);
+    jobs.j[jobs.n++] = tca::copy_job(v, vl ? *vl : ck, w.v, ck, B, Hkv, N, d, 0);
     return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
 }
 
@@ -379,9 +380,9 @@ size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int
 
 attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, const attn_layout* q_layout,
                           const void* k, const attn_layout* k_layout, const void* v, const attn_layout* v_layout,
-                          const float* rope_cos, const float* rope_sin, void* o, float* lse, void* workspace,
-                          size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                          void* stream) {
+                          const float* rope_cos, const float* rope_sin, void* k_rot, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, void* stream) {
     attn_status s = check_sizes(dtype, out_dtype, B, Hq, Hkv, N, d, causal, scale);
     if (s != ATTN_OK) return s;
     if ((int64_t)B * N == 0) return ATTN_OK;
@@ -389,8 +390,10 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     if (s != ATTN_OK) return s;
     s = check_ptrs({o, lse, workspace});
     if (s != ATTN_OK) return s;
-    const RopeWs w = rope_ws(workspace, false, dtype, out_dtype, B, Hq, Hkv, N, d);
+    if (k_rot != nullptr && !aligned16(k_rot)) return ATTN_EINVAL;
+    RopeWs w = rope_ws(workspace, false, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
+    if (k_rot != nullptr) w.k = static_cast<char*>(k_rot);   // the rotated keys go to the caller's buffer
     hipStream_t st = (hipStream_t)stream;
     if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
         v_in_place(v, v_layout, Hkv, N, d)) {
@@ -404,7 +407,8 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         a.rope = &rq;
         return from_hip(tca::launch_fwd_mfma(a, st));
     }
-    hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
+    hipError_t e =
+        stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, true, st);
     if (e != hipSuccess) return ATTN_EHIP;
     const AttnArgs a = make_args(dtype, out_dtype, w.q, w.k, w.v, o, lse, nullptr, nullptr, nullptr, nullptr,
                                  nullptr, 0, B, Hq, Hkv, N, d, causal, scale);
@@ -413,8 +417,8 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
 
 attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q, const attn_layout* q_layout,
                           const void* k, const attn_layout* k_layout, const void* v, const attn_layout* v_layout,
-                          const float* rope_cos, const float* rope_sin, const void* o, const float* lse,
-                          const void* dO, void* dq, const attn_layout* dq_layout, void* dk,
+                          const float* rope_cos, const float* rope_sin, const void* k_rot, const void* o,
+                          const float* lse, const void* dO, void* dq, const attn_layout* dq_layout, void* dk,
                           const attn_layout* dk_layout, void* dv, const attn_layout* dv_layout, void* workspace,
                           size_t workspace_bytes, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                           void* stream) {
@@ -428,16 +432,21 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         return ATTN_EINVAL;
     s = check_ptrs({o, lse, dO, workspace});
     if (s != ATTN_OK) return s;
-    const RopeWs w = rope_ws(workspace, true, dtype, out_dtype, B, Hq, Hkv, N, d);
+    if (k_rot != nullptr && !aligned16(k_rot)) return ATTN_EINVAL;
+    RopeWs w = rope_ws(workspace, true, dtype, out_dtype, B, Hq, Hkv, N, d);
     if (workspace_bytes < w.total) return ATTN_EINVAL;
+    const bool rotate_k = k_rot == nullptr;   // else the forward's rotated keys are read back
+    if (!rotate_k) w.k = static_cast<char*>(const_cast<void*>(k_rot));
     hipStream_t st = (hipStream_t)stream;
     if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
         rows_aligned16(dq, dq_layout, elsize(out_dtype)) && v_in_place(v, v_layout, Hkv, N, d)) {
-        // fused: only k is staged (rotated). The dQ pass reads q through its strides,
-        // rotates it in registers (its fp16 copy for the dK/dV pass is rotated too), reads
-        // v in place and stores dq turned back through dq's strides; the dK/dV pass reads v
-        // in place and stores dk turned back, and dv, through their strides
-        if (stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
+        // fused: only k is staged (rotated), unless the forward's copy is given. The dQ
+        // pass reads q through its strides, rotates it in registers (its fp16 copy for
+        // the dK/dV pass is rotated too), reads v in place and stores dq turned back
+        // through dq's strides; the dK/dV pass reads v in place and stores dk turned
+        // back, and dv, through their strides
+        if (rotate_k && stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
+            return ATTN_EHIP;
         const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, v, v_layout, Hq, Hkv, N, d);
         const tca::KVRope rv = make_kvrope(v, v_layout, dk, dk_layout, dv, dv_layout, rope_cos, rope_sin, Hkv, N, d);
         AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, dO, dq, dk, dv, w.bwd, w.bwd_bytes, B, Hq, Hkv,
@@ -450,7 +459,8 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         a2.kvrope = &rv;
         return run_dkdv(a2, st);
     }
-    hipError_t e = stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, st);
+    hipError_t e =
+        stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, rotate_k, st);
     if (e != hipSuccess) return ATTN_EHIP;
     const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
     const void* o_in = o;
