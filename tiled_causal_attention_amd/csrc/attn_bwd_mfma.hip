@@ -79,24 +79,43 @@ __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32
     }
 }
 
+// The table values a lane needs to turn its dQ row back (ROPE): frequency
+// 32x + 8 a4 + 4h .. +3 of row qi for dim block x < D/64. Loaded on their own so
+// that the kernel can issue them before its last barrier.
+template <int D, bool ROPE>
+struct DqTab {
+    f32x4 c[D / 64][4], s[D / 64][4];
+    __device__ __forceinline__ void load(const QRope& rq, int qi, int h) {
+        if constexpr (ROPE) {
+            const float* cr = rq.cs + (size_t)qi * (D / 2);
+            const float* sr = rq.sn + (size_t)qi * (D / 2);
+#pragma unroll
+            for (int x = 0; x < D / 64; ++x)
+#pragma unroll
+                for (int a4 = 0; a4 < 4; ++a4) {
+                    c[x][a4] = *reinterpret_cast<const f32x4*>(cr + 32 * x + 8 * a4 + 4 * h);
+                    s[x][a4] = *reinterpret_cast<const f32x4*>(sr + 32 * x + 8 * a4 + 4 * h);
+                }
+        }
+    }
+};
+
 // Store one query row's dQ (val[x][a4] holds dims 32x + 8 a4 + 4h .. +3). ROPE: the
 // pairs (dim, dim + D/2) -- blocks x and x + D/64 of the same lane -- are turned
-// back by the transpose rotation at row position qi and written through rq's dq
-// strides; otherwise the row goes to `row` as it is.
+// back by the transpose rotation at row position qi (tab: that row's table values)
+// and written through rq's dq strides; otherwise the row goes to `row` as it is.
 template <int D, typename OT, bool ROPE>
-__device__ __forceinline__ void store_dq_row(OT* row, const f32x4 (&val)[D / 32][4], const QRope& rq, int b, int hq,
-                                             int qi, int h) {
+__device__ __forceinline__ void store_dq_row(OT* row, const f32x4 (&val)[D / 32][4], const QRope& rq,
+                                             const DqTab<D, ROPE>& tab, int b, int hq, int qi, int h) {
     constexpr int DB = D / 32;
     if constexpr (ROPE) {
         OT* dst = static_cast<OT*>(rq.dq) + b * rq.gb + hq * rq.gh + qi * rq.gn;
-        const float* cr = rq.cs + (size_t)qi * (D / 2);
-        const float* sr = rq.sn + (size_t)qi * (D / 2);
 #pragma unroll
         for (int x = 0; x < DB / 2; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4) {
                 const int i0 = 32 * x + 8 * a4 + 4 * h;
-                const f32x4 c = *reinterpret_cast<const f32x4*>(cr + i0), s = *reinterpret_cast<const f32x4*>(sr + i0);
+                const f32x4 c = tab.c[x][a4], s = tab.s[x][a4];
                 const f32x4 g1 = val[x][a4], g2 = val[x + DB / 2][a4];
                 store_out4(dst + i0, f32x4{g1[0] * c[0] + g2[0] * s[0], g1[1] * c[1] + g2[1] * s[1],
                                            g1[2] * c[2] + g2[2] * s[2], g1[3] * c[3] + g2[3] * s[3]});
@@ -301,6 +320,10 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         __syncthreads();
     }
 
+    // ROPE: the storing waves issue the loads of their row's table values first, so
+    // that they arrive during the copies and the key-half merge below
+    DqTab<D, ROPE> dtab;
+    if (ROPE && qok && khalf == 0) dtab.load(rq, qi, h);
     // key half 0 leaves fp16 copies of its Q and dO rows in the workspace for
     // the dK/dV phase, which copies them into LDS without conversion (stored
     // after the tile loop, where the writes overlap other workgroups' math)
@@ -324,7 +347,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                 for (int a4 = 0; a4 < 4; ++a4)
                     val[x][a4] = f32x4{dqa[x][4 * a4 + 0] * scale, dqa[x][4 * a4 + 1] * scale,
                                        dqa[x][4 * a4 + 2] * scale, dqa[x][4 * a4 + 3] * scale};
-            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, tm.b, hq, qi, h);
+            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, dtab, tm.b, hq, qi, h);
         }
     } else {
         // ---- sum the two key halves' partial dQ through LDS (the K buffers are free
@@ -350,7 +373,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
                     val[x][a4] = f32x4{(dqa[x][4 * a4 + 0] + o1[0]) * scale, (dqa[x][4 * a4 + 1] + o1[1]) * scale,
                                        (dqa[x][4 * a4 + 2] + o1[2]) * scale, (dqa[x][4 * a4 + 3] + o1[3]) * scale};
                 }
-            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, tm.b, hq, qi, h);
+            store_dq_row<D, OT, ROPE>(dq + (bh * N + qi) * D, val, rq, dtab, tm.b, hq, qi, h);
         }
     }
 }
