@@ -267,9 +267,10 @@ attn_status attn_fwd_naive(attn_dtype dtype, attn_dtype out_dtype,
                            void* stream);
 
 /* Workspace bytes attn_decode needs for these sizes: the per-split partial
- * outputs and log-sum-exps when the keys are split (nsplit * B*Hq*Nq * (d + 1)
- * floats, each part rounded up to 256 bytes), else 0. A function of the sizes
- * only; 0 for invalid sizes. */
+ * outputs and log-sum-exps when the keys are split into more ranges than one
+ * workgroup merges itself (nsplit * B*Hq*Nq * (d + 1) floats, each part rounded
+ * up to 256 bytes), else 0. A function of the sizes and `dtype` only; 0 for
+ * invalid sizes. */
 size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /* Few-query attention over a key/value cache (decode): o and lse for Nq query
@@ -283,11 +284,15 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
  *   j <= Nk - Nq + i (bottom-right alignment); causal = 0 sees all Nk keys.
  *   With Nq = Nk the result is attn_fwd's (up to rounding order).
  *   GQA head map, scale and the definitions of o and lse as for attn_fwd.
- * The keys are split into ranges processed in parallel; each writes a partial
- * output and its log-sum-exp into `workspace` (at least
+ * The keys are split into ranges processed in parallel, whose partial outputs
+ * are merged through their log-sum-exps. When a call has at least 256 (batch,
+ * KV head, query-row chunk) groups and up to 16 ranges per group (8 when a wave
+ * holds 8 query rows, or 4 float32 ones), a group's ranges are the waves of one
+ * workgroup and merge in on-chip memory: one launch, no workspace. Otherwise each range writes its
+ * partial output and log-sum-exp into `workspace` (at least
  * attn_decode_workspace_bytes(...) bytes of device memory, 16-byte aligned;
- * NULL allowed when that is 0), and a second kernel merges them through the
- * log-sum-exps. Arithmetic is float32 on the vector units for every dtype.
+ * NULL allowed when that is 0) and a second kernel merges them. Arithmetic is
+ * float32 on the vector units for every dtype.
  * Sizes: B >= 0, Nq >= 0 (B*Nq == 0 is a no-op), Nq <= Nk, Hq % Hkv == 0,
  * d in {16, 32, 64, 128}, (Nk+256)*d*4 < 2^31; otherwise ATTN_EINVAL (or
  * ATTN_EUNSUPPORTED for d). Results are bitwise reproducible. */

@@ -295,13 +295,20 @@ def test_decode_noops_and_workspace(L):
     assert dec(L, B=0, **nul) == OK
     assert dec(L, Nq=0, **nul) == OK
     assert dec(L, B=0, causal=3, **nul) == EINVAL
-    # one split: no workspace; many splits: partial outputs and LSEs, 256-byte parts
+    # one split: no workspace; more: partial outputs and LSEs, 256-byte parts, unless
+    # the call has >= 256 row groups of <= 16 splits each, merged inside one workgroup
     assert L.attn_decode_workspace_bytes(BF16, 1, 2, 1, 1, 64, 64) == 0
-    n = L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 1, 1024, 64)
+    n = L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 1, 1024, 64)              # 32 groups of 16 splits
     rows = 8 * 12
     assert n > 0 and n % 256 == 0
     nsplit = round(n / (rows * 64 * 4 + rows * 4))
+    assert nsplit == 16
     assert n == ((nsplit * rows * 64 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
+    assert L.attn_decode_workspace_bytes(BF16, 64, 12, 4, 1, 1024, 64) == 0     # 256 groups of 16 splits
+    # float32 queries of 4 rows: at most 8 splits per workgroup
+    assert L.attn_decode_workspace_bytes(F32, 128, 8, 2, 1, 400, 64) == 0        # 7 splits
+    assert L.attn_decode_workspace_bytes(F32, 128, 8, 2, 1, 600, 64) > 0         # 10 splits
+    assert L.attn_decode_workspace_bytes(BF16, 128, 8, 2, 1, 600, 64) == 0
     assert L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 2, 1, 64) == 0   # invalid: Nq > Nk
 
 

@@ -82,6 +82,12 @@ SHAPES = [
     (1, 4, 2, 1, 4000, 32, "bf16"),    # 63 splits: the merge splits each row's columns
     (1, 4, 1, 1, 5000, 128, "f32"),    # 79 splits, float32 inputs
     (1, 4, 1, 1, 16384, 64, "bf16"),   # 256 splits of 64 keys: the most a row can have
+    # >= 256 row groups: each group's splits merged in one workgroup (up to 16 waves;
+    # 8 for 8-row and float32 4-row waves)
+    (64, 12, 4, 1, 1024, 64, "bf16"),  # 16 splits of 4 rows
+    (128, 8, 2, 1, 400, 64, "f32"),    # 7 splits of 4 float32 rows
+    (256, 8, 1, 1, 512, 128, "bf16"),  # 8 splits of 8 rows
+    (16, 2, 2, 70, 200, 64, "bf16"),   # Nq = 70 > 64: early rows see no key of the last split
 ]
 
 

@@ -60,9 +60,10 @@ def test_fwd_bwd_graph_replays_match_eager(name):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("name", ["decode_wide_d128", "decode_gpt2_gqa"])
+@pytest.mark.parametrize("name", ["decode_wide_d128", "decode_gpt2_gqa", "decode_gpt2_gqa_b64"])
 def test_decode_graph_replays_match_eager(name):
-    # wide: 128 key splits per row (column-block merge); GPT-2-small: 16 (whole-row merge)
+    # wide: 128 key splits per row (column-block merge); GPT-2-small: 16 (whole-row merge);
+    # batch 64: 256 row groups, each group's 16 splits merged inside its workgroup
     s = workloads.DECODE_CONFIGS[name]
     q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
     o = torch.empty((s.B, s.Hq, s.Nq, s.d), device="cuda")

@@ -23,10 +23,13 @@ def _gpu():
     yield
 
 
-def _pair(s, seed):
+def _pair(s, seed, scratch=True):
     q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s, seed))
     ws_bytes = int(tca.lib().attn_decode_workspace_bytes(tca.ATTN_BF16, s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d))
-    assert 0 < ws_bytes <= tca.DECODE_SCRATCH_BYTES, ws_bytes
+    if scratch:
+        assert 0 < ws_bytes <= tca.DECODE_SCRATCH_BYTES, ws_bytes
+    else:
+        assert ws_bytes == 0, ws_bytes
     o_ref, l_ref = tca.attn_decode(q, k, v, causal=bool(s.causal), scale=s.scale)
     o = torch.full_like(o_ref, float("nan"))
     lse = torch.full_like(l_ref, float("nan"))
@@ -36,11 +39,12 @@ def _pair(s, seed):
 
 
 def test_noalloc_matches_workspace_decode_twice():
-    wide = workloads.DECODE_CONFIGS["decode_wide_d128"]       # 128 splits of 64 keys, d = 128
-    small = workloads.DECODE_CONFIGS["decode_gpt2_gqa"]       # fewer rows, splits and columns
+    wide = workloads.DECODE_CONFIGS["decode_wide_d128"]       # 128 splits of 64 keys, d = 128: 4.2 MB
     big_first = workloads.make_decode_shape(wide.B, wide.Hq, wide.Hkv, 2, wide.Nk, wide.d)   # 8 MiB of partials
-    for s, seed in ((big_first, 31), (small, 32)):
+    small = workloads.DECODE_CONFIGS["decode_gpt2_gqa"]       # fewer rows, splits and columns
+    merged = workloads.make_decode_shape(64, 12, 4, 1, 1024, 64)   # splits merged in workgroups: no scratch
+    for s, seed, scratch in ((big_first, 31, True), (small, 32, True), (merged, 33, False)):
         print(f"[no-alloc] {s.B, s.Hq, s.Hkv, s.Nq, s.Nk, s.d}", flush=True)
-        (o, lse), (o_ref, l_ref) = _pair(s, seed)
+        (o, lse), (o_ref, l_ref) = _pair(s, seed, scratch)
         assert torch.equal(o, o_ref), s
         assert torch.equal(lse, l_ref), s

@@ -18,7 +18,11 @@
 //    row chunk, split) item and the splits run in parallel. Each writes a
 //    normalised partial output and its LSE; a second kernel merges the splits
 //    through the LSEs: LSE = log sum_s e^LSE_s, O = sum_s e^(LSE_s - LSE) O_s.
-//    A single split writes the result directly.
+//    A single split writes the result directly. With at most 16 splits (8 for
+//    8-row waves) and at least 256 (batch, KV head, row chunk) groups, the splits
+//    of a group are instead the waves of one workgroup, which merge through LDS:
+//    one launch and no workspace. With fewer groups the CUs would not all be
+//    streaming, so the splits stay spread over the chip.
 //  * Lane layout: lane = CPR * slot + c, CPR = d / 8. A slot is one key, c is an
 //    8-element chunk of its row, so one load instruction covers 64/CPR
 //    consecutive whole K (or V) rows: 1 KB of contiguous bf16 per wave. Each
@@ -43,6 +47,13 @@ constexpr int kUnroll = 2;       // keys per slot per batch (two batches in flig
 constexpr float kTau = 8.f;      // lazy-rescale threshold, log2 units
 constexpr int kTargetWaves = 4096;   // work items aimed for (4 per SIMD)
 constexpr int kMinSplitKeys = 64;    // keys per split at least
+// splits merged inside one workgroup at most (its waves): 16 waves of at most 128
+// registers share a CU; waves with more registers (8 rows; 4 rows of float32
+// queries) go 8 to a workgroup
+template <typename T, int RM>
+constexpr int kFusedWaves = (RM == 8 || (RM == 4 && std::is_same<T, float>::value)) ? 8 : 16;
+inline int fused_waves(int rm, bool in32) { return (rm == 8 || (rm == 4 && in32)) ? 8 : 16; }
+constexpr long long kFusedMinGroups = 256;   // workgroups a merged-in-LDS launch needs at least (one per CU)
 }  // namespace dec
 
 // DPP lane moves within rows of 16 lanes (gfx9 encodings).
@@ -96,26 +107,28 @@ template <> struct Chunk<float> {
     }
 };
 
-// Work item (one wave): item = ((unit * nrc) + rc) * nsplit + split, unit = b * Hkv + hkv.
-// Rows of the item: rho = rc * RM + r < G * Nq, query head hkv * G + rho / Nq,
-// query row rho % Nq. Keys: [split * split_len, min(Nk, (split + 1) * split_len)).
-// nsplit == 1: o and lse are written; otherwise opart [nsplit][B Hq Nq][D] (O_s,
-// normalised) and lpart [nsplit][B Hq Nq] (LSE_s in log2 units, -inf when the
-// split holds no visible key of the row).
-template <typename T, typename OT, int D, int RM>
-__global__ void __launch_bounds__(64 * dec::kWaves)
-decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-                    OT* __restrict__ o, float* __restrict__ lse, float* __restrict__ opart,
-                    float* __restrict__ lpart, int Hq, int Hkv, int Nq, int Nk, int causal, float scale,
-                    int nrc, int nsplit, int split_len, int nitems, int nrows) {
+// One wave's split: keys [split * split_len, min(Nk, (split + 1) * split_len)) of
+// unit = b * Hkv + hkv for rows rho = rc * RM + r < G * Nq (query head hkv * G +
+// rho / Nq, query row rho % Nq). On return the lanes of slot 0 hold, per row, the
+// running max m (log2 units), the sum l and the unnormalised output columns acc
+// (lane c: columns 8c .. 8c + 7); grow is the row's global index (b, hq, i) and ok
+// whether the row exists.
+template <int RM>
+struct SplitState {
+    float m[RM], l[RM], acc[RM][8];
+    size_t grow[RM];
+    bool ok[RM];
+};
+
+template <typename T, int D, int RM>
+__device__ __forceinline__ void decode_split_wave(SplitState<RM>& out, const T* __restrict__ q,
+                                                  const T* __restrict__ k, const T* __restrict__ v, int Hq, int Hkv,
+                                                  int Nq, int Nk, int causal, float scale, int unit, int rc, int split,
+                                                  int split_len) {
     using namespace dec;
     constexpr int CPR = D / 8;        // lanes per key row
     constexpr int KS = 64 / CPR;      // key slots per wave
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= nitems) return;       // whole waves only; the kernel has no barrier
-    const int split = item % nsplit, rest = item / nsplit;
-    const int rc = rest % nrc, unit = rest / nrc;
     const int b = unit / Hkv, hkv = unit % Hkv;
     const int G = Hq / Hkv, R = G * Nq;
     const int slot = lane / CPR, c = lane % CPR;
@@ -149,8 +162,8 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     float qr[RM][8];
     u32x4 qp2[RM];
     int lim[RM];          // keys j < lim[r] are visible to row r in this split
-    size_t grow[RM];      // global row index (b, hq, i) of row r
-    bool ok[RM];
+    size_t (&grow)[RM] = out.grow;   // global row index (b, hq, i) of row r
+    bool (&ok)[RM] = out.ok;
     int kend = k0;        // keys this wave must visit
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
@@ -173,7 +186,9 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
         }
     }
 
-    float m[RM], l[RM], acc[RM][8];
+    float (&m)[RM] = out.m;
+    float (&l)[RM] = out.l;
+    float (&acc)[RM][8] = out.acc;
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
         m[r] = -0x1p100f;   // finite and far below any score: the first rescale factor is 0
@@ -273,7 +288,33 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
             m[r] = mn;
         }
     }
+}
 
+// Work item (one wave): item = ((unit * nrc) + rc) * nsplit + split, unit = b * Hkv + hkv.
+// nsplit == 1: o and lse are written; otherwise opart [nsplit][B Hq Nq][D] (O_s,
+// normalised) and lpart [nsplit][B Hq Nq] (LSE_s in log2 units, -inf when the
+// split holds no visible key of the row).
+template <typename T, typename OT, int D, int RM>
+__global__ void __launch_bounds__(64 * dec::kWaves)
+decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                    OT* __restrict__ o, float* __restrict__ lse, float* __restrict__ opart,
+                    float* __restrict__ lpart, int Hq, int Hkv, int Nq, int Nk, int causal, float scale,
+                    int nrc, int nsplit, int split_len, int nitems, int nrows) {
+    using namespace dec;
+    constexpr int CPR = D / 8;
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * kWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= nitems) return;       // whole waves only; the kernel has no barrier
+    const int split = item % nsplit, rest = item / nsplit;
+    const int rc = rest % nrc, unit = rest / nrc;
+    SplitState<RM> st;
+    decode_split_wave<T, D, RM>(st, q, k, v, Hq, Hkv, Nq, Nk, causal, scale, unit, rc, split, split_len);
+    const int slot = lane / CPR, c = lane % CPR;
+    const float (&m)[RM] = st.m;
+    const float (&l)[RM] = st.l;
+    const float (&acc)[RM][8] = st.acc;
+    const size_t (&grow)[RM] = st.grow;
+    const bool (&ok)[RM] = st.ok;
     if (slot != 0) return;
 #pragma unroll
     for (int r = 0; r < RM; ++r) {
@@ -294,6 +335,62 @@ decode_split_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
             *reinterpret_cast<f32x4*>(opart + prow * D + 8 * c + 4) = hi4;
             if (c == 0) lpart[prow] = l2;
         }
+    }
+}
+
+// All nsplit splits of one (batch, KV head, row chunk) in one workgroup, wave w
+// taking split w: each wave leaves its rows' normalised partial output and LSE
+// (log2 units) in LDS, then the workgroup merges them as the merge kernel does,
+// thread t taking column t % D of row t / D: LSE = log2 sum_w 2^LSE_w,
+// O = sum_w 2^(LSE_w - LSE) O_w, with the splits added in order. Split 0 holds key
+// 0, visible to every row, so the maximum is finite. Launched with 64 * nsplit
+// threads, nsplit <= kFusedWaves<T, RM>.
+template <typename T, typename OT, int D, int RM>
+__global__ void __launch_bounds__((64 * dec::kFusedWaves<T, RM>))
+decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+                    OT* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk, int causal,
+                    float scale, int nrc, int nsplit, int split_len) {
+    using namespace dec;
+    constexpr int MW = kFusedWaves<T, RM>;
+    constexpr int CPR = D / 8;
+    __shared__ __attribute__((aligned(16))) float po[MW][RM][D];
+    __shared__ float pl[MW][RM];
+    const int lane = threadIdx.x & 63;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rc = blockIdx.x % nrc, unit = blockIdx.x / nrc;
+    SplitState<RM> st;
+    decode_split_wave<T, D, RM>(st, q, k, v, Hq, Hkv, Nq, Nk, causal, scale, unit, rc, w, split_len);
+    const int slot = lane / CPR, c = lane % CPR;
+    if (slot == 0) {
+#pragma unroll
+        for (int r = 0; r < RM; ++r) {
+            const bool any = st.l[r] > 0.f;
+            const float inv = any ? 1.f / st.l[r] : 0.f;
+            *reinterpret_cast<f32x4*>(&po[w][r][8 * c]) =
+                f32x4{st.acc[r][0] * inv, st.acc[r][1] * inv, st.acc[r][2] * inv, st.acc[r][3] * inv};
+            *reinterpret_cast<f32x4*>(&po[w][r][8 * c + 4]) =
+                f32x4{st.acc[r][4] * inv, st.acc[r][5] * inv, st.acc[r][6] * inv, st.acc[r][7] * inv};
+            if (c == 0) pl[w][r] = any ? st.m[r] + __log2f(st.l[r]) : -INFINITY;
+        }
+    }
+    __syncthreads();
+    const int G = Hq / Hkv, R = G * Nq;
+    const int b = unit / Hkv, hkv = unit % Hkv;
+    for (int t = threadIdx.x; t < RM * D; t += 64 * nsplit) {
+        const int r = t / D, col = t % D;
+        const int rho = rc * RM + r;
+        if (rho >= R) continue;
+        const size_t grow = ((size_t)b * Hq + hkv * G + rho / Nq) * Nq + rho % Nq;
+        float mx = pl[0][r];
+        for (int sidx = 1; sidx < nsplit; ++sidx) mx = vmax(mx, pl[sidx][r]);
+        float sum = 0.f, a = 0.f;
+        for (int sidx = 0; sidx < nsplit; ++sidx) {
+            const float wgt = fast_exp2(pl[sidx][r] - mx);
+            sum += wgt;
+            a = fmaf(wgt, po[sidx][r][col], a);
+        }
+        store_out1(o + grow * D + col, a * (1.f / sum));
+        if (col == 0) lse[grow] = (mx + __log2f(sum)) * kLn2;
     }
 }
 
@@ -368,7 +465,7 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
 }
 
 // ---------------------------------------------------------------- host side
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32) {
     DecodePlan p;
     const int R = (Hq / Hkv) * Nq;
     p.rm = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
@@ -383,19 +480,29 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
     if (p.split_len < 64) p.split_len = 64;
     p.nsplit = (int)(((long long)Nk + p.split_len - 1) / p.split_len);
     if (p.nsplit < 1) p.nsplit = 1;
+    // merged in the workgroup when there are enough workgroups to fill the CUs: with
+    // fewer, one CU streaming a whole row chunk's splits is slower than splits spread
+    // over the chip plus a merge kernel
+    p.fused = p.nsplit > 1 && p.nsplit <= dec::fused_waves(p.rm, in32) && items0 >= dec::kFusedMinGroups;
     (void)d;
     return p;
 }
 
-size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, d);
-    if (p.nsplit <= 1) return 0;
+size_t decode_workspace_size(bool in32, int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    const DecodePlan p = decode_plan(B, Hq, Hkv, Nq, Nk, d, in32);
+    if (p.nsplit <= 1 || p.fused) return 0;
     const size_t rows = (size_t)B * Hq * Nq;
     return ws_round((size_t)p.nsplit * rows * d * sizeof(float)) + ws_round((size_t)p.nsplit * rows * sizeof(float));
 }
 
 template <typename T, typename OT, int D, int RM>
 static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    if (p.fused) {   // one workgroup per (batch, KV head, row chunk), one wave per split
+        hipLaunchKernelGGL((decode_fused_kernel<T, OT, D, RM>), dim3((unsigned)(a.B * a.Hkv * p.nrc)),
+                           dim3(64 * p.nsplit), 0, st, (const T*)a.q, (const T*)a.k, (const T*)a.v, (OT*)a.o, a.lse,
+                           a.Hq, a.Hkv, a.Nq, a.Nk, a.causal, a.scale, p.nrc, p.nsplit, p.split_len);
+        return hipGetLastError();
+    }
     const int nitems = a.B * a.Hkv * p.nrc * p.nsplit;
     const int nrows = a.B * a.Hq * a.Nq;
     float* opart = nullptr;
@@ -472,8 +579,8 @@ hipError_t decode_scratch(void** out) {
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-    const DecodePlan p = decode_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d);
     const bool in32 = a.dtype == ATTN_F32, out32 = a.out_dtype == ATTN_F32;
+    const DecodePlan p = decode_plan(a.B, a.Hq, a.Hkv, a.Nq, a.Nk, a.d, in32);
     if (in32) return out32 ? launch_decode_d<float, float>(a, p, st) : launch_decode_d<float, bf16_t>(a, p, st);
     return out32 ? launch_decode_d<bf16_t, float>(a, p, st) : launch_decode_d<bf16_t, bf16_t>(a, p, st);
 }

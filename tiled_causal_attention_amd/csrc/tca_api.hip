@@ -509,9 +509,9 @@ attn_status attn_fwd_naive(attn_dtype dtype, attn_dtype out_dtype, const void* q
 }
 
 size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int Nq, int Nk, int d) {
-    (void)dtype;
+    if (!known_dtype(dtype)) return 0;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Nq < 1 || Nk < Nq || !supported_d(d)) return 0;
-    return tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+    return tca::decode_workspace_size(dtype == ATTN_F32, B, Hq, Hkv, Nq, Nk, d);
 }
 
 attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype, const void* q, const void* k, const void* v,
@@ -520,7 +520,7 @@ attn_status attn_decode(attn_dtype dtype, attn_dtype out_dtype, const void* q, c
     bool noop = false;
     attn_status s = check_decode(dtype, out_dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, &noop);
     if (s != ATTN_OK || noop) return s;
-    const size_t need = tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+    const size_t need = tca::decode_workspace_size(dtype == ATTN_F32, B, Hq, Hkv, Nq, Nk, d);
     if (need > 0 && (workspace_bytes < need || workspace == nullptr || !aligned16(workspace))) return ATTN_EINVAL;
     const tca::DecodeArgs a =
         decode_args(dtype, out_dtype, q, k, v, o, lse, workspace, B, Hq, Hkv, Nq, Nk, d, causal, scale);
@@ -533,7 +533,7 @@ attn_status attn_decode_noalloc(attn_dtype dtype, attn_dtype out_dtype, const vo
     bool noop = false;
     attn_status s = check_decode(dtype, out_dtype, q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, causal, scale, &noop);
     if (s != ATTN_OK || noop) return s;
-    const size_t need = tca::decode_workspace_size(B, Hq, Hkv, Nq, Nk, d);
+    const size_t need = tca::decode_workspace_size(dtype == ATTN_F32, B, Hq, Hkv, Nq, Nk, d);
     if (need > tca::kDecodeScratchBytes) return ATTN_ESCRATCH;
     void* ws = nullptr;
     if (need > 0 && tca::decode_scratch(&ws) != hipSuccess) return ATTN_EHIP;

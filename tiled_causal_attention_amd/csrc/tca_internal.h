@@ -98,9 +98,10 @@ struct DecodeArgs {
 // splits of split_len keys (a multiple of 64).
 struct DecodePlan {
     int rm, nrc, nsplit, split_len;
+    bool fused;   // the splits of a row chunk are the waves of one workgroup, merged in LDS
 };
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d);
-size_t decode_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32);
+size_t decode_workspace_size(bool in32, int B, int Hq, int Hkv, int Nq, int Nk, int d);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 // Size of the fixed device array behind attn_decode_noalloc, and its address on
 // the current device (looked up on the first call per device, then cached).

@@ -136,6 +136,8 @@ class DecodeShape:
 DECODE_CONFIGS: Dict[str, DecodeShape] = {
     "decode_gpt2_gqa": DecodeShape("decode_gpt2_gqa", 8, 12, 4, 1, 1024, 64, "bf16", 2001),
     "decode_wide_d128": DecodeShape("decode_wide_d128", 4, 16, 4, 1, 8192, 128, "bf16", 2002),
+    # a serving batch of 64 sequences on the GPT-2-small GQA shape
+    "decode_gpt2_gqa_b64": DecodeShape("decode_gpt2_gqa_b64", 64, 12, 4, 1, 1024, 64, "bf16", 2003),
 }
 
 
