@@ -82,6 +82,7 @@ SHAPES = [
     (1, 4, 2, 1, 4000, 32, "bf16"),    # 63 splits: the merge splits each row's columns
     (1, 4, 1, 1, 5000, 128, "f32"),    # 79 splits, float32 inputs
     (1, 4, 1, 1, 16384, 64, "bf16"),   # 256 splits of 64 keys: the most a row can have
+    (1, 2, 1, 1, 3000, 16, "bf16"),    # 47 splits at d = 16: the 256-thread whole-row merge
     # >= 256 row groups: each group's splits merged in one workgroup (up to 16 waves;
     # 8 for 8-row and float32 4-row waves)
     (64, 12, 4, 1, 1024, 64, "bf16"),  # 16 splits of 4 rows
