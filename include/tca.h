@@ -195,18 +195,23 @@ size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int
  * are written as by attn_fwd. With bfloat16 inputs, d in {64, 128}, tables,
  * and q and v rows starting on 16-byte boundaries (v rows at least d elements
  * apart), the matrix-core forward reads q through its strides and rotates it in
- * registers and reads v in place; only k is rotated (rounded to `dtype`) into a
- * contiguous copy in `workspace` (at least attn_fwd_rope_workspace_bytes), once
- * for every query tile that reads it. Otherwise the rotated q, k and a
- * contiguous v are staged there and attn_fwd's kernels run on them. Pointers to
+ * registers and reads v in place; only k is rotated into a contiguous copy in
+ * `workspace` (at least attn_fwd_rope_workspace_bytes), once for every query tile
+ * that reads it. On that path the rotated q and k are rounded to fp16 (11-bit
+ * significand; |x| < 65504) and Q*K^T is an fp16 product, so the rotation adds
+ * an eighth of an input rounding. Otherwise the rotated q, k (rounded to
+ * `dtype`) and a contiguous v are staged there and attn_fwd's kernels run on
+ * them. Pointers to
  * strided tensors need element alignment only; o and lse as for attn_fwd.
  * Strides must be >= 0 and the caller's buffers must hold every addressed
  * element.
- * k_rot: NULL, or device memory for B*Hkv*N*d elements of `dtype`, 16-byte
- * aligned. The rotated keys (k itself without tables), contiguous [B, Hkv, N, d]
- * and rounded to `dtype`, are then written there instead of into `workspace`,
- * on every path, so that a training step can keep them as a saved activation and
- * hand them to attn_bwd_rope, which then skips its own rotation of k. The
+ * k_rot: NULL, or device memory for B*Hkv*N*d elements of `dtype`'s size (2
+ * bytes for bfloat16, 4 for float32), 16-byte aligned. The rotated keys (k itself
+ * without tables), contiguous [B, Hkv, N, d] in the precision the path computes
+ * with (fp16 on the matrix-core path, else `dtype`), are then written there
+ * instead of into `workspace`, on every path, so that a training step can keep
+ * them as a saved activation and hand them to attn_bwd_rope, which then skips its
+ * own rotation of k. The buffer's contents are for attn_bwd_rope only. The
  * workspace size does not change. */
 attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype,
                           const void* q, const attn_layout* q_layout,

@@ -1,5 +1,5 @@
-"""GPU parity on seeded random shapes: fwd + bwd and decode against the float64
-oracle, through the C ABI.
+"""GPU parity on seeded random shapes: fwd + bwd, rotary fwd + bwd and decode
+against the float64 oracle, through the C ABI.
 
 The cases are drawn once from a fixed seed, over everything the entry points
 accept and the kernels branch on: batch, GQA group (1 to 6 query heads per KV
@@ -117,4 +117,59 @@ def test_random_decode(case):
     torch.cuda.synchronize()
     ro, rl = oracle.attn_decode(q, k, v, causal, scale)
     for name, got, ref in (("o", o, ro), ("lse", lse, rl)):
+        _check(name, got, ref, dtype, ctx)
+
+
+def _rope_cases(n=12, seed=20262):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([16, 32, 64, 128], p=[0.15, 0.15, 0.4, 0.3]))
+        dtype = "f32" if rng.random() < 0.25 else "bf16"
+        Hkv = int(rng.integers(1, 3))
+        G = int(rng.choice([1, 2, 3, 4]))
+        B = int(rng.integers(1, 3))
+        N = int(rng.choice(_N_EDGE)) if rng.random() < 0.5 else int(rng.integers(1, 400))
+        layout = str(rng.choice(["fused", "odd"]))
+        keep_k = bool(rng.random() < 0.5)
+        causal = int(rng.random() < 0.7)
+        scale = _scale(rng, d)
+        if layout == "odd" and dtype == "bf16":
+            # the staged path rounds the rotated q, k to bfloat16 (an input-sized
+            # rounding whose effect grows with the scores): scales up to 1/sqrt(d)
+            scale = float(np.float32(math.copysign(min(abs(scale), 1.0 / math.sqrt(d)), scale)))
+        out.append((i, B, G * Hkv, Hkv, N, d, dtype, causal, scale, layout, keep_k, 7000 + i))
+    return out
+
+
+@pytest.mark.parametrize("case", _rope_cases(), ids=lambda c: f"rope{c[0]}")
+def test_random_rope(case):
+    # rotary q/k on views of one fused projection buffer (16-byte aligned rows) or on
+    # rows d + 1 elements apart starting one element in (the staged path), with or
+    # without the forward's rotated keys kept for the backward
+    i, B, Hq, Hkv, N, d, dtype, causal, scale, layout, keep_k, seed = case
+    ctx = f"case {i}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} {dtype} causal={causal} scale={scale:.4f} {layout} k_rot={keep_k}"
+    print(f"[random rope] {ctx}", flush=True)
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype=dtype, seed=seed, causal=causal)
+    q, k, v, do = workloads.make_inputs(s)
+    cos, sin = workloads.rope_tables(N, d, base=500.0)
+    if layout == "fused":
+        buf = torch.empty((B, N, Hq + 2 * Hkv, d), dtype=q.dtype, device="cuda")
+        views = [buf[:, :, :Hq], buf[:, :, Hq:Hq + Hkv], buf[:, :, Hq + Hkv:]]
+        qv, kv, vv = (x.permute(0, 2, 1, 3) for x in views)
+        qv.copy_(q), kv.copy_(k), vv.copy_(v)
+    else:
+        def odd(t):
+            b = torch.zeros(t.shape[:3] + (d + 1,), dtype=t.dtype, device="cuda")
+            b[..., 1:].copy_(t.cuda())
+            return b[..., 1:]
+        qv, kv, vv = odd(q), odd(k), odd(v)
+    kr = torch.empty((B, Hkv, N, d), dtype=q.dtype, device="cuda") if keep_k else None
+    cd, sd = cos.cuda(), sin.cuda()
+    o, lse = tca.attn_fwd_rope(qv, kv, vv, cd, sd, causal=bool(causal), scale=scale, k_rot=kr)
+    dq, dk, dv = tca.attn_bwd_rope(qv, kv, vv, o, lse, do.cuda(), cd, sd, causal=bool(causal), scale=scale, k_rot=kr)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd_rope(q, k, v, cos, sin, causal, scale)
+    rq, rk, rv = oracle.attn_bwd_rope(q, k, v, do, cos, sin, causal, scale)
+    for name, got, ref in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check(name, got, ref, dtype, ctx)

@@ -378,10 +378,13 @@ def _tables(cos, sin, N, d):
 
 
 def _check_k_rot(k_rot, q, B, Hkv, N, d):
-    """k_rot: None or a contiguous tensor of q's dtype and device holding [B, Hkv, N, d]."""
+    """k_rot: None or a contiguous [B, Hkv, N, d] tensor on q's device with q's element
+    size (bfloat16 or float16 storage for bfloat16 inputs, float32 for float32). The
+    library keeps the rotated keys there in its own precision (fp16 on the
+    matrix-core path), for attn_bwd_rope."""
     if k_rot is None:
         return None
-    _expect(k_rot, "k_rot", (B, Hkv, N, d), (q.dtype,))
+    _expect(k_rot, "k_rot", (B, Hkv, N, d), (q.dtype, torch.float16) if q.dtype == torch.bfloat16 else (q.dtype,))
     _same_device(q, k_rot=k_rot)
     return _ptr(k_rot)
 
@@ -392,8 +395,9 @@ def attn_fwd_rope(q, k, v, cos=None, sin=None, causal: bool = True, scale: Optio
     """Forward with rotary position embedding of q and k (rotate-half pairing; cos,
     sin: [N, d/2] float32 tables, or both None) on [B, H, N, d] views with any
     strides (e.g. slices of one fused QKV projection). Returns (o, lse) like attn_fwd.
-    k_rot: optional contiguous [B, Hkv, N, d] tensor of q's dtype that receives the
-    rotated keys, to be passed to attn_bwd_rope (which then does not rotate k again)."""
+    k_rot: optional contiguous [B, Hkv, N, d] tensor with q's element size that receives
+    the rotated keys (fp16 on the matrix-core path), to be passed to attn_bwd_rope
+    (which then does not rotate k again)."""
     B, Hq, Hkv, N, d = _check_qkv(q, k, v)
     kr = _check_k_rot(k_rot, q, B, Hkv, N, d)
     scale = default_scale(d) if scale is None else float(scale)

@@ -65,16 +65,18 @@ __device__ __forceinline__ void bwd_load_kv(u32x4 (&kreg)[KCH], u32x4 (&vreg)[KC
     }
 }
 
-// Registers -> LDS: K converted to fp16 rows, V kept as bf16 rows. kdst/vdst
-// point at this thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8)));
-// chunk u sits T u / (D/8) rows further down (T threads).
-template <int D, int KCH>
+// Registers -> LDS: K as fp16 rows (converted from bf16, or as it is when KF16:
+// the rotated keys come in fp16), V kept as bf16 rows. kdst/vdst point at this
+// thread's chunk 0 (row tid / (D/8), column 8 (tid % (D/8))); chunk u sits
+// T u / (D/8) rows further down (T threads).
+template <int D, int KCH, bool KF16>
 __device__ __forceinline__ void bwd_store_kv(const u32x4 (&kreg)[KCH], const u32x4 (&vreg)[KCH],
                                              _Float16* kdst, bf16_t* vdst) {
     constexpr int ROWS_PER_U = bwdq::kThreads<D> / (D / 8);
 #pragma unroll
     for (int u = 0; u < KCH; ++u) {
-        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::kPad<D>)) = bf16x8_to_f16x8(kreg[u]);
+        *reinterpret_cast<u32x4*>(kdst + u * ROWS_PER_U * (D + bwdq::kPad<D>)) =
+            KF16 ? kreg[u] : bf16x8_to_f16x8(kreg[u]);
         *reinterpret_cast<u32x4*>(vdst + u * ROWS_PER_U * (D + bwdq::kPad<D>)) = vreg[u];
     }
 }
@@ -131,9 +133,10 @@ __device__ __forceinline__ void store_dq_row(OT* row, const f32x4 (&val)[D / 32]
 }
 
 // OT: element type of o (read) and dq (written): float32 or bfloat16.
-// ROPE: Q is read through rq's strides and rotated in registers (so the fp16 Q copy
-// left for the dK/dV pass is rotated too; K holds the rotated keys), and dQ is
-// turned back by the transpose rotation and stored through rq's dq strides.
+// ROPE: Q is read through rq's strides and rotated in registers into fp16 (so the
+// fp16 Q copy left for the dK/dV pass is rotated too; K holds the rotated keys in
+// fp16), and dQ is turned back by the transpose rotation and stored through rq's dq
+// strides.
 template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(bwdq::kThreads<D>, (D == 64) ? 3 : 2)
 bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -211,7 +214,8 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
         if constexpr (ROPE) rope_rotate_q<D>(qraw, qtab);
 #pragma unroll
         for (int c = 0; c < DC; ++c) {
-            const u32x4 qh16 = bf16x8_to_f16x8(apply_qsign(qraw[c], sc));
+            // the rotated Q is fp16 already
+            const u32x4 qh16 = ROPE ? apply_qsign(qraw[c], sc) : bf16x8_to_f16x8(apply_qsign(qraw[c], sc));
             qb[c] = qok ? __builtin_bit_cast(f16x8, qh16) : f16x8{};
             db[c] = qok ? __builtin_bit_cast(bf16x8, dvr[c]) : bf16x8{};
         }
@@ -254,7 +258,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
     const int st_off = (tid / CPR) * LD + (tid % CPR) * 8;           // LDS slot of chunk 0 (elements)
     constexpr int TBUF = BC * LD;                                      // elements per LDS tile buffer
 
-    bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
+    bwd_store_kv<D, KCH, ROPE>(kreg, vreg, &Ks[0][0][0] + st_off, &Vs[0][0][0] + st_off);
     if (ntile > 1) bwd_load_kv<D, KCH, ROPE>(kreg, vreg, krs, ld_off + BC * D * 2, vrows, vld_off, vtile);
     __syncthreads();
     if constexpr (NKH == 2) {
@@ -311,7 +315,7 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
             }
         }
         if (j + 1 < ntile) {
-            bwd_store_kv<D, KCH>(kreg, vreg, &Ks[0][0][0] + (buf ^ 1) * TBUF + st_off,
+            bwd_store_kv<D, KCH, ROPE>(kreg, vreg, &Ks[0][0][0] + (buf ^ 1) * TBUF + st_off,
                                  &Vs[0][0][0] + (buf ^ 1) * TBUF + st_off);
             if (j + 2 < ntile)
                 bwd_load_kv<D, KCH, ROPE>(kreg, vreg, krs, ld_off + (uint32_t)(j + 2) * (BC * D * 2), vrows,
@@ -412,8 +416,8 @@ template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-r
 
 // OT: element type of dk and dv (float32, or bfloat16 rounded to nearest even).
 // ROPE: V is read in place through rv's strides, K holds the rotated keys
-// (contiguous), and dK is turned back by the transpose rotation at the store; dK and
-// dV go through rv's strides.
+// (contiguous, fp16), and dK is turned back by the transpose rotation at the store;
+// dK and dV go through rv's strides.
 template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, (D == 128) ? 2 : 1)
 bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -556,7 +560,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                       : v + kvoff + (size_t)min(kw, N - 1) * D + 8 * h;
 #pragma unroll
             for (int c = 0; c < DC; ++c) {
-                kb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(krow + 16 * c)));
+                const u32x4 kw8 = *reinterpret_cast<const u32x4*>(krow + 16 * c);
+                kb[c] = __builtin_bit_cast(f16x8, ROPE ? kw8 : bf16x8_to_f16x8(kw8));   // rotated keys: fp16
                 vb[c] = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(*reinterpret_cast<const u32x4*>(vrow + 16 * c)));
             }
 #pragma unroll

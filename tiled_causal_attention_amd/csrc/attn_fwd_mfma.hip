@@ -104,7 +104,8 @@ __device__ __forceinline__ void store_kv_tile(const u32x4 (&kreg)[KCH], const u3
 
 // OT: element type of o (float32, or bfloat16 rounded to nearest even at the store).
 // ROPE: Q is read through rq's strides and rotated in registers (rotary embedding),
-// V is read in place through rq's V strides, and K holds the rotated keys, contiguous.
+// V is read in place through rq's V strides, and K holds the rotated keys, contiguous,
+// in fp16: the rotated Q and K meet in an fp16 product.
 template <int D, typename OT, bool ROPE>
 __global__ void __launch_bounds__(fwd::kThreads<D>, (D == 64) ? 4 : 2)
 fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -221,7 +222,10 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                 for (int c = 0; c < DC; ++c) {
                     const bf16x8 a =
                         *reinterpret_cast<const bf16x8*>(&Ks[buf][KPW * khalf + 32 * kb + krow_a][16 * c + 8 * h]);
-                    s[kb] = mfma_bf16(a, qb[c], s[kb]);
+                    if constexpr (ROPE)   // rotated K and Q hold fp16 bits
+                        s[kb] = mfma_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, qb[c]), s[kb]);
+                    else
+                        s[kb] = mfma_bf16(a, qb[c], s[kb]);
                 }
             }
             // ---- mask: only blocks crossing the diagonal or the end of the sequence

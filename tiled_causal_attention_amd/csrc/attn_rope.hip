@@ -16,8 +16,8 @@
 // threads on consecutive pairs). On the matrix-core path the kernels take over all
 // of it except the rotation of k: they read q and v through their strides, rotate
 // q in registers and store dq, dk, dv through their strides (dq, dk turned back),
-// and only k is rotated into a contiguous copy here, once per call, for the tiles
-// of every query block to read.
+// and only k is rotated here, into a contiguous fp16 copy (the precision the
+// kernels rotate q to), for the tiles of every query block to read.
 #include "tca_internal.h"
 
 namespace tca {
@@ -60,6 +60,16 @@ __device__ __forceinline__ void store8(bf16_t* p, const float (&x)[8]) {
     } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) store_out1(p + e, x[e]);
+    }
+}
+template <bool VEC>
+__device__ __forceinline__ void store8(_Float16* p, const float (&x)[8]) {
+    if constexpr (VEC) {
+        *reinterpret_cast<u32x4*>(p) = u32x4{pack_f16(x[0], x[1]), pack_f16(x[2], x[3]), pack_f16(x[4], x[5]),
+                                             pack_f16(x[6], x[7])};
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = (_Float16)x[e];
     }
 }
 template <bool VEC>
@@ -144,6 +154,10 @@ hipError_t layout_copy(attn_dtype ti, attn_dtype to, const CopyJobs& jobs, const
     if (ti == ATTN_F32)
         return to == ATTN_F32 ? copy_t<float, float>(jobs, cs, sn, N, d, st) : copy_t<float, bf16_t>(jobs, cs, sn, N, d, st);
     return to == ATTN_F32 ? copy_t<bf16_t, float>(jobs, cs, sn, N, d, st) : copy_t<bf16_t, bf16_t>(jobs, cs, sn, N, d, st);
+}
+
+hipError_t layout_copy_to_f16(const CopyJobs& jobs, const float* cs, const float* sn, int N, int d, hipStream_t st) {
+    return copy_t<bf16_t, _Float16>(jobs, cs, sn, N, d, st);
 }
 
 CopyJob copy_job(const void* src, const attn_layout& sl, void* dst, const attn_layout& dl, int B, int H, int N, int d,

@@ -167,15 +167,15 @@ bool rows_aligned16(const void* p, const attn_layout* l, size_t es) {
            ((size_t)l->stride_n * es) % 16 == 0;
 }
 
-// k, rotated, into its contiguous staging copy, one launch (on the fused path q is
-// rotated in the kernels' registers and v is read in place)
-hipError_t stage_k(const RopeWs& w, attn_dtype dtype, const void* k, const attn_layout* kl, const float* cs,
-                   const float* sn, int B, int Hkv, int N, int d, hipStream_t st) {
+// k (bfloat16), rotated, into its contiguous fp16 staging copy, one launch (on the
+// fused path q is rotated into fp16 in the kernels' registers and v is read in place)
+hipError_t stage_k(const RopeWs& w, const void* k, const attn_layout* kl, const float* cs, const float* sn, int B,
+                   int Hkv, int N, int d, hipStream_t st) {
     const attn_layout ck = contiguous_layout(Hkv, N, d);
     tca::CopyJobs jobs;
     jobs.n = 1;
     jobs.j[0] = tca::copy_job(k, kl ? *kl : ck, w.k, ck, B, Hkv, N, d, 1);
-    return tca::layout_copy(dtype, dtype, jobs, cs, sn, N, d, st);
+    return tca::layout_copy_to_f16(jobs, cs, sn, N, d, st);
 }
 
 // V read in place by the matrix-core kernels: 16-byte aligned rows at least d apart, and
@@ -399,7 +399,7 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         v_in_place(v, v_layout, Hkv, N, d)) {
         // fused: the forward reads q through its strides and rotates it in registers, and
         // reads v in place; only k is staged (rotated once, read by every query tile)
-        if (stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
+        if (stage_k(w, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
         const tca::QRope rq =
             make_qrope(q, q_layout, rope_cos, rope_sin, nullptr, nullptr, v, v_layout, Hq, Hkv, N, d);
         AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
@@ -445,7 +445,7 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         // the dK/dV pass is rotated too), reads v in place and stores dq turned back
         // through dq's strides; the dK/dV pass reads v in place and stores dk turned
         // back, and dv, through their strides
-        if (rotate_k && stage_k(w, dtype, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
+        if (rotate_k && stage_k(w, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
             return ATTN_EHIP;
         const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, v, v_layout, Hq, Hkv, N, d);
         const tca::KVRope rv = make_kvrope(v, v_layout, dk, dk_layout, dv, dv_layout, rope_cos, rope_sin, Hkv, N, d);

@@ -400,7 +400,9 @@ struct QRopeRow {
 };
 
 // Rotate the Q chunks a lane holds: chunk c (dims 16c + 8h .. +7) pairs with chunk
-// c + D/32 (the same dims + D/2). The rotated values are rounded to bfloat16.
+// c + D/32 (the same dims + D/2). The rotated values are rounded to fp16 (11-bit
+// significand; bfloat16 would add an input-sized rounding whose effect on the
+// outputs grows with the scores), so the products that take them run on fp16.
 template <int D>
 __device__ __forceinline__ void rope_rotate_q(u32x4 (&qr)[D / 16], const QRopeRow<D>& tab) {
     constexpr int DC = D / 16;
@@ -416,8 +418,8 @@ __device__ __forceinline__ void rope_rotate_q(u32x4 (&qr)[D / 16], const QRopeRo
         for (int t = 0; t < 4; ++t) {
             const float a0 = bf16_lo(aw[t]), a1 = bf16_hi(aw[t]), b0 = bf16_lo(bw[t]), b1 = bf16_hi(bw[t]);
             const float c_0 = cv[2 * t], c_1 = cv[2 * t + 1], s_0 = sv[2 * t], s_1 = sv[2 * t + 1];
-            ra[t] = pack_bf16(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
-            rbw[t] = pack_bf16(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
+            ra[t] = pack_f16(a0 * c_0 - b0 * s_0, a1 * c_1 - b1 * s_1);
+            rbw[t] = pack_f16(b0 * c_0 + a0 * s_0, b1 * c_1 + a1 * s_1);
         }
         qr[c] = u32x4{ra[0], ra[1], ra[2], ra[3]};
         qr[c + DC / 2] = u32x4{rbw[0], rbw[1], rbw[2], rbw[3]};

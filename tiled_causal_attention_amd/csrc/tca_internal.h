@@ -127,6 +127,8 @@ CopyJob copy_job(const void* src, const attn_layout& sl, void* dst, const attn_l
                  int rot);
 hipError_t layout_copy(attn_dtype ti, attn_dtype to, const CopyJobs& jobs, const float* cs, const float* sn, int N,
                        int d, hipStream_t st);
+// The same from bfloat16 into fp16 (the rotated keys of the matrix-core rotary path).
+hipError_t layout_copy_to_f16(const CopyJobs& jobs, const float* cs, const float* sn, int N, int d, hipStream_t st);
 
 // Unoptimised forward through a materialised score matrix (B*Hq*N*N floats of workspace).
 size_t naive_workspace_size(int B, int Hq, int N);
