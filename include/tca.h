@@ -192,16 +192,17 @@ size_t attn_bwd_rope_workspace_bytes(attn_dtype dtype, attn_dtype out_dtype, int
  * (x_i cos - x_{i+d/2} sin, x_{i+d/2} cos + x_i sin) before the attention;
  * both NULL means no rotation (strided input only). d must be even for
  * tables. q, k, v are read through their layouts (NULL: contiguous); o and lse
- * are written as by attn_fwd. With bfloat16 inputs, d in {64, 128}, tables,
- * and q and v rows starting on 16-byte boundaries (v rows at least d elements
- * apart), the matrix-core forward reads q through its strides and rotates it in
- * registers and reads v in place; only k is rotated into a contiguous copy in
- * `workspace` (at least attn_fwd_rope_workspace_bytes), once for every query tile
- * that reads it. On that path the rotated q and k are rounded to fp16 (11-bit
- * significand; |x| < 65504) and Q*K^T is an fp16 product, so the rotation adds
- * an eighth of an input rounding. Otherwise the rotated q, k (rounded to
- * `dtype`) and a contiguous v are staged there and attn_fwd's kernels run on
- * them. Pointers to
+ * are written as by attn_fwd. With bfloat16 inputs, d in {64, 128} and tables,
+ * the matrix-core forward reads q through its strides and rotates it in
+ * registers and reads v in place (each through an exact contiguous copy in
+ * `workspace` instead when its rows do not start on 16-byte boundaries, or v's
+ * rows are less than d elements apart); only k is rotated into a contiguous copy
+ * in `workspace` (at least attn_fwd_rope_workspace_bytes), once for every query
+ * tile that reads it. On that path the rotated q and k are rounded to fp16
+ * (11-bit significand; |x| < 65504) and Q*K^T is an fp16 product, so the
+ * rotation adds an eighth of an input rounding. Otherwise (float32 inputs, d in
+ * {16, 32}, or no tables) the rotated q, k (rounded to `dtype`) and a contiguous
+ * v are staged there and attn_fwd's kernels run on them. Pointers to
  * strided tensors need element alignment only; o and lse as for attn_fwd.
  * Strides must be >= 0 and the caller's buffers must hold every addressed
  * element.
@@ -228,10 +229,11 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype,
  * lse exactly as attn_fwd_rope wrote them (contiguous), dO contiguous in
  * `dtype`. dq and dk are turned back by the transpose rotation
  * (g_i cos + g_{i+d/2} sin, g_{i+d/2} cos - g_i sin) with a single rounding to
- * `out_dtype`. On the fused path of attn_fwd_rope (and dq rows 16-byte aligned)
- * k is rotated into `workspace` again; the dQ pass reads q and v through their
- * strides and stores dq turned back through dq's, and the dK/dV pass reads v in
- * place and stores dk turned back, and dv, through their layouts. Otherwise the
+ * `out_dtype`. On the matrix-core path of attn_fwd_rope, k is rotated into
+ * `workspace` again; the dQ pass reads q and v through their strides and stores
+ * dq turned back through dq's (through a contiguous copy scattered afterwards
+ * when dq's rows are not 16-byte aligned), and the dK/dV pass reads v in place
+ * and stores dk turned back, and dv, through their layouts. Otherwise the
  * rotated copies are staged, attn_bwd's kernels write float32 gradients into
  * `workspace`, and one launch turns dq, dk back and scatters all three.
  * k_rot: NULL, or the k_rot that attn_fwd_rope filled for the same k, tables

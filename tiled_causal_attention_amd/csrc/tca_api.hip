@@ -186,6 +186,38 @@ bool v_in_place(const void* v, const attn_layout* vl, int Hkv, int N, int d) {
     return l.stride_n >= d && (int64_t)(N + 64) * l.stride_n * 2 < ((int64_t)1 << 32);
 }
 
+// q and v as the matrix-core rotary kernels read them: in place when their rows allow it
+// (q: 16-byte aligned rows; v: as v_in_place), else through exact contiguous copies
+// in the workspace (one launch for both). qv/vv and ql/vl receive what to read.
+hipError_t fused_inputs(const RopeWs& w, const void* q, const attn_layout* q_layout, const void* v,
+                        const attn_layout* v_layout, int B, int Hq, int Hkv, int N, int d, const void** qv,
+                        const attn_layout** ql, const void** vv, const attn_layout** vl, hipStream_t st) {
+    const attn_layout cq = contiguous_layout(Hq, N, d), ck = contiguous_layout(Hkv, N, d);
+    *qv = q;
+    *ql = q_layout;
+    *vv = v;
+    *vl = v_layout;
+    tca::CopyJobs jobs;
+    jobs.n = 0;
+    if (!rows_aligned16(q, q_layout, 2)) {
+        jobs.j[jobs.n++] = tca::copy_job(q, q_layout ? *q_layout : cq, w.q, cq, B, Hq, N, d, 0);
+        *qv = w.q;
+        *ql = nullptr;
+    }
+    if (!v_in_place(v, v_layout, Hkv, N, d)) {
+        jobs.j[jobs.n++] = tca::copy_job(v, v_layout ? *v_layout : ck, w.v, ck, B, Hkv, N, d, 0);
+        *vv = w.v;
+        *vl = nullptr;
+    }
+    return jobs.n ? tca::layout_copy(ATTN_BF16, ATTN_BF16, jobs, nullptr, nullptr, N, d, st) : hipSuccess;
+}
+
+// The matrix-core rotary kernels take every bfloat16 call with tables and d in {64, 128}
+// whose contiguous copies they could read (a contiguous V head's byte offsets fit 32 bits)
+bool fused_rope(attn_dtype dtype, const float* cs, int N, int d) {
+    return cs != nullptr && tca::mfma_shape(dtype, d) && (int64_t)(N + 64) * d * 2 < ((int64_t)1 << 32);
+}
+
 tca::QRope make_qrope(const void* q, const attn_layout* ql, const float* cs, const float* sn, void* dq,
                       const attn_layout* gl, const void* v, const attn_layout* vl, int Hq, int Hkv, int N, int d) {
     const attn_layout cq = contiguous_layout(Hq, N, d);
@@ -395,14 +427,18 @@ attn_status attn_fwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     if (workspace_bytes < w.total) return ATTN_EINVAL;
     if (k_rot != nullptr) w.k = static_cast<char*>(k_rot);   // the rotated keys go to the caller's buffer
     hipStream_t st = (hipStream_t)stream;
-    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
-        v_in_place(v, v_layout, Hkv, N, d)) {
-        // fused: the forward reads q through its strides and rotates it in registers, and
-        // reads v in place; only k is staged (rotated once, read by every query tile)
+    if (fused_rope(dtype, rope_cos, N, d)) {
+        // fused: the forward reads q through its strides and rotates it into fp16 in
+        // registers, and reads v in place (both through contiguous copies where their
+        // rows do not allow it); only k is staged (rotated into fp16 once, read by every
+        // query tile)
+        const void *qv, *vv;
+        const attn_layout *ql, *vl;
+        if (fused_inputs(w, q, q_layout, v, v_layout, B, Hq, Hkv, N, d, &qv, &ql, &vv, &vl, st) != hipSuccess)
+            return ATTN_EHIP;
         if (stage_k(w, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess) return ATTN_EHIP;
-        const tca::QRope rq =
-            make_qrope(q, q_layout, rope_cos, rope_sin, nullptr, nullptr, v, v_layout, Hq, Hkv, N, d);
-        AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+        const tca::QRope rq = make_qrope(qv, ql, rope_cos, rope_sin, nullptr, nullptr, vv, vl, Hq, Hkv, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, qv, w.k, vv, o, lse, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
                                B, Hq, Hkv, N, d, causal, scale);
         a.rope = &rq;
         return from_hip(tca::launch_fwd_mfma(a, st));
@@ -438,18 +474,27 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
     const bool rotate_k = k_rot == nullptr;   // else the forward's rotated keys are read back
     if (!rotate_k) w.k = static_cast<char*>(const_cast<void*>(k_rot));
     hipStream_t st = (hipStream_t)stream;
-    if (rope_cos && tca::mfma_shape(dtype, d) && rows_aligned16(q, q_layout, 2) &&
-        rows_aligned16(dq, dq_layout, elsize(out_dtype)) && v_in_place(v, v_layout, Hkv, N, d)) {
-        // fused: only k is staged (rotated), unless the forward's copy is given. The dQ
-        // pass reads q through its strides, rotates it in registers (its fp16 copy for
-        // the dK/dV pass is rotated too), reads v in place and stores dq turned back
-        // through dq's strides; the dK/dV pass reads v in place and stores dk turned
-        // back, and dv, through their strides
+    if (fused_rope(dtype, rope_cos, N, d)) {
+        // fused: only k is staged (rotated into fp16), unless the forward's copy is given.
+        // The dQ pass reads q through its strides, rotates it into fp16 in registers (its
+        // fp16 copy for the dK/dV pass is rotated too), reads v in place and stores dq
+        // turned back through dq's strides; the dK/dV pass reads v in place and stores dk
+        // turned back, and dv, through their strides. q and v go through contiguous copies
+        // where their rows do not allow reading them in place, and dq, whose rows are
+        // stored 16 or 8 bytes at a time, through a contiguous copy scattered afterwards
+        // where its rows are not 16-byte aligned.
+        const void *qv, *vv;
+        const attn_layout *ql, *vl;
+        if (fused_inputs(w, q, q_layout, v, v_layout, B, Hq, Hkv, N, d, &qv, &ql, &vv, &vl, st) != hipSuccess)
+            return ATTN_EHIP;
         if (rotate_k && stage_k(w, k, k_layout, rope_cos, rope_sin, B, Hkv, N, d, st) != hipSuccess)
             return ATTN_EHIP;
-        const tca::QRope rq = make_qrope(q, q_layout, rope_cos, rope_sin, dq, dq_layout, v, v_layout, Hq, Hkv, N, d);
-        const tca::KVRope rv = make_kvrope(v, v_layout, dk, dk_layout, dv, dv_layout, rope_cos, rope_sin, Hkv, N, d);
-        AttnArgs a = make_args(dtype, out_dtype, q, w.k, v, o, lse, dO, dq, dk, dv, w.bwd, w.bwd_bytes, B, Hq, Hkv,
+        const bool dq_direct = rows_aligned16(dq, dq_layout, elsize(out_dtype));
+        void* dqt = dq_direct ? dq : static_cast<void*>(w.dq);
+        const attn_layout* dql = dq_direct ? dq_layout : nullptr;
+        const tca::QRope rq = make_qrope(qv, ql, rope_cos, rope_sin, dqt, dql, vv, vl, Hq, Hkv, N, d);
+        const tca::KVRope rv = make_kvrope(vv, vl, dk, dk_layout, dv, dv_layout, rope_cos, rope_sin, Hkv, N, d);
+        AttnArgs a = make_args(dtype, out_dtype, qv, w.k, vv, o, lse, dO, dqt, dk, dv, w.bwd, w.bwd_bytes, B, Hq, Hkv,
                                N, d, causal, scale);
         a.rope = &rq;
         s = run_dq(a, st);
@@ -457,7 +502,13 @@ attn_status attn_bwd_rope(attn_dtype dtype, attn_dtype out_dtype, const void* q,
         AttnArgs a2 = a;
         a2.rope = nullptr;
         a2.kvrope = &rv;
-        return run_dkdv(a2, st);
+        s = run_dkdv(a2, st);
+        if (s != ATTN_OK || dq_direct) return s;
+        const attn_layout cq = contiguous_layout(Hq, N, d);
+        tca::CopyJobs jobs;
+        jobs.n = 1;
+        jobs.j[0] = tca::copy_job(w.dq, cq, dq, dq_layout ? *dq_layout : cq, B, Hq, N, d, 0);
+        return from_hip(tca::layout_copy(out_dtype, out_dtype, jobs, nullptr, nullptr, N, d, st));
     }
     hipError_t e =
         stage_qkv(w, dtype, q, q_layout, k, k_layout, v, v_layout, rope_cos, rope_sin, B, Hq, Hkv, N, d, rotate_k, st);
