@@ -174,3 +174,34 @@ def test_random_rope(case):
     rq, rk, rv = oracle.attn_bwd_rope(q, k, v, do, cos, sin, causal, scale)
     for name, got, ref in (("o", o, ro), ("lse", lse, rl), ("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
         _check(name, got, ref, dtype, ctx)
+
+
+@pytest.mark.parametrize("case", _fwd_cases()[:20], ids=lambda c: f"bo{c[0]}")
+def test_random_bf16_outputs_are_rounded(case):
+    # bfloat16 outputs are the float32 results rounded once: o and lse of the forward,
+    # and dq, dk, dv of a backward that takes the bfloat16 o against a float32-output
+    # backward given that o widened; bit for bit on every path
+    i, B, Hq, Hkv, N, d, dtype, causal, scale, seed = case
+    print(f"[random bf16 out] case {i}: B={B} Hq={Hq} Hkv={Hkv} N={N} d={d} {dtype} causal={causal}", flush=True)
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype=dtype, seed=seed, causal=causal)
+    q, k, v, do = (t.cuda() for t in workloads.make_inputs(s))
+    o16, l16 = tca.attn_fwd(q, k, v, causal=bool(causal), scale=scale, out_dtype=torch.bfloat16)
+    o32, l32 = tca.attn_fwd(q, k, v, causal=bool(causal), scale=scale)
+    g16 = tca.attn_bwd(q, k, v, o16, l16, do, causal=bool(causal), scale=scale)
+    g32 = tca.attn_bwd(q, k, v, o16.float(), l16, do, causal=bool(causal), scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(l16, l32), i
+    assert torch.equal(o16, o32.to(torch.bfloat16)), i
+    for name, a, b in zip(("dq", "dk", "dv"), g16, g32):
+        assert a.dtype == torch.bfloat16 and torch.equal(a, b.to(torch.bfloat16)), f"case {i} {name}"
+
+
+@pytest.mark.parametrize("case", _decode_cases()[:10], ids=lambda c: f"dbo{c[0]}")
+def test_random_decode_bf16_outputs_are_rounded(case):
+    i, B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale, seed = case
+    s = workloads.make_decode_shape(B, Hq, Hkv, Nq, Nk, d, dtype=dtype, seed=seed, causal=causal)
+    q, k, v = (t.cuda() for t in workloads.make_decode_inputs(s))
+    o16, l16 = tca.attn_decode(q, k, v, causal=bool(causal), scale=scale, out_dtype=torch.bfloat16)
+    o32, l32 = tca.attn_decode(q, k, v, causal=bool(causal), scale=scale)
+    torch.cuda.synchronize()
+    assert torch.equal(l16, l32) and torch.equal(o16, o32.to(torch.bfloat16)), i
