@@ -45,8 +45,10 @@
  * |x| >= 2^-14 (inputs must satisfy |x| < 65504). The probabilities P and the
  * score gradient dS are rounded to fp16 (11-bit significand) for the products
  * that consume them (P*V, P^T*dO, dS*K, dS^T*Q), whose other operand is
- * converted to fp16 likewise. bf16 inputs with d in {16, 32} are computed in
- * float32.
+ * converted to fp16 likewise; dS = P o (dP - D) must therefore stay within the
+ * fp16 range (|dS| < 65504, which |P| <= 1 leaves to dP = dO*V^T and D), and
+ * values below 2^-14 lose precision as fp16 subnormals. bf16 inputs with d in
+ * {16, 32} are computed in float32.
  *
  * Memory ownership: the caller owns every buffer. All tensor pointers are
  * device memory (hipMalloc or equivalent), 16-byte aligned, and must stay
