@@ -300,8 +300,12 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
  * workgroup and merge in on-chip memory: one launch, no workspace. Otherwise each range writes its
  * partial output and log-sum-exp into `workspace` (at least
  * attn_decode_workspace_bytes(...) bytes of device memory, 16-byte aligned;
- * NULL allowed when that is 0) and a second kernel merges them. Arithmetic is
- * float32 on the vector units for every dtype.
+ * NULL allowed when that is 0) and a second kernel merges them. Arithmetic:
+ * bf16 inputs at d = 64 or 128 with at least 3 query rows per KV head (Hq/Hkv *
+ * Nq; 2 at d = 64), when not merged in one workgroup, run on the matrix cores as
+ * the forward does (bf16 Q K^T, fp32 accumulation, probabilities rounded to fp16
+ * for P V, so |x| < 65504 is required of v as of attn_fwd's inputs); every other
+ * call computes in float32 on the vector units.
  * Sizes: B >= 0, Nq >= 0 (B*Nq == 0 is a no-op), Nq <= Nk, Hq % Hkv == 0,
  * d in {16, 32, 64, 128}, (Nk+256)*d*4 < 2^31; otherwise ATTN_EINVAL (or
  * ATTN_EUNSUPPORTED for d). Results are bitwise reproducible. */

@@ -5,8 +5,10 @@ Query row i of Nq is sequence position Nk - Nq + i and, causally, sees keys
 j <= Nk - Nq + i. Tolerances per output tensor (o, lse): float32 inputs and
 outputs max |x - ref| <= 1e-4; bfloat16 inputs max |x - ref| <= 2e-2 and
 ||x - ref||_2 / ||ref||_2 <= 1e-2; bfloat16 outputs add half a bfloat16 ulp
-(<= 2^-8 |x|) per element. The kernels compute in float32 from exactly
-widened inputs, so the errors seen are float32 rounding, far inside these.
+(<= 2^-8 |x|) per element. The vector-unit kernels compute in float32 from
+exactly widened inputs (errors of float32 rounding); the matrix-core split
+(bf16 inputs, d 64 or 128, 3+ rows per KV head or 2 at d = 64) rounds the
+probabilities to fp16 for P V as the forward does, errors ~1e-4, far inside.
 """
 import numpy as np
 import pytest
@@ -89,6 +91,9 @@ SHAPES = [
     (128, 8, 2, 1, 400, 64, "f32"),    # 7 splits of 4 float32 rows
     (256, 8, 1, 1, 512, 128, "bf16"),  # 8 splits of 8 rows
     (16, 2, 2, 70, 200, 64, "bf16"),   # Nq = 70 > 64: early rows see no key of the last split
+    # either side of the matrix-core split's threshold (bf16 at d = 128)
+    (2, 8, 4, 1, 900, 128, "bf16"),    # 2 rows per KV head: the vector-unit split
+    (2, 12, 4, 1, 1000, 128, "bf16"),  # 3 rows: the matrix-core split
 ]
 
 

@@ -8,12 +8,17 @@
 //
 // With few rows the work is a stream over the K/V cache: a GQA group of G
 // query heads and Nq rows does 4 d G Nq flops per key against 4 d bytes of
-// bf16 K and V, a few flops per byte, so HBM bandwidth bounds it and the
-// kernel is built around the loads, on the VALU (a matrix-core tile would sit
-// mostly empty):
+// bf16 K and V, a few flops per byte, so HBM bandwidth bounds it. There are two
+// split kernels. decode_mfma_kernel (bf16 inputs, d = 64 or 128, at least 3 rows
+// per KV head, or 2 at d = 64) runs the forward's tile step on the matrix cores
+// with the group's rows as the 32 columns of the products: columns that are
+// mostly empty still cost less than the VALU dot products, whose per-key work
+// otherwise outlasts the loads (details at the kernel). decode_split_kernel
+// serves every other case on the VALU and is built around the loads:
 //
 //  * The G * Nq rows that share a KV head are processed together (RM rows per
-//    wave, RM in {1, 2, 4, 8}), so each K/V row is read once per group.
+//    wave, RM in {1, 2, 4, 8}; 32 on the matrix cores), so each K/V row is read
+//    once per group.
 //  * Split-K: the keys are cut into splits; one wave owns one (batch, KV head,
 //    row chunk, split) item and the splits run in parallel. Each writes a
 //    normalised partial output and its LSE; a second kernel merges the splits
@@ -394,6 +399,162 @@ decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     }
 }
 
+// Matrix-core split for bf16 inputs at d = 64 and 128. One wave per (batch, KV
+// head, row chunk, key split) item, as decode_split_kernel, but the chunk holds
+// 32 rows of the GQA group -- the columns of 32x32x16 products -- and each
+// 64-key tile is the forward's step with the roles kept: S^T = K Q^T with this
+// lane's K rows as the A operand (read straight from global memory: rows past
+// Nk read as zero) and the chunk's queries as the B operand, the online softmax
+// down each column, and O^T += V^T P^T with P rounded to fp16 from the score
+// accumulator and V^T read transposed from LDS. The V tile reaches LDS by direct
+// copies (the dK/dV pass's swizzled rows, bf16 bits, converted to fp16 at the
+// read), so the wave's only wait per tile is one round trip for K and V
+// together. Rows past the chunk's G * Nq rows carry zero queries and are not
+// stored. The scale's sign is folded into Q (ScoreScale), so the exponent's
+// multiplier is positive and masked keys stay at -inf. Output as the split
+// kernel's: o, lse when nsplit == 1, else the normalised partial and its LSE
+// (log2 units) per split for the merge kernel.
+namespace decm {
+constexpr int BC = 64;   // keys per tile
+using dec::kTau;
+}
+
+template <typename OT, int D>
+__global__ void __launch_bounds__(64, (D == 64) ? 3 : 2)   // waves per SIMD at least
+decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                   OT* __restrict__ o, float* __restrict__ lse, float* __restrict__ opart,
+                   float* __restrict__ lpart, int Hq, int Hkv, int Nq, int Nk, int causal, ScoreScale sc,
+                   int nrc, int nsplit, int split_len, int nrows) {
+    using namespace decm;
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int NCOPY = BC * D * 2 / 1024;   // 1 KB direct copies per V tile
+    __shared__ __attribute__((aligned(16))) _Float16 Vs[BC * D];
+    const int lane = threadIdx.x, h = lane >> 5, r = lane & 31;
+    const int item = blockIdx.x;
+    const int split = item % nsplit, rest = item / nsplit;
+    const int rc = rest % nrc, unit = rest / nrc;
+    const int b = unit / Hkv, hkv = unit % Hkv;
+    const int G = Hq / Hkv, R = G * Nq;
+
+    // this lane's row: column r of the products
+    const int rho = rc * 32 + r;
+    const bool ok = rho < R;
+    const int rv = ok ? rho : R - 1;
+    const int g = rv / Nq, i = rv % Nq;
+    const size_t grow = ((size_t)b * Hq + hkv * G + g) * Nq + i;
+    const int k0 = split * split_len, k1 = min(Nk, k0 + split_len);
+    const int lim = !ok ? k0 : (causal ? min(k1, Nk - Nq + i + 1) : k1);   // keys below lim are visible
+
+    bf16x8 qb[DC];
+    {
+        const bf16_t* qrow = q + grow * D + 8 * h;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+            qb[c] = ok ? __builtin_bit_cast(bf16x8, apply_qsign(x, sc)) : bf16x8{};
+        }
+    }
+    const size_t kvoff = (size_t)unit * Nk * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
+    const int krow_a = perm32(r);
+    const float sl2 = sc.sl2;
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int x = 0; x < DB; ++x) oacc[x] = f32x16{};
+    float m_s = -0x1p100f;   // finite, far below any score: the first rescale factor is 0
+    float l_run = 0.f;
+
+    for (int t0 = k0; t0 < k1; t0 += BC) {
+        if (t0 > k0) __syncthreads();   // the previous tile's V reads are done before the copies land
+        {
+            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff + (size_t)t0 * D, (uint32_t)((Nk - t0) * D * 2));
+#pragma unroll
+            for (int u = 0; u < NCOPY; ++u) lds_copy16(vrs, Vs + u * 512, tile_copy_src<D>(u, lane));
+        }
+        u32x4 ka[2][DC];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int c = 0; c < DC; ++c)
+                ka[kb][c] = buf_load16(krs, (uint32_t)(((t0 + 32 * kb + krow_a) * D + 16 * c + 8 * h) * 2));
+        wait_vmem_all();   // the V copies are in LDS
+        __syncthreads();
+        // ---- S^T = K Q^T; accumulator e of block kb: key t0 + 32 kb + 16(e/8) + 8h + e%8
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x16{};
+#pragma unroll
+            for (int c = 0; c < DC; ++c) s[kb] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[kb][c]), qb[c], s[kb]);
+            const int lm = lim - t0 - 32 * kb - 8 * h;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[kb][e] = (16 * (e >> 3) + (e & 7) < lm) ? s[kb][e] : -INFINITY;
+        }
+        // ---- online softmax down each column, lazy rescale (log2 units)
+        const float mt = max_halves(vmax(max16(s[0]), max16(s[1]))) * sl2;
+        if (__any(mt > m_s + kTau)) {
+            const float m_new = vmax(m_s, mt);
+            const float alpha = fast_exp2(m_s - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int x = 0; x < DB; ++x)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
+            m_s = m_new;
+        }
+        // ---- O^T += V^T P^T, P in fp16 (its rounded values are the ones summed)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int c2 = 0; c2 < 2; ++c2) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    pk[t] = pack_f16(fast_exp2(fmaf(s[kb][8 * c2 + 2 * t], sl2, -m_s)),
+                                     fast_exp2(fmaf(s[kb][8 * c2 + 2 * t + 1], sl2, -m_s)));
+                    l_run = add_f16_pair(pk[t], l_run);
+                }
+                const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+                for (int x = 0; x < DB; ++x) {
+                    const f16x8 vt = tile_tr_operand<D>(Vs, 32 * kb + 16 * c2, 32 * x, h, r);   // bf16 bits
+                    const f16x8 a = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, vt)));
+                    oacc[x] = mfma_f16(a, pb, oacc[x]);
+                }
+            }
+    }
+
+    // ---- this split's normalised output and LSE; lane (h, r) holds dims 32x + 8(e/4) + 4h + e%4
+    const float l_tot = sum_halves(l_run);
+    if (!ok) return;
+    const bool any = l_tot > 0.f;
+    const float inv = any ? 1.f / l_tot : 0.f;
+    const float l2 = any ? m_s + __log2f(l_tot) : -INFINITY;
+    if (nsplit == 1) {
+        OT* orow = o + grow * D;
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+                store_out4(orow + 32 * x + 8 * a4 + 4 * h,
+                           f32x4{oacc[x][4 * a4] * inv, oacc[x][4 * a4 + 1] * inv, oacc[x][4 * a4 + 2] * inv,
+                                 oacc[x][4 * a4 + 3] * inv});
+        if (h == 0) lse[grow] = l2 * kLn2;
+    } else {
+        const size_t prow = (size_t)split * nrows + grow;
+        float* orow = opart + prow * D;
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int a4 = 0; a4 < 4; ++a4)
+                *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) =
+                    f32x4{oacc[x][4 * a4] * inv, oacc[x][4 * a4 + 1] * inv, oacc[x][4 * a4 + 2] * inv,
+                          oacc[x][4 * a4 + 3] * inv};
+        if (h == 0) lpart[prow] = l2;
+    }
+}
+
 // Merge of the splits of one row: LSE = log2 sum_s 2^LSE_s (log2 units in lpart),
 // O = sum_s 2^(LSE_s - LSE) O_s. CB = D / (2 NP) workgroups of 256 threads per
 // row, each owning NP column pairs: with many splits NP = 16 (4 workgroups per
@@ -465,12 +626,10 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
 }
 
 // ---------------------------------------------------------------- host side
-DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32) {
-    DecodePlan p;
-    const int R = (Hq / Hkv) * Nq;
-    p.rm = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
-    p.nrc = (R + p.rm - 1) / p.rm;
-    const long long items0 = (long long)B * Hkv * p.nrc;
+// Key splits for `items0` (batch, KV head, row chunk) groups: about kTargetWaves
+// waves in all, at least kMinSplitKeys keys (a multiple of 64) per split, at most
+// 256 splits per row.
+static void plan_splits(DecodePlan& p, long long items0, int Nk) {
     long long want = (dec::kTargetWaves + items0 - 1) / items0;
     const long long cap = ((long long)Nk + dec::kMinSplitKeys - 1) / dec::kMinSplitKeys;
     want = want < 1 ? 1 : want;
@@ -480,11 +639,29 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32)
     if (p.split_len < 64) p.split_len = 64;
     p.nsplit = (int)(((long long)Nk + p.split_len - 1) / p.split_len);
     if (p.nsplit < 1) p.nsplit = 1;
+}
+
+DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32) {
+    DecodePlan p;
+    const int R = (Hq / Hkv) * Nq;
+    p.rm = R <= 1 ? 1 : R <= 2 ? 2 : R <= 4 ? 4 : 8;
+    p.nrc = (R + p.rm - 1) / p.rm;
+    const long long items0 = (long long)B * Hkv * p.nrc;
+    plan_splits(p, items0, Nk);
     // merged in the workgroup when there are enough workgroups to fill the CUs: with
     // fewer, one CU streaming a whole row chunk's splits is slower than splits spread
     // over the chip plus a merge kernel
     p.fused = p.nsplit > 1 && p.nsplit <= dec::fused_waves(p.rm, in32) && items0 >= dec::kFusedMinGroups;
-    (void)d;
+    p.mfma = false;
+    if (!p.fused && !in32 && (d == 64 || d == 128) && (R >= 3 || (R == 2 && d == 64))) {
+        // matrix-core splits, row chunks of 32 rows: measured faster from 3 rows per
+        // KV head (2 at d = 64); with one or two rows the 32-column products sit
+        // nearly empty and the VALU split, whose K reads are whole rows, is faster
+        p.mfma = true;
+        p.rm = 32;
+        p.nrc = (R + 31) / 32;
+        plan_splits(p, (long long)B * Hkv * p.nrc, Nk);
+    }
     return p;
 }
 
@@ -493,6 +670,44 @@ size_t decode_workspace_size(bool in32, int B, int Hq, int Hkv, int Nq, int Nk, 
     if (p.nsplit <= 1 || p.fused) return 0;
     const size_t rows = (size_t)B * Hq * Nq;
     return ws_round((size_t)p.nsplit * rows * d * sizeof(float)) + ws_round((size_t)p.nsplit * rows * sizeof(float));
+}
+
+// The merge of the split partials (after either split kernel).
+template <typename OT, int D>
+static void launch_merge(const DecodeArgs& a, const DecodePlan& p, const float* opart, const float* lpart, int nrows,
+                         hipStream_t st) {
+    if (p.nsplit > kMergeColSplits && D >= 32) {
+        constexpr int NP = D >= 32 ? 16 : D / 2;
+        hipLaunchKernelGGL((decode_merge_kernel<OT, D, NP>), dim3((unsigned)((long long)nrows * (D / (2 * NP)))),
+                           dim3(kMergeThreads), 0, st, opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
+    } else if (p.nsplit > 1) {
+        hipLaunchKernelGGL((decode_merge_kernel<OT, D, D / 2>), dim3((unsigned)nrows), dim3(kMergeThreads), 0, st,
+                           opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
+    }
+}
+
+// Split partials in the workspace: opart [nsplit][rows][D] floats, then lpart [nsplit][rows].
+static void split_partials(const DecodeArgs& a, const DecodePlan& p, int nrows, float** opart, float** lpart) {
+    *opart = nullptr;
+    *lpart = nullptr;
+    if (p.nsplit > 1) {
+        *opart = static_cast<float*>(a.workspace);
+        *lpart = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
+                                          ws_round((size_t)p.nsplit * nrows * a.d * sizeof(float)));
+    }
+}
+
+template <typename OT, int D>
+static hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    const int nitems = a.B * a.Hkv * p.nrc * p.nsplit;
+    const int nrows = a.B * a.Hq * a.Nq;
+    float *opart, *lpart;
+    split_partials(a, p, nrows, &opart, &lpart);
+    hipLaunchKernelGGL((decode_mfma_kernel<OT, D>), dim3((unsigned)nitems), dim3(64), 0, st, (const bf16_t*)a.q,
+                       (const bf16_t*)a.k, (const bf16_t*)a.v, (OT*)a.o, a.lse, opart, lpart, a.Hq, a.Hkv, a.Nq,
+                       a.Nk, a.causal, score_scale(a.scale), p.nrc, p.nsplit, p.split_len, nrows);
+    launch_merge<OT, D>(a, p, opart, lpart, nrows, st);
+    return hipGetLastError();
 }
 
 template <typename T, typename OT, int D, int RM>
@@ -505,25 +720,13 @@ static hipError_t launch_decode_t(const DecodeArgs& a, const DecodePlan& p, hipS
     }
     const int nitems = a.B * a.Hkv * p.nrc * p.nsplit;
     const int nrows = a.B * a.Hq * a.Nq;
-    float* opart = nullptr;
-    float* lpart = nullptr;
-    if (p.nsplit > 1) {
-        opart = static_cast<float*>(a.workspace);
-        lpart = reinterpret_cast<float*>(static_cast<char*>(a.workspace) +
-                                         ws_round((size_t)p.nsplit * nrows * D * sizeof(float)));
-    }
+    float *opart, *lpart;
+    split_partials(a, p, nrows, &opart, &lpart);
     const dim3 grid((unsigned)((nitems + dec::kWaves - 1) / dec::kWaves));
     hipLaunchKernelGGL((decode_split_kernel<T, OT, D, RM>), grid, dim3(64 * dec::kWaves), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, (OT*)a.o, a.lse, opart, lpart, a.Hq,
                        a.Hkv, a.Nq, a.Nk, a.causal, a.scale, p.nrc, p.nsplit, p.split_len, nitems, nrows);
-    if (p.nsplit > kMergeColSplits && D >= 32) {
-        constexpr int NP = D >= 32 ? 16 : D / 2;
-        hipLaunchKernelGGL((decode_merge_kernel<OT, D, NP>), dim3((unsigned)((long long)nrows * (D / (2 * NP)))),
-                           dim3(kMergeThreads), 0, st, opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
-    } else if (p.nsplit > 1) {
-        hipLaunchKernelGGL((decode_merge_kernel<OT, D, D / 2>), dim3((unsigned)nrows), dim3(kMergeThreads), 0, st,
-                           opart, lpart, (OT*)a.o, a.lse, nrows, p.nsplit);
-    }
+    launch_merge<OT, D>(a, p, opart, lpart, nrows, st);
     return hipGetLastError();
 }
 
@@ -539,6 +742,9 @@ static hipError_t launch_decode_rm(const DecodeArgs& a, const DecodePlan& p, hip
 
 template <typename T, typename OT>
 static hipError_t launch_decode_d(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        if (p.mfma) return (a.d == 64) ? launch_decode_mfma<OT, 64>(a, p, st) : launch_decode_mfma<OT, 128>(a, p, st);
+    }
     switch (a.d) {
         case 16: return launch_decode_rm<T, OT, 16>(a, p, st);
         case 32: return launch_decode_rm<T, OT, 32>(a, p, st);

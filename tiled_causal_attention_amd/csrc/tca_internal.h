@@ -94,11 +94,12 @@ struct DecodeArgs {
     float scale;
 };
 // Launch shape of the decode kernels, a function of the sizes only: RM rows per
-// wave (1, 2, 4 or 8), nrc row chunks of a GQA group's G * Nq rows, nsplit key
-// splits of split_len keys (a multiple of 64).
+// wave (1, 2, 4 or 8; 32 on the matrix-core split), nrc row chunks of a GQA
+// group's G * Nq rows, nsplit key splits of split_len keys (a multiple of 64).
 struct DecodePlan {
     int rm, nrc, nsplit, split_len;
     bool fused;   // the splits of a row chunk are the waves of one workgroup, merged in LDS
+    bool mfma;    // bf16 inputs, d 64 or 128, not fused: decode_mfma_kernel's 32-row chunks
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32);
 size_t decode_workspace_size(bool in32, int B, int Hq, int Hkv, int Nq, int Nk, int d);
