@@ -297,7 +297,10 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
  * are merged through their log-sum-exps. When a call has at least 256 (batch,
  * KV head, query-row chunk) groups and up to 16 ranges per group (8 when a wave
  * holds 8 query rows, or 4 float32 ones), a group's ranges are the waves of one
- * workgroup and merge in on-chip memory: one launch, no workspace. Otherwise each range writes its
+ * workgroup and merge in on-chip memory: one launch, no workspace -- except bf16
+ * calls at d = 128 with 8 or more query rows per KV head whose partials fit
+ * ATTN_DECODE_SCRATCH_BYTES, which take the matrix-core ranges below (measured
+ * faster there). Otherwise each range writes its
  * partial output and log-sum-exp into `workspace` (at least
  * attn_decode_workspace_bytes(...) bytes of device memory, 16-byte aligned;
  * NULL allowed when that is 0) and a second kernel merges them. Arithmetic:

@@ -653,14 +653,24 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32)
     // over the chip plus a merge kernel
     p.fused = p.nsplit > 1 && p.nsplit <= dec::fused_waves(p.rm, in32) && items0 >= dec::kFusedMinGroups;
     p.mfma = false;
-    if (!p.fused && !in32 && (d == 64 || d == 128) && (R >= 3 || (R == 2 && d == 64))) {
-        // matrix-core splits, row chunks of 32 rows: measured faster from 3 rows per
-        // KV head (2 at d = 64); with one or two rows the 32-column products sit
-        // nearly empty and the VALU split, whose K reads are whole rows, is faster
-        p.mfma = true;
-        p.rm = 32;
-        p.nrc = (R + 31) / 32;
-        plan_splits(p, (long long)B * Hkv * p.nrc, Nk);
+    // matrix-core splits, row chunks of 32 rows: measured faster from 3 rows per KV
+    // head (2 at d = 64); with one or two rows the 32-column products sit nearly
+    // empty and the VALU split, whose K reads are whole rows, is faster. Against the
+    // workgroup-merged VALU form they win only at d = 128 with 8 or more rows (the
+    // merged form's 8-row waves), and take its place there when their split partials
+    // fit the no-allocation scratch (so both entry points keep serving the same calls).
+    if (!in32 && (d == 64 || d == 128) && (R >= 3 || (R == 2 && d == 64))) {
+        DecodePlan m = p;
+        m.mfma = true;
+        m.fused = false;
+        m.rm = 32;
+        m.nrc = (R + 31) / 32;
+        plan_splits(m, (long long)B * Hkv * m.nrc, Nk);
+        const size_t rows = (size_t)B * Hq * Nq;
+        const size_t part = m.nsplit <= 1 ? 0
+                                          : ws_round((size_t)m.nsplit * rows * d * sizeof(float)) +
+                                                ws_round((size_t)m.nsplit * rows * sizeof(float));
+        if (!p.fused || (d == 128 && R >= 8 && part <= kDecodeScratchBytes)) p = m;
     }
     return p;
 }
