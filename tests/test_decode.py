@@ -111,6 +111,25 @@ def test_decode_bf16_out(B, Hq, Hkv, Nq, Nk, d, dtype):
     parity(s, torch.bfloat16)
 
 
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d", [(2, 6, 2, 1, 300, 64), (1, 8, 1, 2, 700, 128), (2, 4, 4, 1, 500, 64)])
+def test_decode_zero_and_negative_scale(B, Hq, Hkv, Nq, Nk, d, scale):
+    # both split kernels (3 and 16 rows per KV head on the matrix cores, 1 on the
+    # vector units); scale 0 weighs every visible key equally (O = mean of V, LSE =
+    # ln of the visible count), a negative scale reverses the score order
+    s = workloads.make_decode_shape(B, Hq, Hkv, Nq, Nk, d, seed=Nk + d)
+    q, k, v = workloads.make_decode_inputs(s)
+    o, lse = tca.attn_decode(q.cuda(), k.cuda(), v.cuda(), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_decode(q, k, v, 1, scale)
+    ctx = f"decode {B,Hq,Hkv,Nq,Nk,d} scale={scale}"
+    check("o", o, ro, "bf16", False, ctx)
+    check("lse", lse, rl, "bf16", False, ctx)
+    if scale == 0.0:
+        pos = np.arange(Nk - Nq, Nk) + 1.0
+        assert np.allclose(lse.cpu().numpy(), np.log(pos)[None, None, :], atol=1e-5)
+
+
 def test_decode_peaked_softmax():
     # the stress distribution (Q, K ~ N(0, 3^2)) over a long cache: the running
     # max moves often and the lazy rescale must keep every split exact
