@@ -297,8 +297,9 @@ def test_decode_noops_and_workspace(L):
     assert dec(L, B=0, causal=3, **nul) == EINVAL
     # one split: no workspace; more: partial outputs and LSEs, 256-byte parts, unless
     # the call has >= 256 row groups of <= 16 splits each, merged inside one workgroup
-    # (bf16 calls with 8+ rows per KV head at d = 128 take the matrix-core split
-    # instead, when its partials fit the no-allocation scratch)
+    # (bf16 calls at d = 64 or 128 with 3+ rows per KV head merge in the matrix-core
+    # form from 256 chunks of 32 rows; with fewer chunks, 8+ rows at d = 128 take the
+    # matrix-core split instead, when its partials fit the no-allocation scratch)
     assert L.attn_decode_workspace_bytes(BF16, 1, 2, 1, 1, 64, 64) == 0
     n = L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 1, 1024, 64)              # 32 groups of 16 splits
     rows = 8 * 12
@@ -312,10 +313,11 @@ def test_decode_noops_and_workspace(L):
     assert L.attn_decode_workspace_bytes(F32, 128, 8, 2, 1, 600, 64) > 0         # 10 splits
     assert L.attn_decode_workspace_bytes(BF16, 128, 8, 2, 1, 600, 64) == 0    # 4 rows: merged
     assert L.attn_decode_workspace_bytes(BF16, 256, 8, 1, 1, 512, 64) == 0    # 8 rows at d = 64: merged
-    n = L.attn_decode_workspace_bytes(BF16, 256, 8, 1, 1, 512, 128)           # 8 rows at d = 128: matrix cores
-    rows, nsplit = 256 * 8, 8
-    assert n == ((nsplit * rows * 128 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
+    assert L.attn_decode_workspace_bytes(BF16, 256, 8, 1, 1, 512, 128) == 0   # 8 rows at d = 128: merged
     assert L.attn_decode_workspace_bytes(F32, 256, 8, 1, 1, 512, 128) == 0    # float32: merged
+    n = L.attn_decode_workspace_bytes(BF16, 128, 16, 1, 1, 512, 128)  # 256 8-row chunks, 128 of 32 rows
+    rows, nsplit = 128 * 16, 8                                         # -> the matrix-core split
+    assert n == ((nsplit * rows * 128 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
     assert L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 2, 1, 64) == 0   # invalid: Nq > Nk
 
 

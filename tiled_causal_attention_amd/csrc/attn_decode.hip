@@ -415,10 +415,142 @@ decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 // kernel's: o, lse when nsplit == 1, else the normalised partial and its LSE
 // (log2 units) per split for the merge kernel.
 namespace decm {
-constexpr int BC = 64;   // keys per tile
+constexpr int BC = 64;           // keys per tile
+constexpr int kFusedWaves = 8;   // waves of the workgroup-merged form
 using dec::kTau;
 }
 
+// One wave's running state over the tiles it has seen: the unnormalised O^T
+// accumulator (lane (h, r): dims 32x + 8(e/4) + 4h + e%4 of row r), the running
+// max in log2 units, and this lane's half of the sum of the fp16-rounded
+// probabilities.
+template <int D>
+struct MfmaDecState {
+    f32x16 oacc[D / 32];
+    float m_s, l_run;
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int x = 0; x < D / 32; ++x) oacc[x] = f32x16{};
+        m_s = -0x1p100f;   // finite, far below any score: the first rescale factor is 0
+        l_run = 0.f;
+    }
+};
+
+// This lane's row (column r of the products) of a (batch, KV head, 32-row chunk):
+// its global index (b, hq, i), whether it exists, and its sequence position.
+struct MfmaDecRow {
+    size_t grow;
+    bool ok;
+    int pos;
+    __device__ __forceinline__ MfmaDecRow(int b, int hkv, int rc, int r, int Hq, int Hkv, int Nq, int Nk) {
+        const int G = Hq / Hkv, R = G * Nq;
+        const int rho = rc * 32 + r;
+        ok = rho < R;
+        const int rv = ok ? rho : R - 1;
+        const int g = rv / Nq, i = rv % Nq;
+        grow = ((size_t)b * Hq + hkv * G + g) * Nq + i;
+        pos = Nk - Nq + i;
+    }
+};
+
+// The row's query as B operands (bf16, the scale's sign folded in; zero for a row
+// past the chunk's rows).
+template <int D>
+__device__ __forceinline__ void mfma_dec_load_q(bf16x8 (&qb)[D / 16], const bf16_t* q, const MfmaDecRow& row,
+                                                const ScoreScale& sc, int h) {
+    const bf16_t* qrow = q + row.grow * D + 8 * h;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
+        qb[c] = row.ok ? __builtin_bit_cast(bf16x8, apply_qsign(x, sc)) : bf16x8{};
+    }
+}
+
+// Keys [t0, t0 + 64) of the unit, keys below `lim` visible to this lane's row. The
+// V tile is copied into this wave's LDS buffer Vs (swizzled rows, bf16 bits) and
+// the K rows are loaded as A operands; the wave waits for both (one round trip),
+// then S^T = K Q^T, the online softmax down each column and O^T += V^T P^T with P
+// rounded to fp16 and V^T read transposed (converted to fp16 at the read). Only
+// this wave touches Vs: the fences keep its LDS reads of the previous tile ahead
+// of the copies and its reads of this tile behind their arrival.
+template <int D>
+__device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 (&qb)[D / 16],
+                                              __amdgpu_buffer_rsrc_t krs, const bf16_t* vunit, int Nk, int t0,
+                                              int lim, _Float16* Vs, float sl2, int lane) {
+    using namespace decm;
+    constexpr int DC = D / 16, DB = D / 32;
+    constexpr int NCOPY = BC * D * 2 / 1024;   // 1 KB direct copies per V tile
+    const int h = lane >> 5, r = lane & 31;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    {
+        const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vunit + (size_t)t0 * D, (uint32_t)((Nk - t0) * D * 2));
+#pragma unroll
+        for (int u = 0; u < NCOPY; ++u) lds_copy16(vrs, Vs + u * 512, tile_copy_src<D>(u, lane));
+    }
+    const int krow_a = perm32(r);
+    u32x4 ka[2][DC];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c = 0; c < DC; ++c)
+            ka[kb][c] = buf_load16(krs, (uint32_t)(((t0 + 32 * kb + krow_a) * D + 16 * c + 8 * h) * 2));
+    wait_vmem_all();   // the V copies are in LDS
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // ---- S^T = K Q^T; accumulator e of block kb: key t0 + 32 kb + 16(e/8) + 8h + e%8
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+#pragma unroll
+        for (int c = 0; c < DC; ++c) s[kb] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[kb][c]), qb[c], s[kb]);
+        const int lm = lim - t0 - 32 * kb - 8 * h;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = (16 * (e >> 3) + (e & 7) < lm) ? s[kb][e] : -INFINITY;
+    }
+    // ---- online softmax down each column, lazy rescale (log2 units)
+    const float mt = max_halves(vmax(max16(s[0]), max16(s[1]))) * sl2;
+    if (__any(mt > st.m_s + kTau)) {
+        const float m_new = vmax(st.m_s, mt);
+        const float alpha = fast_exp2(st.m_s - m_new);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int x = 0; x < DB; ++x)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) st.oacc[x][e] *= alpha;
+        st.m_s = m_new;
+    }
+    // ---- O^T += V^T P^T, P in fp16 (its rounded values are the ones summed)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+            uint32_t pk[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                pk[t] = pack_f16(fast_exp2(fmaf(s[kb][8 * c2 + 2 * t], sl2, -st.m_s)),
+                                 fast_exp2(fmaf(s[kb][8 * c2 + 2 * t + 1], sl2, -st.m_s)));
+                st.l_run = add_f16_pair(pk[t], st.l_run);
+            }
+            const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+#pragma unroll
+            for (int x = 0; x < DB; ++x) {
+                const f16x8 vt = tile_tr_operand<D>(Vs, 32 * kb + 16 * c2, 32 * x, h, r);   // bf16 bits
+                const f16x8 a = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, vt)));
+                st.oacc[x] = mfma_f16(a, pb, st.oacc[x]);
+            }
+        }
+}
+
+// Matrix-core split for bf16 inputs at d = 64 and 128. One wave per (batch, KV
+// head, row chunk, key split) item, as decode_split_kernel, but the chunk holds
+// 32 rows of the GQA group -- the columns of 32x32x16 products -- and each
+// 64-key tile is the forward's step with the roles kept (mfma_dec_tile): K rows
+// as the A operand straight from global memory (rows past Nk read as zero), the
+// chunk's queries as the B operand, V through LDS. Rows past the chunk's G * Nq
+// rows carry zero queries and are not stored. The scale's sign is folded into Q
+// (ScoreScale), so the exponent's multiplier is positive and masked keys stay at
+// -inf. Output as the split kernel's: o, lse when nsplit == 1, else the
+// normalised partial and its LSE (log2 units) per split for the merge kernel.
 template <typename OT, int D>
 __global__ void __launch_bounds__(64, (D == 64) ? 3 : 2)   // waves per SIMD at least
 decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
@@ -426,132 +558,121 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, c
                    float* __restrict__ lpart, int Hq, int Hkv, int Nq, int Nk, int causal, ScoreScale sc,
                    int nrc, int nsplit, int split_len, int nrows) {
     using namespace decm;
-    constexpr int DC = D / 16, DB = D / 32;
-    constexpr int NCOPY = BC * D * 2 / 1024;   // 1 KB direct copies per V tile
+    constexpr int DB = D / 32;
     __shared__ __attribute__((aligned(16))) _Float16 Vs[BC * D];
     const int lane = threadIdx.x, h = lane >> 5, r = lane & 31;
     const int item = blockIdx.x;
     const int split = item % nsplit, rest = item / nsplit;
     const int rc = rest % nrc, unit = rest / nrc;
     const int b = unit / Hkv, hkv = unit % Hkv;
-    const int G = Hq / Hkv, R = G * Nq;
-
-    // this lane's row: column r of the products
-    const int rho = rc * 32 + r;
-    const bool ok = rho < R;
-    const int rv = ok ? rho : R - 1;
-    const int g = rv / Nq, i = rv % Nq;
-    const size_t grow = ((size_t)b * Hq + hkv * G + g) * Nq + i;
+    const MfmaDecRow row(b, hkv, rc, r, Hq, Hkv, Nq, Nk);
     const int k0 = split * split_len, k1 = min(Nk, k0 + split_len);
-    const int lim = !ok ? k0 : (causal ? min(k1, Nk - Nq + i + 1) : k1);   // keys below lim are visible
+    const int lim = !row.ok ? k0 : (causal ? min(k1, row.pos + 1) : k1);   // keys below lim are visible
 
-    bf16x8 qb[DC];
-    {
-        const bf16_t* qrow = q + grow * D + 8 * h;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-            qb[c] = ok ? __builtin_bit_cast(bf16x8, apply_qsign(x, sc)) : bf16x8{};
-        }
-    }
+    bf16x8 qb[D / 16];
+    mfma_dec_load_q<D>(qb, q, row, sc, h);
     const size_t kvoff = (size_t)unit * Nk * D;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
-    const int krow_a = perm32(r);
-    const float sl2 = sc.sl2;
+    MfmaDecState<D> st;
+    st.init();
+    for (int t0 = k0; t0 < k1; t0 += BC) mfma_dec_tile<D>(st, qb, krs, v + kvoff, Nk, t0, lim, Vs, sc.sl2, lane);
 
-    f32x16 oacc[DB];
-#pragma unroll
-    for (int x = 0; x < DB; ++x) oacc[x] = f32x16{};
-    float m_s = -0x1p100f;   // finite, far below any score: the first rescale factor is 0
-    float l_run = 0.f;
-
-    for (int t0 = k0; t0 < k1; t0 += BC) {
-        if (t0 > k0) __syncthreads();   // the previous tile's V reads are done before the copies land
-        {
-            const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kvoff + (size_t)t0 * D, (uint32_t)((Nk - t0) * D * 2));
-#pragma unroll
-            for (int u = 0; u < NCOPY; ++u) lds_copy16(vrs, Vs + u * 512, tile_copy_src<D>(u, lane));
-        }
-        u32x4 ka[2][DC];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int c = 0; c < DC; ++c)
-                ka[kb][c] = buf_load16(krs, (uint32_t)(((t0 + 32 * kb + krow_a) * D + 16 * c + 8 * h) * 2));
-        wait_vmem_all();   // the V copies are in LDS
-        __syncthreads();
-        // ---- S^T = K Q^T; accumulator e of block kb: key t0 + 32 kb + 16(e/8) + 8h + e%8
-        f32x16 s[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            s[kb] = f32x16{};
-#pragma unroll
-            for (int c = 0; c < DC; ++c) s[kb] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[kb][c]), qb[c], s[kb]);
-            const int lm = lim - t0 - 32 * kb - 8 * h;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[kb][e] = (16 * (e >> 3) + (e & 7) < lm) ? s[kb][e] : -INFINITY;
-        }
-        // ---- online softmax down each column, lazy rescale (log2 units)
-        const float mt = max_halves(vmax(max16(s[0]), max16(s[1]))) * sl2;
-        if (__any(mt > m_s + kTau)) {
-            const float m_new = vmax(m_s, mt);
-            const float alpha = fast_exp2(m_s - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int x = 0; x < DB; ++x)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) oacc[x][e] *= alpha;
-            m_s = m_new;
-        }
-        // ---- O^T += V^T P^T, P in fp16 (its rounded values are the ones summed)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int c2 = 0; c2 < 2; ++c2) {
-                uint32_t pk[4];
-#pragma unroll
-                for (int t = 0; t < 4; ++t) {
-                    pk[t] = pack_f16(fast_exp2(fmaf(s[kb][8 * c2 + 2 * t], sl2, -m_s)),
-                                     fast_exp2(fmaf(s[kb][8 * c2 + 2 * t + 1], sl2, -m_s)));
-                    l_run = add_f16_pair(pk[t], l_run);
-                }
-                const f16x8 pb = __builtin_bit_cast(f16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-#pragma unroll
-                for (int x = 0; x < DB; ++x) {
-                    const f16x8 vt = tile_tr_operand<D>(Vs, 32 * kb + 16 * c2, 32 * x, h, r);   // bf16 bits
-                    const f16x8 a = __builtin_bit_cast(f16x8, bf16x8_to_f16x8(__builtin_bit_cast(u32x4, vt)));
-                    oacc[x] = mfma_f16(a, pb, oacc[x]);
-                }
-            }
-    }
-
-    // ---- this split's normalised output and LSE; lane (h, r) holds dims 32x + 8(e/4) + 4h + e%4
-    const float l_tot = sum_halves(l_run);
-    if (!ok) return;
+    // ---- this split's normalised output and LSE
+    const float l_tot = sum_halves(st.l_run);
+    if (!row.ok) return;
     const bool any = l_tot > 0.f;
     const float inv = any ? 1.f / l_tot : 0.f;
-    const float l2 = any ? m_s + __log2f(l_tot) : -INFINITY;
+    const float l2 = any ? st.m_s + __log2f(l_tot) : -INFINITY;
     if (nsplit == 1) {
-        OT* orow = o + grow * D;
+        OT* orow = o + row.grow * D;
 #pragma unroll
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
                 store_out4(orow + 32 * x + 8 * a4 + 4 * h,
-                           f32x4{oacc[x][4 * a4] * inv, oacc[x][4 * a4 + 1] * inv, oacc[x][4 * a4 + 2] * inv,
-                                 oacc[x][4 * a4 + 3] * inv});
-        if (h == 0) lse[grow] = l2 * kLn2;
+                           f32x4{st.oacc[x][4 * a4] * inv, st.oacc[x][4 * a4 + 1] * inv,
+                                 st.oacc[x][4 * a4 + 2] * inv, st.oacc[x][4 * a4 + 3] * inv});
+        if (h == 0) lse[row.grow] = l2 * kLn2;
     } else {
-        const size_t prow = (size_t)split * nrows + grow;
+        const size_t prow = (size_t)split * nrows + row.grow;
         float* orow = opart + prow * D;
 #pragma unroll
         for (int x = 0; x < DB; ++x)
 #pragma unroll
             for (int a4 = 0; a4 < 4; ++a4)
                 *reinterpret_cast<f32x4*>(orow + 32 * x + 8 * a4 + 4 * h) =
-                    f32x4{oacc[x][4 * a4] * inv, oacc[x][4 * a4 + 1] * inv, oacc[x][4 * a4 + 2] * inv,
-                          oacc[x][4 * a4 + 3] * inv};
+                    f32x4{st.oacc[x][4 * a4] * inv, st.oacc[x][4 * a4 + 1] * inv, st.oacc[x][4 * a4 + 2] * inv,
+                          st.oacc[x][4 * a4 + 3] * inv};
         if (h == 0) lpart[prow] = l2;
+    }
+}
+
+// The workgroup-merged form of the matrix-core split: one workgroup of 8 waves per
+// (batch, KV head, 32-row chunk); wave w takes the 64-key tiles w, w + 8, ... of
+// the whole cache with one running state, leaves its unnormalised output (over
+// its V buffer, [32 rows][D] floats at merge_off positions) and its rows' max and
+// sum in LDS, and after one barrier the workgroup merges the 8 states in wave
+// order: M = max_w m_w, L = sum_w 2^(m_w - M) l_w, O = sum_w 2^(m_w - M) O_w / L.
+// One launch, no workspace. The wave holding key 0 gives every row a finite max.
+template <typename OT, int D>
+__global__ void __launch_bounds__(64 * decm::kFusedWaves)
+decode_mfma_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                         OT* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk, int causal,
+                         ScoreScale sc, int nrc) {
+    using namespace decm;
+    constexpr int W = kFusedWaves, DB = D / 32;
+    static_assert(32 * D * 4 == BC * D * 2, "a wave's partial output fills its V buffer");
+    __shared__ __attribute__((aligned(16))) _Float16 Vs[W][BC * D];
+    __shared__ float ml[W][2][32];
+    const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int rc = blockIdx.x % nrc, unit = blockIdx.x / nrc;
+    const int b = unit / Hkv, hkv = unit % Hkv;
+    const MfmaDecRow row(b, hkv, rc, r, Hq, Hkv, Nq, Nk);
+    const int lim = !row.ok ? 0 : (causal ? min(Nk, row.pos + 1) : Nk);
+
+    bf16x8 qb[D / 16];
+    mfma_dec_load_q<D>(qb, q, row, sc, h);
+    const size_t kvoff = (size_t)unit * Nk * D;
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
+    MfmaDecState<D> st;
+    st.init();
+    const int ntiles = (Nk + BC - 1) / BC;
+    for (int t = w; t < ntiles; t += W) mfma_dec_tile<D>(st, qb, krs, v + kvoff, Nk, t * BC, lim, Vs[w], sc.sl2, lane);
+
+    // ---- this wave's state into LDS (its V buffer, whose reads are done)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    float* po = reinterpret_cast<float*>(Vs[w]);
+#pragma unroll
+    for (int x = 0; x < DB; ++x)
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4)
+            *reinterpret_cast<f32x4*>(po + merge_off<D>(r, 8 * x + 2 * a4 + h)) =
+                f32x4{st.oacc[x][4 * a4], st.oacc[x][4 * a4 + 1], st.oacc[x][4 * a4 + 2], st.oacc[x][4 * a4 + 3]};
+    const float l_tot = sum_halves(st.l_run);
+    if (h == 0) {
+        ml[w][0][r] = st.m_s;
+        ml[w][1][r] = l_tot;
+    }
+    __syncthreads();
+    // ---- merge: thread t takes element (row, column) t, t + 64 W, ... of the chunk
+    const int R = (Hq / Hkv) * Nq;
+    for (int idx = threadIdx.x; idx < 32 * D; idx += 64 * W) {
+        const int rr = idx / D, c = idx % D;
+        if (rc * 32 + rr >= R) break;   // rows grow with idx
+        float M = ml[0][0][rr];
+#pragma unroll
+        for (int ww = 1; ww < W; ++ww) M = vmax(M, ml[ww][0][rr]);
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) {
+            const float wt = fast_exp2(ml[ww][0][rr] - M);
+            L = fmaf(wt, ml[ww][1][rr], L);
+            acc = fmaf(wt, reinterpret_cast<const float*>(Vs[ww])[merge_off<D>(rr, c >> 2) + (c & 3)], acc);
+        }
+        const MfmaDecRow orow(b, hkv, rc, rr, Hq, Hkv, Nq, Nk);
+        store_out1(o + orow.grow * D + c, acc / L);
+        if (c == 0) lse[orow.grow] = (M + __log2f(L)) * kLn2;
     }
 }
 
@@ -655,22 +776,29 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32)
     p.mfma = false;
     // matrix-core splits, row chunks of 32 rows: measured faster from 3 rows per KV
     // head (2 at d = 64); with one or two rows the 32-column products sit nearly
-    // empty and the VALU split, whose K reads are whole rows, is faster. Against the
-    // workgroup-merged VALU form they win only at d = 128 with 8 or more rows (the
-    // merged form's 8-row waves), and take its place there when their split partials
-    // fit the no-allocation scratch (so both entry points keep serving the same calls).
+    // empty and the VALU split, whose K reads are whole rows, is faster. With at
+    // least 256 chunks (one workgroup per CU) their workgroup-merged form serves the
+    // call; otherwise they replace the VALU's merged form only at d = 128 with 8 or
+    // more rows, and only when their split partials fit the no-allocation scratch
+    // (so both entry points keep serving the same calls).
     if (!in32 && (d == 64 || d == 128) && (R >= 3 || (R == 2 && d == 64))) {
         DecodePlan m = p;
         m.mfma = true;
         m.fused = false;
         m.rm = 32;
         m.nrc = (R + 31) / 32;
-        plan_splits(m, (long long)B * Hkv * m.nrc, Nk);
+        const long long chunks = (long long)B * Hkv * m.nrc;
+        plan_splits(m, chunks, Nk);
         const size_t rows = (size_t)B * Hq * Nq;
         const size_t part = m.nsplit <= 1 ? 0
                                           : ws_round((size_t)m.nsplit * rows * d * sizeof(float)) +
                                                 ws_round((size_t)m.nsplit * rows * sizeof(float));
-        if (!p.fused || (d == 128 && R >= 8 && part <= kDecodeScratchBytes)) p = m;
+        if (chunks >= dec::kFusedMinGroups && m.nsplit > 1) {
+            m.fused = true;   // the waves take 64-key tiles in turn; nsplit is not used
+            p = m;
+        } else if (!p.fused || (d == 128 && R >= 8 && part <= kDecodeScratchBytes)) {
+            p = m;
+        }
     }
     return p;
 }
@@ -709,6 +837,13 @@ static void split_partials(const DecodeArgs& a, const DecodePlan& p, int nrows, 
 
 template <typename OT, int D>
 static hipError_t launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+    if (p.fused) {
+        hipLaunchKernelGGL((decode_mfma_fused_kernel<OT, D>), dim3((unsigned)(a.B * a.Hkv * p.nrc)),
+                           dim3(64 * decm::kFusedWaves), 0, st, (const bf16_t*)a.q, (const bf16_t*)a.k,
+                           (const bf16_t*)a.v, (OT*)a.o, a.lse, a.Hq, a.Hkv, a.Nq, a.Nk, a.causal,
+                           score_scale(a.scale), p.nrc);
+        return hipGetLastError();
+    }
     const int nitems = a.B * a.Hkv * p.nrc * p.nsplit;
     const int nrows = a.B * a.Hq * a.Nq;
     float *opart, *lpart;

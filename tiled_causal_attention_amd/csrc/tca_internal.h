@@ -99,7 +99,7 @@ struct DecodeArgs {
 struct DecodePlan {
     int rm, nrc, nsplit, split_len;
     bool fused;   // the splits of a row chunk are the waves of one workgroup, merged in LDS
-    bool mfma;    // bf16 inputs, d 64 or 128, not fused: decode_mfma_kernel's 32-row chunks
+    bool mfma;    // bf16 inputs, d 64 or 128: the matrix-core kernels' 32-row chunks (fused: merged form)
 };
 DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32);
 size_t decode_workspace_size(bool in32, int B, int Hq, int Hkv, int Nq, int Nk, int d);
