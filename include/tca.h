@@ -295,17 +295,19 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
  *   GQA head map, scale and the definitions of o and lse as for attn_fwd.
  * The keys are split into ranges processed in parallel, whose partial outputs
  * are merged through their log-sum-exps. When a call has at least 256 (batch,
- * KV head, query-row chunk) groups and up to 16 ranges per group (8 when a wave
- * holds 8 query rows, or 4 float32 ones), a group's ranges are the waves of one
- * workgroup and merge in on-chip memory: one launch, no workspace -- except bf16
- * calls at d = 128 with 8 or more query rows per KV head whose partials fit
- * ATTN_DECODE_SCRATCH_BYTES, which take the matrix-core ranges below (measured
- * faster there). Otherwise each range writes its
+ * KV head, query-row chunk) groups, a group's ranges are the waves of one
+ * workgroup and merge in on-chip memory: one launch, no workspace. On the vector
+ * units that needs up to 16 ranges per group (8 when a wave holds 8 query rows,
+ * or 4 float32 ones); on the matrix cores (below) the chunks hold 32 rows and
+ * 8 waves take the key ranges in turn. With fewer groups, bf16 calls at d = 128
+ * with 8 or more query rows per KV head whose partials fit
+ * ATTN_DECODE_SCRATCH_BYTES take the matrix-core ranges even where the vector
+ * units would merge in a workgroup (measured faster). Otherwise each range writes its
  * partial output and log-sum-exp into `workspace` (at least
  * attn_decode_workspace_bytes(...) bytes of device memory, 16-byte aligned;
  * NULL allowed when that is 0) and a second kernel merges them. Arithmetic:
  * bf16 inputs at d = 64 or 128 with at least 3 query rows per KV head (Hq/Hkv *
- * Nq; 2 at d = 64), when not merged in one workgroup, run on the matrix cores as
+ * Nq; 2 at d = 64) run on the matrix cores as
  * the forward does (bf16 Q K^T, fp32 accumulation, probabilities rounded to fp16
  * for P V, so |x| < 65504 is required of v as of attn_fwd's inputs); every other
  * call computes in float32 on the vector units.

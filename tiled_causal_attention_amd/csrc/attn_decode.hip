@@ -23,11 +23,13 @@
 //    row chunk, split) item and the splits run in parallel. Each writes a
 //    normalised partial output and its LSE; a second kernel merges the splits
 //    through the LSEs: LSE = log sum_s e^LSE_s, O = sum_s e^(LSE_s - LSE) O_s.
-//    A single split writes the result directly. With at most 16 splits (8 for
-//    8-row waves) and at least 256 (batch, KV head, row chunk) groups, the splits
-//    of a group are instead the waves of one workgroup, which merge through LDS:
-//    one launch and no workspace. With fewer groups the CUs would not all be
-//    streaming, so the splits stay spread over the chip.
+//    A single split writes the result directly. With at least 256 (batch, KV
+//    head, row chunk) groups the splits of a group are instead the waves of one
+//    workgroup, which merge through LDS: one launch and no workspace
+//    (decode_fused_kernel, at most 16 splits, 8 for 8-row waves;
+//    decode_mfma_fused_kernel, 8 waves taking the 64-key tiles in turn). With
+//    fewer groups the CUs would not all be streaming, so the splits stay spread
+//    over the chip.
 //  * Lane layout: lane = CPR * slot + c, CPR = d / 8. A slot is one key, c is an
 //    8-element chunk of its row, so one load instruction covers 64/CPR
 //    consecutive whole K (or V) rows: 1 KB of contiguous bf16 per wave. Each
