@@ -401,21 +401,12 @@ decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
     }
 }
 
-// Matrix-core split for bf16 inputs at d = 64 and 128. One wave per (batch, KV
-// head, row chunk, key split) item, as decode_split_kernel, but the chunk holds
-// 32 rows of the GQA group -- the columns of 32x32x16 products -- and each
-// 64-key tile is the forward's step with the roles kept: S^T = K Q^T with this
-// lane's K rows as the A operand (read straight from global memory: rows past
-// Nk read as zero) and the chunk's queries as the B operand, the online softmax
-// down each column, and O^T += V^T P^T with P rounded to fp16 from the score
-// accumulator and V^T read transposed from LDS. The V tile reaches LDS by direct
-// copies (the dK/dV pass's swizzled rows, bf16 bits, converted to fp16 at the
-// read), so the wave's only wait per tile is one round trip for K and V
-// together. Rows past the chunk's G * Nq rows carry zero queries and are not
-// stored. The scale's sign is folded into Q (ScoreScale), so the exponent's
-// multiplier is positive and masked keys stay at -inf. Output as the split
-// kernel's: o, lse when nsplit == 1, else the normalised partial and its LSE
-// (log2 units) per split for the merge kernel.
+// ---------------------------------------------------------------- matrix cores
+// The matrix-core decode (bf16 inputs, d = 64 or 128): a chunk of 32 rows of a
+// KV head's GQA group is the column set of 32x32x16 products, and each 64-key
+// tile of the cache takes the forward's step (mfma_dec_tile). Two kernels use
+// it: a split kernel (one wave per key split, merged by decode_merge_kernel) and
+// a workgroup-merged form for calls with many chunks.
 namespace decm {
 constexpr int BC = 64;           // keys per tile
 constexpr int kFusedWaves = 8;   // waves of the workgroup-merged form
