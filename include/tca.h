@@ -294,12 +294,13 @@ size_t attn_decode_workspace_bytes(attn_dtype dtype, int B, int Hq, int Hkv, int
  *   With Nq = Nk the result is attn_fwd's (up to rounding order).
  *   GQA head map, scale and the definitions of o and lse as for attn_fwd.
  * The keys are split into ranges processed in parallel, whose partial outputs
- * are merged through their log-sum-exps. When a call has at least 256 (batch,
- * KV head, query-row chunk) groups, a group's ranges are the waves of one
- * workgroup and merge in on-chip memory: one launch, no workspace. On the vector
- * units that needs up to 16 ranges per group (8 when a wave holds 8 query rows,
- * or 4 float32 ones); on the matrix cores (below) the chunks hold 32 rows and
- * 8 waves take the key ranges in turn. With fewer groups, bf16 calls at d = 128
+ * are merged through their log-sum-exps. When a call has enough (batch, KV
+ * head, query-row chunk) groups, a group's ranges are the waves of one workgroup
+ * and merge in on-chip memory: one launch, no workspace. On the vector units
+ * that takes at least 256 groups and up to 16 ranges per group (8 when a wave
+ * holds 8 query rows, or 4 float32 ones); on the matrix cores (below) at least
+ * 128 chunks of 32 rows, whose 8 waves take the key ranges in turn. With fewer
+ * groups, bf16 calls at d = 128
  * with 8 or more query rows per KV head whose partials fit
  * ATTN_DECODE_SCRATCH_BYTES take the matrix-core ranges even where the vector
  * units would merge in a workgroup (measured faster). Otherwise each range writes its

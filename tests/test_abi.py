@@ -298,7 +298,7 @@ def test_decode_noops_and_workspace(L):
     # one split: no workspace; more: partial outputs and LSEs, 256-byte parts, unless
     # the call has >= 256 row groups of <= 16 splits each, merged inside one workgroup
     # (bf16 calls at d = 64 or 128 with 3+ rows per KV head merge in the matrix-core
-    # form from 256 chunks of 32 rows; with fewer chunks, 8+ rows at d = 128 take the
+    # form from 128 chunks of 32 rows; with fewer chunks, 8+ rows at d = 128 take the
     # matrix-core split instead, when its partials fit the no-allocation scratch)
     assert L.attn_decode_workspace_bytes(BF16, 1, 2, 1, 1, 64, 64) == 0
     n = L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 1, 1024, 64)              # 32 groups of 16 splits
@@ -315,8 +315,10 @@ def test_decode_noops_and_workspace(L):
     assert L.attn_decode_workspace_bytes(BF16, 256, 8, 1, 1, 512, 64) == 0    # 8 rows at d = 64: merged
     assert L.attn_decode_workspace_bytes(BF16, 256, 8, 1, 1, 512, 128) == 0   # 8 rows at d = 128: merged
     assert L.attn_decode_workspace_bytes(F32, 256, 8, 1, 1, 512, 128) == 0    # float32: merged
-    n = L.attn_decode_workspace_bytes(BF16, 128, 16, 1, 1, 512, 128)  # 256 8-row chunks, 128 of 32 rows
-    rows, nsplit = 128 * 16, 8                                         # -> the matrix-core split
+    assert L.attn_decode_workspace_bytes(BF16, 32, 12, 4, 1, 1024, 64) == 0  # 128 chunks: merged
+    assert L.attn_decode_workspace_bytes(BF16, 16, 12, 4, 1, 1024, 64) > 0   # 64 chunks: split
+    n = L.attn_decode_workspace_bytes(BF16, 64, 32, 1, 1, 512, 128)   # 256 8-row chunks, 64 of 32 rows
+    rows, nsplit = 64 * 32, 8                                          # -> the matrix-core split
     assert n == ((nsplit * rows * 128 * 4 + 255) // 256 + (nsplit * rows * 4 + 255) // 256) * 256
     assert L.attn_decode_workspace_bytes(BF16, 8, 12, 4, 2, 1, 64) == 0   # invalid: Nq > Nk
 

@@ -23,13 +23,13 @@
 //    row chunk, split) item and the splits run in parallel. Each writes a
 //    normalised partial output and its LSE; a second kernel merges the splits
 //    through the LSEs: LSE = log sum_s e^LSE_s, O = sum_s e^(LSE_s - LSE) O_s.
-//    A single split writes the result directly. With at least 256 (batch, KV
-//    head, row chunk) groups the splits of a group are instead the waves of one
+//    A single split writes the result directly. With enough (batch, KV head,
+//    row chunk) groups the splits of a group are instead the waves of one
 //    workgroup, which merge through LDS: one launch and no workspace
-//    (decode_fused_kernel, at most 16 splits, 8 for 8-row waves;
-//    decode_mfma_fused_kernel, 8 waves taking the 64-key tiles in turn). With
-//    fewer groups the CUs would not all be streaming, so the splits stay spread
-//    over the chip.
+//    (decode_fused_kernel from 256 groups, at most 16 splits, 8 for 8-row waves;
+//    decode_mfma_fused_kernel from 128 chunks of 32 rows, 8 waves taking the
+//    64-key tiles in turn). With fewer groups the CUs would not all be
+//    streaming, so the splits stay spread over the chip.
 //  * Lane layout: lane = CPR * slot + c, CPR = d / 8. A slot is one key, c is an
 //    8-element chunk of its row, so one load instruction covers 64/CPR
 //    consecutive whole K (or V) rows: 1 KB of contiguous bf16 per wave. Each
@@ -410,6 +410,10 @@ decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 namespace decm {
 constexpr int BC = 64;           // keys per tile
 constexpr int kFusedWaves = 8;   // waves of the workgroup-merged form
+// 32-row chunks from which the workgroup-merged form serves a call: measured
+// faster than split kernel + merge kernel from 128 chunks on (caches of 1-4K keys),
+// equal or slower below
+constexpr long long kFusedMinChunks = 128;
 using dec::kTau;
 }
 
@@ -770,10 +774,10 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32)
     // matrix-core splits, row chunks of 32 rows: measured faster from 3 rows per KV
     // head (2 at d = 64); with one or two rows the 32-column products sit nearly
     // empty and the VALU split, whose K reads are whole rows, is faster. With at
-    // least 256 chunks (one workgroup per CU) their workgroup-merged form serves the
-    // call; otherwise they replace the VALU's merged form only at d = 128 with 8 or
-    // more rows, and only when their split partials fit the no-allocation scratch
-    // (so both entry points keep serving the same calls).
+    // least 128 chunks their workgroup-merged form serves the call; otherwise they
+    // replace the VALU's merged form only at d = 128 with 8 or more rows, and only
+    // when their split partials fit the no-allocation scratch (so both entry points
+    // keep serving the same calls).
     if (!in32 && (d == 64 || d == 128) && (R >= 3 || (R == 2 && d == 64))) {
         DecodePlan m = p;
         m.mfma = true;
@@ -786,7 +790,7 @@ DecodePlan decode_plan(int B, int Hq, int Hkv, int Nq, int Nk, int d, bool in32)
         const size_t part = m.nsplit <= 1 ? 0
                                           : ws_round((size_t)m.nsplit * rows * d * sizeof(float)) +
                                                 ws_round((size_t)m.nsplit * rows * sizeof(float));
-        if (chunks >= dec::kFusedMinGroups && m.nsplit > 1) {
+        if (chunks >= decm::kFusedMinChunks && m.nsplit > 1) {
             m.fused = true;   // the waves take 64-key tiles in turn; nsplit is not used
             p = m;
         } else if (!p.fused || (d == 128 && R >= 8 && part <= kDecodeScratchBytes)) {
