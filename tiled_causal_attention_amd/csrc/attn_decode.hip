@@ -410,6 +410,11 @@ decode_fused_kernel(const T* __restrict__ q, const T* __restrict__ k, const T* _
 namespace decm {
 constexpr int BC = 64;           // keys per tile
 constexpr int kFusedWaves = 8;   // waves of the workgroup-merged form
+// K reaches the A operands through LDS too (direct copies of whole rows) at d = 64:
+// 1-10% faster there than each lane's 32-byte global loads; at d = 128 the second
+// 16 KB tile per wave costs occupancy (the wide decode 19.8 -> 22.0 us), so K stays
+// in registers
+template <int D> constexpr bool kKLds = (D == 64);
 // 32-row chunks from which the workgroup-merged form serves a call: measured
 // faster than split kernel + merge kernel from 128 chunks on (caches of 1-4K keys),
 // equal or slower below
@@ -464,16 +469,18 @@ __device__ __forceinline__ void mfma_dec_load_q(bf16x8 (&qb)[D / 16], const bf16
 }
 
 // Keys [t0, t0 + 64) of the unit, keys below `lim` visible to this lane's row. The
-// V tile is copied into this wave's LDS buffer Vs (swizzled rows, bf16 bits) and
-// the K rows are loaded as A operands; the wave waits for both (one round trip),
+// V tile is copied into this wave's LDS buffer Vs (swizzled rows, bf16 bits), and
+// the K tile into Ks (kKLds) or the K rows straight into registers as A operands;
+// the wave waits for both (one round trip),
 // then S^T = K Q^T, the online softmax down each column and O^T += V^T P^T with P
 // rounded to fp16 and V^T read transposed (converted to fp16 at the read). Only
 // this wave touches Vs: the fences keep its LDS reads of the previous tile ahead
 // of the copies and its reads of this tile behind their arrival.
 template <int D>
 __device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 (&qb)[D / 16],
-                                              __amdgpu_buffer_rsrc_t krs, const bf16_t* vunit, int Nk, int t0,
-                                              int lim, _Float16* Vs, float sl2, int lane) {
+                                              __amdgpu_buffer_rsrc_t krs, const bf16_t* kunit, const bf16_t* vunit,
+                                              int Nk, int t0, int lim, _Float16* Vs, _Float16* Ks, float sl2,
+                                              int lane) {
     using namespace decm;
     constexpr int DC = D / 16, DB = D / 32;
     constexpr int NCOPY = BC * D * 2 / 1024;   // 1 KB direct copies per V tile
@@ -483,15 +490,22 @@ __device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 
         const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vunit + (size_t)t0 * D, (uint32_t)((Nk - t0) * D * 2));
 #pragma unroll
         for (int u = 0; u < NCOPY; ++u) lds_copy16(vrs, Vs + u * 512, tile_copy_src<D>(u, lane));
+        if constexpr (kKLds<D>) {
+            const __amdgpu_buffer_rsrc_t ks = make_rsrc(kunit + (size_t)t0 * D, (uint32_t)((Nk - t0) * D * 2));
+#pragma unroll
+            for (int u = 0; u < NCOPY; ++u) lds_copy16(ks, Ks + u * 512, tile_copy_src<D>(u, lane));
+        }
     }
     const int krow_a = perm32(r);
     u32x4 ka[2][DC];
+    if constexpr (!kKLds<D>) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-            ka[kb][c] = buf_load16(krs, (uint32_t)(((t0 + 32 * kb + krow_a) * D + 16 * c + 8 * h) * 2));
-    wait_vmem_all();   // the V copies are in LDS
+            for (int c = 0; c < DC; ++c)
+                ka[kb][c] = buf_load16(krs, (uint32_t)(((t0 + 32 * kb + krow_a) * D + 16 * c + 8 * h) * 2));
+    }
+    wait_vmem_all();   // the copies are in LDS
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     // ---- S^T = K Q^T; accumulator e of block kb: key t0 + 32 kb + 16(e/8) + 8h + e%8
     f32x16 s[2];
@@ -499,7 +513,11 @@ __device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 
     for (int kb = 0; kb < 2; ++kb) {
         s[kb] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < DC; ++c) s[kb] = mfma_bf16(__builtin_bit_cast(bf16x8, ka[kb][c]), qb[c], s[kb]);
+        for (int c = 0; c < DC; ++c) {
+            const bf16x8 a = kKLds<D> ? *reinterpret_cast<const bf16x8*>(Ks + tile_off<D>(32 * kb + krow_a, 16 * c + 8 * h))
+                                      : __builtin_bit_cast(bf16x8, ka[kb][c]);
+            s[kb] = mfma_bf16(a, qb[c], s[kb]);
+        }
         const int lm = lim - t0 - 32 * kb - 8 * h;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[kb][e] = (16 * (e >> 3) + (e & 7) < lm) ? s[kb][e] : -INFINITY;
@@ -557,6 +575,7 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, c
     using namespace decm;
     constexpr int DB = D / 32;
     __shared__ __attribute__((aligned(16))) _Float16 Vs[BC * D];
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[kKLds<D> ? BC * D : 8];
     const int lane = threadIdx.x, h = lane >> 5, r = lane & 31;
     const int item = blockIdx.x;
     const int split = item % nsplit, rest = item / nsplit;
@@ -572,7 +591,8 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, c
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
     MfmaDecState<D> st;
     st.init();
-    for (int t0 = k0; t0 < k1; t0 += BC) mfma_dec_tile<D>(st, qb, krs, v + kvoff, Nk, t0, lim, Vs, sc.sl2, lane);
+    for (int t0 = k0; t0 < k1; t0 += BC)
+        mfma_dec_tile<D>(st, qb, krs, k + kvoff, v + kvoff, Nk, t0, lim, Vs, Ks, sc.sl2, lane);
 
     // ---- this split's normalised output and LSE
     const float l_tot = sum_halves(st.l_run);
@@ -620,6 +640,7 @@ decode_mfma_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     constexpr int W = kFusedWaves, DB = D / 32;
     static_assert(32 * D * 4 == BC * D * 2, "a wave's partial output fills its V buffer");
     __shared__ __attribute__((aligned(16))) _Float16 Vs[W][BC * D];
+    __shared__ __attribute__((aligned(16))) _Float16 Ks[kKLds<D> ? W : 1][kKLds<D> ? BC * D : 8];
     __shared__ float ml[W][2][32];
     const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -635,7 +656,8 @@ decode_mfma_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     MfmaDecState<D> st;
     st.init();
     const int ntiles = (Nk + BC - 1) / BC;
-    for (int t = w; t < ntiles; t += W) mfma_dec_tile<D>(st, qb, krs, v + kvoff, Nk, t * BC, lim, Vs[w], sc.sl2, lane);
+    for (int t = w; t < ntiles; t += W)
+        mfma_dec_tile<D>(st, qb, krs, k + kvoff, v + kvoff, Nk, t * BC, lim, Vs[w], Ks[kKLds<D> ? w : 0], sc.sl2, lane);
 
     // ---- this wave's state into LDS (its V buffer, whose reads are done)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
