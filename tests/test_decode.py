@@ -92,6 +92,8 @@ SHAPES = [
     (256, 8, 1, 1, 512, 128, "f32"),   # 8 splits of 8 rows
     (256, 8, 1, 1, 512, 128, "bf16"),  # 8 rows per KV head: the matrix-core merged form
     (32, 12, 4, 1, 1000, 64, "bf16"),  # 128 chunks of 32 rows: the matrix-core merged form, ragged tiles
+    (512, 8, 8, 1, 256, 64, "bf16"),   # one row per KV head: the vector-unit merged form
+    (256, 8, 2, 1, 300, 32, "bf16"),   # d = 32: the vector-unit merged form, 4-row waves
     (16, 2, 2, 70, 200, 64, "bf16"),   # Nq = 70 > 64: early rows see no key of the last split
     # either side of the matrix-core split's threshold (bf16 at d = 128)
     (2, 8, 4, 1, 900, 128, "bf16"),    # 2 rows per KV head: the vector-unit split
