@@ -610,11 +610,23 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // query < N, kw < N and (if causal) kw <= query
             if ((q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31)) {
                 const int lo = (causal ? kw : 0) - q0 - 8 * h;
-                const int hi = (kw < N) ? N - q0 - 8 * h : lo;
+                if (q0 + 32 <= N && kw0 + 32 <= N) {
+                    // a diagonal item away from the end: only the causal bound c_e >= lo
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int ce = 16 * (e >> 3) + (e & 7);
-                    s[e] = (ce >= lo && ce < hi) ? s[e] : -INFINITY;
+                    for (int e = 0; e < 16; ++e) {
+                        const int ce = 16 * (e >> 3) + (e & 7);
+                        s[e] = (ce >= lo) ? s[e] : -INFINITY;
+                    }
+                } else {
+                    // both bounds as one unsigned compare: lo <= c_e < hi iff
+                    // c_e - lo < hi - lo (an empty range when hi <= lo)
+                    const int hi = (kw < N) ? N - q0 - 8 * h : lo;
+                    const unsigned span = (unsigned)(max(hi, lo) - lo);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ce = 16 * (e >> 3) + (e & 7);
+                        s[e] = ((unsigned)(ce - lo) < span) ? s[e] : -INFINITY;
+                    }
                 }
             }
 #pragma unroll
