@@ -610,7 +610,16 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // query < N, kw < N and (if causal) kw <= query
             if ((q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31)) {
                 const int lo = (causal ? kw : 0) - q0 - 8 * h;
-                if (q0 + 32 <= N && kw0 + 32 <= N) {
+                if constexpr (kSplit) {
+                    // d = 128: one two-sided test (the split forms below cost this kernel
+                    // registers it does not have: it spilled)
+                    const int hi = (kw < N) ? N - q0 - 8 * h : lo;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int ce = 16 * (e >> 3) + (e & 7);
+                        s[e] = (ce >= lo && ce < hi) ? s[e] : -INFINITY;
+                    }
+                } else if (q0 + 32 <= N && kw0 + 32 <= N) {
                     // a diagonal item away from the end: only the causal bound c_e >= lo
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
