@@ -71,12 +71,22 @@ def resource_usage() -> list:
     """Per-kernel registers, LDS and occupancy as the compiler reports them
     (hipcc -Rpass-analysis=kernel-resource-usage on the device code)."""
     import re
-    rows, cur = [], None
-    for src in sources():
+    from concurrent.futures import ThreadPoolExecutor
+
+    def report(src):   # one compile per source file, run side by side
         cmd = [hipcc(), *[f for f in HIPCC_FLAGS if f not in ("-shared", "-fPIC")], "-c", src,
                "--offload-device-only", "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"]
         res = subprocess.run(cmd, capture_output=True, text=True)
-        for line in res.stderr.splitlines():
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr[-2000:]}")
+        return res.stderr
+
+    srcs = sources()
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 1)) as pool:
+        texts = list(pool.map(report, srcs))
+    rows, cur = [], None
+    for src, text in zip(srcs, texts):
+        for line in text.splitlines():
             m = re.search(r"remark:\s+(.*?)\s+\[-Rpass", line)
             if not m:
                 continue
