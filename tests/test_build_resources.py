@@ -8,8 +8,8 @@ tests. The report (hipcc -Rpass-analysis=kernel-resource-usage) catches both
 at build time:
   - no kernel spills vector registers or uses scratch memory;
   - the matrix-core kernels keep their waves per SIMD: forward 4 at d = 64 and
-    2 at d = 128, dQ pass 3 and 2, dK/dV pass 2 at both, matrix-core decode
-    split 3 and 2.
+    2 at d = 128, dQ pass 3 and 2, dK/dV pass 2 at both (3 for the d = 64
+    form split by tensor), matrix-core decode split 3 and 2.
 """
 import pytest
 
@@ -34,6 +34,11 @@ MIN_OCCUPANCY = {
     "bwd_dq_kernelILi128E": 2,
     "bwd_dkdv_kernelILi64E": 2,
     "bwd_dkdv_kernelILi128E": 2,
+    # d = 64 split by tensor (last template argument true), float and bf16 outputs
+    "bwd_dkdv_kernelILi64EfLb0ELb1E": 3,
+    "bwd_dkdv_kernelILi64EfLb1ELb1E": 3,
+    "bwd_dkdv_kernelILi64EtLb0ELb1E": 3,
+    "bwd_dkdv_kernelILi64EtLb1ELb1E": 3,
     "decode_mfma_kernelIfLi64E": 3,
     "decode_mfma_kernelIfLi128E": 2,
 }

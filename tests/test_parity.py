@@ -151,6 +151,26 @@ def test_noncausal_midsize(B, Hq, Hkv, N, d):
     full_parity(s, poison=True)
 
 
+def _dkdv_workgroups(B, Hkv, N, causal):
+    """Workgroups of the dK/dV pass: one per 64-key K/V tile of a (batch, KV
+    head) unit, or per mirrored pair of tiles when causal."""
+    t = (N + 63) // 64
+    return B * Hkv * ((t + 1) // 2 if causal else t)
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [
+    (8, 12, 12, 520, 64, 1),    # MHA, ragged tail
+    (4, 16, 8, 777, 64, 0),     # GQA group 2, not causal, ragged
+    (12, 12, 4, 1000, 64, 1),   # GQA group 3, ragged
+])
+def test_dkdv_split_form_d64(B, Hq, Hkv, N, d, causal):
+    # at d = 64 the dK/dV pass runs split by tensor (4-wave workgroups, no partial-sum
+    # exchange) from 1.5 workgroups per CU, 384 on the 256 CUs; these grids are above that
+    assert _dkdv_workgroups(B, Hkv, N, causal) >= 384
+    s = workloads.make_shape(B, Hq, Hkv, N, d, dtype="bf16", seed=900 + N + causal, causal=causal)
+    full_parity(s, poison=True)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_stress_peaked_softmax_small(d):
     # the wide-head stress distribution (Q, K ~ N(0, 3^2)) at a size the full oracle covers

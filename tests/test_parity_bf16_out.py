@@ -165,6 +165,7 @@ def test_stress_peaked_softmax_bf16_out(d):
     (2, 4, 2, 37, 16, "f32", 1),
     (2, 6, 3, 77, 32, "bf16", 0),
     (8, 12, 4, 1024, 64, "bf16", 1),   # the GPT-2-small GQA shape, full size
+    (8, 12, 12, 520, 64, "bf16", 1),   # d = 64 dK/dV pass split by tensor (480 workgroups)
     (2, 8, 2, 512, 64, "bf16", 3),     # causal=3 here: causal, Q and K ~ N(0, 3^2)
     (2, 8, 2, 512, 128, "bf16", 3),
 ])

@@ -113,6 +113,12 @@ def test_strided_without_rope_fused_layout():
     run_parity(workloads.make_shape(2, 12, 4, 300, 64, seed=78), layout="fused", rope=False)
 
 
+def test_rope_dkdv_split_form():
+    # d = 64 with 384 dK/dV workgroups: the pass runs split by tensor, and its epilogue
+    # turns dK back and stores dK, dV through the fused layout
+    run_parity(workloads.make_shape(2, 12, 12, 1024, 64, seed=79, causal=0), layout="fused")
+
+
 def test_rope_headline_shape():
     print("[rope parity] gpt2_gqa", flush=True)
     run_parity(workloads.CONFIGS["gpt2_gqa"], layout="fused")

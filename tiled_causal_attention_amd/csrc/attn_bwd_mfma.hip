@@ -396,21 +396,29 @@ bwd_dq_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const 
 //                             per lane, so P and dS are A operands in place)
 //   dV += P^T dO, dK += dS^T Q (B operands: dO, Q tiles read transposed)
 //
-// d = 64: each wave accumulates partial dK and dV for its keys over its own
-// rows; at the end of a K/V tile the NQW partials of each key half are summed
-// in LDS in a fixed order (deterministic) and written out.
-// d = 128 (split by tensor): holding K, V, dK and dV in one wave takes ~490
-// registers, one wave per SIMD. Instead wave (kh, 0) accumulates only dV and
-// wave (kh, 1) only dK, each over all 64 rows of the query tile: each wave keeps
-// the fp16 operand it needs of its own 32-row block (P or dS) and passes the
-// other one to its partner through 8 KB of LDS, one extra barrier per item. That
-// is 256 registers and 73 KB of LDS: two workgroups per CU, two waves per SIMD
-// from different workgroups, and no end-of-tile exchange.
+// Two forms (SPLIT):
+// - exchange (d = 64, up to 1.5 workgroups per CU): 8 waves, 128-row query
+//   tiles; each wave accumulates partial dK and dV for its keys over its own
+//   rows, and at the end of a K/V tile the NQW = 4 partials of each key half are
+//   summed in LDS in a fixed order (deterministic) and written out. One
+//   workgroup per CU (133 KB of LDS), two waves per SIMD.
+// - split by tensor (d = 128 always; d = 64 from 1.5 workgroups per CU): 4
+//   waves, 64-row query tiles; wave (kh, 0) accumulates only dV and wave (kh, 1)
+//   only dK, each over both 32-row blocks of the query tile: each wave keeps the
+//   fp16 operand it needs of its own block (P or dS) and passes the other one to
+//   its partner through 8 KB of LDS, one extra barrier per item, and there is no
+//   end-of-tile exchange. At d = 128 (holding K, V, dK and dV in one wave would
+//   take ~490 registers) that is 256 registers and 73 KB of LDS, two workgroups
+//   per CU; at d = 64, 168 registers and 41 KB, three workgroups per CU. A staged
+//   row feeds as many products per byte as in the exchange form, but a workgroup
+//   has half the waves, so it needs three times the workgroups to fill the CUs:
+//   exactly one per CU (the GQA shapes at N = 1024 and 4096) keeps the exchange.
 namespace bwdkv {
 constexpr int BC = 64;
-template <int D> struct Cfg;
-template <> struct Cfg<64> { static constexpr int NQW = 4; };   // 8 waves, 128-row query tiles
-template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-row query tiles, 2 per CU
+template <int D, bool SPLIT> struct Cfg { static constexpr int NQW = 2; };   // 4 waves, 64-row query tiles
+template <> struct Cfg<64, false> { static constexpr int NQW = 4; };           // 8 waves, 128-row query tiles
+// d = 64 takes the split form from this many workgroups on (1.5 per CU)
+constexpr long long kSplitMinWorkgroups64 = 384;
 
 }  // namespace bwdkv
 
@@ -418,15 +426,16 @@ template <> struct Cfg<128> { static constexpr int NQW = 2; };  // 4 waves, 64-r
 // ROPE: V is read in place through rv's strides, K holds the rotated keys
 // (contiguous, fp16), and dK is turned back by the transpose rotation at the store;
 // dK and dV go through rv's strides.
-template <int D, typename OT, bool ROPE>
-__global__ void __launch_bounds__(64 * 2 * bwdkv::Cfg<D>::NQW, (D == 128) ? 2 : 1)
+template <int D, typename OT, bool ROPE, bool SPLIT>
+__global__ void __launch_bounds__((64 * 2 * bwdkv::Cfg<D, SPLIT>::NQW), (D == 128) ? 2 : (SPLIT ? 3 : 1))
 bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                 const _Float16* __restrict__ q16, const _Float16* __restrict__ do16,
                 const float* __restrict__ l2, const float* __restrict__ delta,
                 OT* __restrict__ dk, OT* __restrict__ dv,
                 int Hq, int Hkv, int N, int causal, ScoreScale sc, int ntiles, int wg_per_unit, KVRope rv) {
     using namespace bwdkv;
-    constexpr int NQW = Cfg<D>::NQW;
+    static_assert(SPLIT || D == 64, "d = 128 runs split by tensor");
+    constexpr int NQW = Cfg<D, SPLIT>::NQW;
     constexpr int NW = 2 * NQW;               // waves
     constexpr int BQ = 32 * NQW;              // query rows per staged tile
     constexpr int DC = D / 16, DB = D / 32;
@@ -443,7 +452,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     // d = 64: partial-sum exchange area. d = 128 (split by tensor): wave (kh, 0)
     // accumulates dV, wave (kh, 1) dK, each over the whole query tile; they trade
     // the fp16 dS (from qw 0) and P (from qw 1) operands of their blocks here
-    constexpr bool kSplit = (D == 128);
+    constexpr bool kSplit = SPLIT;
     __shared__ __attribute__((aligned(16))) float red[kSplit ? 4 : (NQW / 2) * 2 * BC * D];
     __shared__ __attribute__((aligned(16))) _Float16 xch[kSplit ? 2 * 2 * 2 * 64 * 8 : 8];   // [kh][qw][c2][lane][8]
 
@@ -611,8 +620,8 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             if ((q0 + 32 > N) || (kw0 + 32 > N) || (causal && q0 < kw0 + 31)) {
                 const int lo = (causal ? kw : 0) - q0 - 8 * h;
                 if constexpr (kSplit) {
-                    // d = 128: one two-sided test (the split forms below cost this kernel
-                    // registers it does not have: it spilled)
+                    // split by tensor: one two-sided test (the forms below cost the d = 128
+                    // kernel registers it does not have: it spilled)
                     const int hi = (kw < N) ? N - q0 - 8 * h : lo;
 #pragma unroll
                     for (int e = 0; e < 16; ++e) {
@@ -881,17 +890,28 @@ static hipError_t launch_bwd_dq_d(const AttnArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int D, typename OT, bool ROPE, bool SPLIT>
+static hipError_t launch_bwd_dkdv_form(const AttnArgs& a, hipStream_t st, int ntiles, int per_unit) {
+    const int threads = 64 * 2 * bwdkv::Cfg<D, SPLIT>::NQW;
+    const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
+    const KVRope rv = ROPE ? *a.kvrope : KVRope{};
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT, ROPE, SPLIT>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads),
+                       0, st, (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, (OT*)a.dk,
+                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, score_scale(a.scale), ntiles, per_unit, rv);
+    return hipGetLastError();
+}
+
 template <int D, typename OT, bool ROPE>
 static hipError_t launch_bwd_dkdv_d(const AttnArgs& a, hipStream_t st) {
     const int ntiles = (a.N + bwdkv::BC - 1) / bwdkv::BC;
     const int per_unit = a.causal ? (ntiles + 1) / 2 : ntiles;
-    const int threads = 64 * 2 * bwdkv::Cfg<D>::NQW;
-    const BwdWorkspace ws = bwd_workspace_layout(a.workspace, a.dtype, a.B, a.Hq, a.N, a.d);
-    const KVRope rv = ROPE ? *a.kvrope : KVRope{};
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, OT, ROPE>), dim3((unsigned)(per_unit * a.B * a.Hkv)), dim3(threads), 0, st,
-                       (const bf16_t*)a.k, (const bf16_t*)a.v, ws.q16, ws.do16, ws.l2, ws.delta, (OT*)a.dk,
-                       (OT*)a.dv, a.Hq, a.Hkv, a.N, a.causal, score_scale(a.scale), ntiles, per_unit, rv);
-    return hipGetLastError();
+    if constexpr (D == 128) {
+        return launch_bwd_dkdv_form<D, OT, ROPE, true>(a, st, ntiles, per_unit);
+    } else {
+        const long long wgs = (long long)per_unit * a.B * a.Hkv;
+        return (wgs >= bwdkv::kSplitMinWorkgroups64) ? launch_bwd_dkdv_form<D, OT, ROPE, true>(a, st, ntiles, per_unit)
+                                                     : launch_bwd_dkdv_form<D, OT, ROPE, false>(a, st, ntiles, per_unit);
+    }
 }
 
 template <bool ROPE>
