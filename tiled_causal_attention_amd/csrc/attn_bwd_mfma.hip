@@ -449,7 +449,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
     __shared__ __attribute__((aligned(16))) _Float16 Qs0[BQ * D], Qs1[BQ * D];
     __shared__ __attribute__((aligned(16))) _Float16 dOs0[BQ * D], dOs1[BQ * D];
     __shared__ __attribute__((aligned(16))) float Ls0[BQ], Ls1[BQ], Ds0[BQ], Ds1[BQ];
-    // d = 64: partial-sum exchange area. d = 128 (split by tensor): wave (kh, 0)
+    // exchange form: partial-sum exchange area. Split by tensor: wave (kh, 0)
     // accumulates dV, wave (kh, 1) dK, each over the whole query tile; they trade
     // the fp16 dS (from qw 0) and P (from qw 1) operands of their blocks here
     constexpr bool kSplit = SPLIT;
@@ -762,7 +762,7 @@ bwd_dkdv_kernel(const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
             // NQW - 1 blocks addressed to it in source order (fixed order: deterministic) and
             // stores its keys. One exchange round; every wave shares the adds and the stores.
             // A block is lane-major 16-byte chunks (16 lanes of a cycle hit 256 contiguous
-            // bytes: no bank conflicts). The blocks fill `red`, then (d = 64) this item's Q and
+            // bytes: no bank conflicts). The blocks fill `red`, then this item's Q and
             // dO buffers, which every wave has finished reading at the barrier below.
             constexpr int E = 16 / NQW;                  // accumulators owned per wave
             constexpr int BS = 2 * DB * E * 64;          // floats per block (16-byte chunks, 64 lanes)
