@@ -705,10 +705,13 @@ decode_mfma_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 // thread t = (split group g, column pair p) accumulates its two columns over
 // splits g, g + NG, ... (NG = 256 / NP groups), with the partial sums added
 // across the groups through LDS in a fixed order. Every thread loads only its
-// own splits. Split 0 holds key 0, visible to every row, so the maximum is
-// finite.
+// own splits; the first kMergePre of them before the split statistics, so their
+// loads are in flight during the reductions rather than after them (the sums
+// run in the same order either way). Split 0 holds key 0, visible to every row,
+// so the maximum is finite.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeColSplits = 32;   // more splits per row than this: column blocks of 16 pairs
+constexpr int kMergePre = 4;          // partial-row loads per thread issued ahead of the statistics
 template <typename OT, int D, int NP>
 __global__ void __launch_bounds__(kMergeThreads)
 decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ lpart, OT* __restrict__ o,
@@ -725,6 +728,12 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     const int c0 = 2 * NP * (blockIdx.x % CB);   // first column of this workgroup
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int p = tid % NP, g = tid / NP;
+    float2 xe[kMergePre];
+#pragma unroll
+    for (int i = 0; i < kMergePre; ++i) {   // unconditional (clamped) loads: one wait for all of them
+        const int sidx = min(g + i * NG, nsplit - 1);
+        xe[i] = *reinterpret_cast<const float2*>(opart + ((size_t)sidx * nrows + row) * D + c0 + 2 * p);
+    }
     const float ls = tid < nsplit ? lpart[(size_t)tid * nrows + row] : -INFINITY;
     float mx = ls;
 #pragma unroll
@@ -742,8 +751,17 @@ decode_merge_kernel(const float* __restrict__ opart, const float* __restrict__ l
     __syncthreads();
     sum = (red[0] + red[1]) + (red[2] + red[3]);
     float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMergePre; ++i) {
+        const int sidx = g + i * NG;
+        if (sidx < nsplit) {
+            const float wgt = wsh[sidx];
+            a0 = fmaf(wgt, xe[i].x, a0);
+            a1 = fmaf(wgt, xe[i].y, a1);
+        }
+    }
 #pragma unroll 4
-    for (int sidx = g; sidx < nsplit; sidx += NG) {
+    for (int sidx = g + kMergePre * NG; sidx < nsplit; sidx += NG) {
         const float2 x = *reinterpret_cast<const float2*>(opart + ((size_t)sidx * nrows + row) * D + c0 + 2 * p);
         const float wgt = wsh[sidx];
         a0 = fmaf(wgt, x.x, a0);
