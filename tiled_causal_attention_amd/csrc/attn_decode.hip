@@ -455,17 +455,16 @@ struct MfmaDecRow {
     }
 };
 
-// The row's query as B operands (bf16, the scale's sign folded in; zero for a row
-// past the chunk's rows).
+// The row's query chunks as loaded (a row past the chunk's rows reads the last
+// one; its operand is zeroed when the first tile forms the operands): no use of
+// the loaded values here, so the first tile's K and V requests go out behind
+// these loads instead of after their arrival.
 template <int D>
-__device__ __forceinline__ void mfma_dec_load_q(bf16x8 (&qb)[D / 16], const bf16_t* q, const MfmaDecRow& row,
-                                                const ScoreScale& sc, int h) {
+__device__ __forceinline__ void mfma_dec_load_q(u32x4 (&qraw)[D / 16], const bf16_t* q, const MfmaDecRow& row,
+                                                int h) {
     const bf16_t* qrow = q + row.grow * D + 8 * h;
 #pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-        qb[c] = row.ok ? __builtin_bit_cast(bf16x8, apply_qsign(x, sc)) : bf16x8{};
-    }
+    for (int c = 0; c < D / 16; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
 }
 
 // Keys [t0, t0 + 64) of the unit, keys below `lim` visible to this lane's row. The
@@ -476,8 +475,13 @@ __device__ __forceinline__ void mfma_dec_load_q(bf16x8 (&qb)[D / 16], const bf16
 // rounded to fp16 and V^T read transposed (converted to fp16 at the read). Only
 // this wave touches Vs: the fences keep its LDS reads of the previous tile ahead
 // of the copies and its reads of this tile behind their arrival.
+//
+// The query's B operands (bf16, the scale's sign folded in, zero for a row past the
+// chunk's rows) are formed from its loaded chunks in the first tile (`first`, wave
+// uniform), after the wait that covers the query loads too.
 template <int D>
-__device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 (&qb)[D / 16],
+__device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, bf16x8 (&qb)[D / 16], const u32x4 (&qraw)[D / 16],
+                                              bool first, bool qok, const ScoreScale& sc,
                                               __amdgpu_buffer_rsrc_t krs, const bf16_t* kunit, const bf16_t* vunit,
                                               int Nk, int t0, int lim, _Float16* Vs, _Float16* Ks, float sl2,
                                               int lane) {
@@ -507,6 +511,10 @@ __device__ __forceinline__ void mfma_dec_tile(MfmaDecState<D>& st, const bf16x8 
     }
     wait_vmem_all();   // the copies are in LDS
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (first) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qb[c] = qok ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
+    }
     // ---- S^T = K Q^T; accumulator e of block kb: key t0 + 32 kb + 16(e/8) + 8h + e%8
     f32x16 s[2];
 #pragma unroll
@@ -585,14 +593,16 @@ decode_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, c
     const int k0 = split * split_len, k1 = min(Nk, k0 + split_len);
     const int lim = !row.ok ? k0 : (causal ? min(k1, row.pos + 1) : k1);   // keys below lim are visible
 
+    u32x4 qraw[D / 16];
     bf16x8 qb[D / 16];
-    mfma_dec_load_q<D>(qb, q, row, sc, h);
+    mfma_dec_load_q<D>(qraw, q, row, h);
     const size_t kvoff = (size_t)unit * Nk * D;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
     MfmaDecState<D> st;
     st.init();
     for (int t0 = k0; t0 < k1; t0 += BC)
-        mfma_dec_tile<D>(st, qb, krs, k + kvoff, v + kvoff, Nk, t0, lim, Vs, Ks, sc.sl2, lane);
+        mfma_dec_tile<D>(st, qb, qraw, t0 == k0, row.ok, sc, krs, k + kvoff, v + kvoff, Nk, t0, lim, Vs, Ks, sc.sl2,
+                         lane);
 
     // ---- this split's normalised output and LSE
     const float l_tot = sum_halves(st.l_run);
@@ -649,15 +659,17 @@ decode_mfma_fused_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     const MfmaDecRow row(b, hkv, rc, r, Hq, Hkv, Nq, Nk);
     const int lim = !row.ok ? 0 : (causal ? min(Nk, row.pos + 1) : Nk);
 
+    u32x4 qraw[D / 16];
     bf16x8 qb[D / 16];
-    mfma_dec_load_q<D>(qb, q, row, sc, h);
+    mfma_dec_load_q<D>(qraw, q, row, h);
     const size_t kvoff = (size_t)unit * Nk * D;
     const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kvoff, (uint32_t)((size_t)Nk * D * 2));
     MfmaDecState<D> st;
     st.init();
     const int ntiles = (Nk + BC - 1) / BC;
     for (int t = w; t < ntiles; t += W)
-        mfma_dec_tile<D>(st, qb, krs, k + kvoff, v + kvoff, Nk, t * BC, lim, Vs[w], Ks[kKLds<D> ? w : 0], sc.sl2, lane);
+        mfma_dec_tile<D>(st, qb, qraw, t == w, row.ok, sc, krs, k + kvoff, v + kvoff, Nk, t * BC, lim, Vs[w],
+                         Ks[kKLds<D> ? w : 0], sc.sl2, lane);
 
     // ---- this wave's state into LDS (its V buffer, whose reads are done)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
