@@ -142,9 +142,10 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* qh = q + bh * N * D;
     const float sl2 = sc.sl2;              // scores in log2 units (positive multiplier)
 
-    // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]. With ROPE
-    // the row's table values are loaded next to it and the rotation waits until the
-    // first K/V tile is staged, so both loads' latency overlaps the tile loads.
+    // Q rows of this wave as B operands: lane holds Q[qi][16c + 8h .. +7]. The operands
+    // are formed (with ROPE: the row rotated, its table values loaded next to it) only
+    // after the first K/V tile is staged, so the first tile's loads go out behind the
+    // Q loads rather than after their arrival.
     bf16x8 qb[DC];
     u32x4 qraw[DC];
     QRopeRow<D> qtab;
@@ -154,13 +155,7 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                   : qh + (size_t)qc * D + 8 * h;
 #pragma unroll
         for (int c = 0; c < DC; ++c) qraw[c] = *reinterpret_cast<const u32x4*>(qrow + 16 * c);
-        if constexpr (ROPE) {
-            qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
-        } else {
-#pragma unroll
-            for (int c = 0; c < DC; ++c)
-                qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
-        }
+        if constexpr (ROPE) qtab.load(rq.cs + (size_t)qc * (D / 2), rq.sn + (size_t)qc * (D / 2), h);
     }
 
     // K/V tile prefetch registers: thread owns chunks tid + NT u (coalesced rows)
@@ -197,12 +192,9 @@ fwd_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     store_kv_tile<D, KCH>(kreg, vreg, kst0, vst0);
     if (ntile > 1) load_kv_tile<D, KCH, ROPE>(kreg, vreg, krs, ld_off + BC * D * 2, vrows, vld_off, vtile);
     __syncthreads();
-    if constexpr (ROPE) {
-        rope_rotate_q<D>(qraw, qtab);
+    if constexpr (ROPE) rope_rotate_q<D>(qraw, qtab);
 #pragma unroll
-        for (int c = 0; c < DC; ++c)
-            qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
-    }
+    for (int c = 0; c < DC; ++c) qb[c] = (qi < N) ? __builtin_bit_cast(bf16x8, apply_qsign(qraw[c], sc)) : bf16x8{};
 
     for (int j = 0; j < ntile; ++j) {
         const int buf = j & 1, k0 = j * BC;
