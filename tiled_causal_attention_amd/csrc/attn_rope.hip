@@ -90,7 +90,9 @@ layout_copy_kernel(CopyJobs jobs, const float* __restrict__ cs, const float* __r
     const long long idx = (long long)blockIdx.x * rope::kThreads + threadIdx.x;
     if (idx >= total) return;
     const int jn = (jobs.n > 1 && idx >= jobs.j[1].begin) + (jobs.n > 2 && idx >= jobs.j[2].begin);
-    const CopyJob& J = jobs.j[jn];
+    // the thread's job selected by value: the descriptors stay in scalar registers
+    // (an indexed access would first load them per lane from the argument block)
+    const CopyJob J = jn == 0 ? jobs.j[0] : (jn == 1 ? jobs.j[1] : jobs.j[2]);
     const long long li = idx - J.begin;
     const int half = d / 2;
     const int i0 = 8 * (int)(li & ((1 << chunk_shift) - 1));
@@ -101,16 +103,26 @@ layout_copy_kernel(CopyJobs jobs, const float* __restrict__ cs, const float* __r
     const unsigned b = bh / (unsigned)J.H;
     const TI* s = static_cast<const TI*>(J.src) + b * J.sb + h * J.sh + (long long)n * J.sn + i0;
     TO* t = static_cast<TO*>(J.dst) + b * J.db + h * J.dh + (long long)n * J.dn + i0;
+    // the row's table entries first (they depend on the position only), so their
+    // loads and the data's are in flight together
+    float cv[8], sv8[8];
+    if (cs != nullptr) {
+        const float* cp = cs + (long long)n * half + i0;
+        const float* sp = sn + (long long)n * half + i0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            cv[e] = cp[e];
+            sv8[e] = sp[e];
+        }
+    }
     float x1[8], x2[8];
     load8<VEC>(s, x1);
     load8<VEC>(s + half, x2);
     if (J.rot != 0) {
-        const float* cp = cs + (long long)n * half + i0;
-        const float* sp = sn + (long long)n * half + i0;
         const float sg = J.rot == 1 ? 1.f : -1.f;   // the transpose flips the sine
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float c = cp[e], sv = sg * sp[e];
+            const float c = cv[e], sv = sg * sv8[e];
             const float a = x1[e], bb = x2[e];
             x1[e] = a * c - bb * sv;
             x2[e] = bb * c + a * sv;
